@@ -1,0 +1,231 @@
+"""Float64 CPU oracle for Orthros attention — TEST INFRASTRUCTURE, not product code.
+
+Only the test suite, the package smoke check and the benchmark's CPU-baseline leg may import
+this module. The product path (the HIP library and its Python binding) never calls it, and it
+imports nothing from the product path.
+
+What it computes follows the paper "Orthros: Phase-Aware Heterogeneous Attention for
+Efficient Transformers":
+  * §3.1, the query definitions: base query q_i = alpha (.) (x_i W_Q) + beta, output-stream
+    query q'_i = alpha' (.) (x'_i W_Q) + beta'. Here the projection x W_Q is the caller's
+    input ``q_raw``; the oracle applies only the element-wise scale-offset.
+  * §3.1 Eq. 4: base-stream sliding-window attention; row t sees keys
+    max(1, t-w+1) .. t (1-based), i.e. exactly w keys including itself.
+  * §3.1 Eq. 5: output-stream full causal cross-attention; row t sees keys 1 .. t.
+  * §3.1: keys and values come from the base tokens only; the output stream never writes
+    them (Algorithm 1, the "shared KV cache" step).
+  * §3.2: the regimes Pre-Training (every position duplicated), Prefilling (one output row
+    at the last prompt token) and Decoding (one new token, duplicated into a base copy that
+    updates the cache and runs the window, and an output copy that attends to the history).
+  * §3.2 SFT regime: output rows only at the response positions.
+
+Readings where the pages are silent or garbled (all listed in the repository's design notes):
+  * scale: the extracted equations lost the square root and the division; the scale is the
+    usual 1/sqrt(d_h) unless the caller passes another one.
+  * positions are 0-based here: row t (0-based) of Eq. 4 sees keys max(0, t-w+1) .. t.
+  * grouped-query attention (absent from the pages): query head h reads key/value head
+    h // (H_q / H_kv).
+  * the scale-offset vectors hold one entry per (query head, channel): shape [H_q * d].
+  * "historical cache" in the decoding regime includes the current token (Eq. 5's upper
+    limit j = t), so a decode step appends the new key/value before attending.
+
+All arithmetic is float64 numpy. Inputs are converted to float64 exactly (bf16 and fp32
+values are representable). No blocking, fusion or reordering beyond a per-row evaluation.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "default_scale",
+    "scale_offset",
+    "attention_weights",
+    "attend",
+    "base_row",
+    "output_row",
+    "prefill",
+    "decode_step",
+    "forward_pt",
+    "forward_sft",
+]
+
+
+def default_scale(head_dim: int) -> float:
+    """Score scale 1/sqrt(d_h) (§3.1 Eq. 4/5; the root was lost in extraction)."""
+    return 1.0 / np.sqrt(float(head_dim))
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+def scale_offset(q_raw, alpha, beta) -> np.ndarray:
+    """§3.1: q = alpha (.) q_raw + beta, element-wise per (query head, channel).
+
+    q_raw: [..., H_q, d]; alpha, beta: [H_q * d] (one entry per head and channel).
+    """
+    q_raw = _f64(q_raw)
+    hq, d = q_raw.shape[-2], q_raw.shape[-1]
+    a = _f64(alpha).reshape(hq, d)
+    b = _f64(beta).reshape(hq, d)
+    return a * q_raw + b
+
+
+def attention_weights(q, K, scale) -> np.ndarray:
+    """Softmax weights of Eq. 4/5 for one query vector q [d] over key rows K [n, d].
+
+    exp(s q.k_j) / sum_m exp(s q.k_m). Every exponent is shifted by the same constant (the
+    largest score) before exponentiation; the shift cancels between numerator and
+    denominator and only keeps exp() finite.
+    """
+    z = scale * (_f64(K) @ _f64(q))
+    e = np.exp(z - z.max())
+    return e / e.sum()
+
+
+def attend(q, K, V, scale) -> np.ndarray:
+    """Eq. 4/5 for one query vector: sum_j softmax_j * v_j over the given rows."""
+    w = attention_weights(q, K, scale)
+    return w @ _f64(V)
+
+
+def _kv_head(h: int, hq: int, hkv: int) -> int:
+    if hq % hkv:
+        raise ValueError("H_q must be a multiple of H_kv")
+    return h // (hq // hkv)
+
+
+def base_row(q_t, K, V, t: int, window: int, scale) -> np.ndarray:
+    """Eq. 4 at 0-based position t for all query heads.
+
+    q_t: [H_q, d] (already scale-offset); K, V: [n, H_kv, d] holding keys 0..t at least.
+    Keys max(0, t-w+1) .. t.
+    """
+    lo = max(0, t - window + 1)
+    return _rows_over(q_t, K[lo:t + 1], V[lo:t + 1], scale)
+
+
+def output_row(q_t, K, V, t: int, scale) -> np.ndarray:
+    """Eq. 5 at 0-based position t for all query heads: keys 0 .. t."""
+    return _rows_over(q_t, K[:t + 1], V[:t + 1], scale)
+
+
+def _rows_over(q_t, Kw, Vw, scale) -> np.ndarray:
+    q_t = _f64(q_t)
+    hq, d = q_t.shape
+    hkv = Kw.shape[1]
+    out = np.empty((hq, d), dtype=np.float64)
+    for h in range(hq):
+        g = _kv_head(h, hq, hkv)
+        out[h] = attend(q_t[h], Kw[:, g, :], Vw[:, g, :], scale)
+    return out
+
+
+def prefill(q_base, q_out, k, v, alpha_b, beta_b, alpha_o, beta_o, window, scale=None,
+            rows=None):
+    """§3.2 Prefilling (T_in = P-1, T_out = 1) for a batch of prompts of length P.
+
+    q_base: [B, P, H_q, d] base-stream raw queries; q_out: [B, 1, H_q, d] raw query of the
+    duplicated last prompt token; k, v: [B, P, H_kv, d].
+    Returns (o_base [B, P, H_q, d], o_out [B, 1, H_q, d], cache_k, cache_v, cache_len) where
+    the cache holds every prompt key/value (the base tokens write it; the output copy does
+    not) and cache_len[b] = P.
+    ``rows``: optional iterable of base positions to evaluate (others left NaN), for
+    sampled checks at large P.
+    """
+    k = _f64(k)
+    v = _f64(v)
+    B, P = k.shape[0], k.shape[1]
+    d = k.shape[-1]
+    s = default_scale(d) if scale is None else scale
+    qb = scale_offset(q_base, alpha_b, beta_b) if rows is None else None
+    o_base = np.full(np.shape(q_base), np.nan)
+    o_out = np.empty(np.shape(q_out))
+    positions = range(P) if rows is None else rows
+    for b in range(B):
+        for t in positions:
+            q_t = qb[b, t] if qb is not None else scale_offset(q_base[b, t], alpha_b, beta_b)
+            o_base[b, t] = base_row(q_t, k[b], v[b], t, window, s)
+        q_o = scale_offset(q_out[b, 0], alpha_o, beta_o)
+        o_out[b, 0] = output_row(q_o, k[b], v[b], P - 1, s)
+    cache_len = np.full(B, P, dtype=np.int64)
+    return o_base, o_out, k.copy(), v.copy(), cache_len
+
+
+def decode_step(cache_k, cache_v, cache_len, q_base, q_out, k_new, v_new,
+                alpha_b, beta_b, alpha_o, beta_o, window, scale=None):
+    """§3.2 Decoding (T = 1): one new token per sequence, duplicated into a pair.
+
+    cache_k, cache_v: [B, >=L_b, H_kv, d] history; cache_len: [B] current lengths L_b.
+    q_base, q_out: [B, H_q, d]; k_new, v_new: [B, H_kv, d].
+    The base copy appends (k_new, v_new) at index L_b (its own key belongs to its window, the
+    upper limit j = t of Eq. 4), then attends over max(0, L_b-w+1) .. L_b (Eq. 4); the output
+    copy attends over 0 .. L_b (Eq. 5) and writes nothing.
+    Returns (o_base [B, H_q, d], o_out [B, H_q, d], new_k_list, new_v_list, new_len) with the
+    appended histories as a list of [L_b+1, H_kv, d] arrays.
+    """
+    B = len(cache_len)
+    d = np.shape(q_base)[-1]
+    s = default_scale(d) if scale is None else scale
+    o_base = np.empty(np.shape(q_base))
+    o_out = np.empty(np.shape(q_out))
+    ks, vs, lens = [], [], []
+    for b in range(B):
+        L = int(cache_len[b])
+        Kb = np.concatenate([_f64(cache_k[b][:L]), _f64(k_new[b])[None]], axis=0)
+        Vb = np.concatenate([_f64(cache_v[b][:L]), _f64(v_new[b])[None]], axis=0)
+        o_base[b] = base_row(scale_offset(q_base[b], alpha_b, beta_b), Kb, Vb, L, window, s)
+        o_out[b] = output_row(scale_offset(q_out[b], alpha_o, beta_o), Kb, Vb, L, s)
+        ks.append(Kb)
+        vs.append(Vb)
+        lens.append(L + 1)
+    return o_base, o_out, ks, vs, np.asarray(lens, dtype=np.int64)
+
+
+def forward_pt(q_base, q_out, k, v, alpha_b, beta_b, alpha_o, beta_o, window, scale=None,
+               base_rows=None, out_rows=None):
+    """§3.2 Pre-Training (T_in = 0, T_out = T): the whole sequence is duplicated.
+
+    Base rows run Eq. 4 at every position with q_base; output rows run Eq. 5 at every position
+    with q_out. Shapes: q_base, q_out [B, T, H_q, d]; k, v [B, T, H_kv, d].
+    ``base_rows`` / ``out_rows``: optional position subsets (others left NaN).
+    """
+    k = _f64(k)
+    v = _f64(v)
+    B, T = k.shape[0], k.shape[1]
+    d = k.shape[-1]
+    s = default_scale(d) if scale is None else scale
+    o_base = np.full(np.shape(q_base), np.nan)
+    o_out = np.full(np.shape(q_out), np.nan)
+    for b in range(B):
+        for t in (range(T) if base_rows is None else base_rows):
+            o_base[b, t] = base_row(scale_offset(q_base[b, t], alpha_b, beta_b), k[b], v[b],
+                                    t, window, s)
+        for t in (range(T) if out_rows is None else out_rows):
+            o_out[b, t] = output_row(scale_offset(q_out[b, t], alpha_o, beta_o), k[b], v[b],
+                                     t, s)
+    return o_base, o_out
+
+
+def forward_sft(q_base, q_out, k, v, out_positions, alpha_b, beta_b, alpha_o, beta_o,
+                window, scale=None):
+    """§3.2 Supervised Fine-Tuning (T_in = T - T_out, T_out >= 1).
+
+    Base rows at every position (Eq. 4); output rows only at ``out_positions`` (Eq. 5), with
+    q_out [B, T_out, H_q, d] holding the duplicated tokens in that order.
+    """
+    k = _f64(k)
+    v = _f64(v)
+    B, T = k.shape[0], k.shape[1]
+    d = k.shape[-1]
+    s = default_scale(d) if scale is None else scale
+    o_base = np.empty(np.shape(q_base))
+    o_out = np.empty(np.shape(q_out))
+    for b in range(B):
+        for t in range(T):
+            o_base[b, t] = base_row(scale_offset(q_base[b, t], alpha_b, beta_b), k[b], v[b],
+                                    t, window, s)
+        for r, t in enumerate(out_positions):
+            o_out[b, r] = output_row(scale_offset(q_out[b, r], alpha_o, beta_o), k[b], v[b],
+                                     int(t), s)
+    return o_base, o_out

@@ -1,0 +1,287 @@
+"""Pins for the float64 oracle, checked against things other than the oracle itself.
+
+Sources of truth, all CPU-only:
+  * a hand-derived worked example (tests/golden/worked_example.json) for the paper
+    "Orthros: Phase-Aware Heterogeneous Attention for Efficient Transformers", §3.1 Eq. 4/5
+    and the query scale-offset definitions;
+  * torch's scaled_dot_product_attention in float64 (a library attention routine) with its own
+    causal flag, its own grouped-query expansion, and an explicit band mask;
+  * closed forms (zero keys give plain averages over the window or the prefix; window 1
+    returns the value row);
+  * invariants of the equations: window >= T is causal attention, GQA equals MHA with
+    repeated key/value heads, linearity in V, weights form a distribution, the PT regime agrees
+    with prefill followed by decode steps (§3.2), the SFT rows agree with PT rows, and a
+    planted key matching the query dominates the output row.
+Each pin is chosen so a plausible slip in the oracle (dropped offset, wrong scale, window off
+by one, wrong head mapping, attend-before-append in decode, transposed operand) fails it.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+RNG = np.random.default_rng(1234)
+
+
+def _val(x):
+    if isinstance(x, str):
+        return {"sqrt2": math.sqrt(2.0), "sqrt2-2": math.sqrt(2.0) - 2.0,
+                "ln2": math.log(2.0), "ln3": math.log(3.0)}[x]
+    return float(x)
+
+
+def _arr(rows):
+    return np.array([[_val(x) for x in r] for r in rows], dtype=np.float64)
+
+
+def _rand(*shape):
+    return RNG.standard_normal(shape)
+
+
+def _affine(hq, d, identity=False):
+    if identity:
+        return np.ones(hq * d), np.zeros(hq * d), np.ones(hq * d), np.zeros(hq * d)
+    return (1 + 0.1 * _rand(hq * d), 0.1 * _rand(hq * d),
+            1 + 0.1 * _rand(hq * d), 0.1 * _rand(hq * d))
+
+
+# ---------------------------------------------------------------------------------------------
+# Worked example (hand-derived, exact)
+# ---------------------------------------------------------------------------------------------
+def _golden():
+    with open(os.path.join(HERE, "golden", "worked_example.json")) as f:
+        g = json.load(f)
+    T = len(g["k"])
+    qb = _arr(g["q_raw_base"]).reshape(1, T, 1, 2)
+    qo = _arr(g["q_raw_out"]).reshape(1, T, 1, 2)
+    k = _arr(g["k"]).reshape(1, T, 1, 2)
+    v = _arr(g["v"]).reshape(1, T, 1, 2)
+    aff = (np.array([_val(x) for x in g["alpha_base"]]), np.array([_val(x) for x in g["beta_base"]]),
+           np.array([_val(x) for x in g["alpha_out"]]), np.array([_val(x) for x in g["beta_out"]]))
+    return g, qb, qo, k, v, aff
+
+
+def test_worked_example_pt():
+    g, qb, qo, k, v, aff = _golden()
+    ob, oo = oracle.forward_pt(qb, qo, k, v, *aff, window=g["window"])
+    np.testing.assert_allclose(ob[0, :, 0], _arr(g["expected_base"]), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(oo[0, :, 0], _arr(g["expected_out"]), rtol=0, atol=1e-12)
+
+
+def test_worked_example_prefill():
+    g, qb, qo, k, v, aff = _golden()
+    ob, oo, ck, cv, ln = oracle.prefill(qb, qo[:, -1:], k, v, *aff, window=g["window"])
+    np.testing.assert_allclose(ob[0, :, 0], _arr(g["expected_base"]), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(oo[0, 0, 0], _arr(g["expected_out"])[-1], rtol=0, atol=1e-12)
+    assert ln.tolist() == [3]
+    np.testing.assert_array_equal(ck, k)
+    np.testing.assert_array_equal(cv, v)
+
+
+def test_worked_example_decode():
+    """Prefill two tokens, decode the third: same rows as the hand derivation."""
+    g, qb, qo, k, v, aff = _golden()
+    _, _, ck, cv, ln = oracle.prefill(qb[:, :2], qo[:, 1:2], k[:, :2], v[:, :2], *aff,
+                                      window=g["window"])
+    ob, oo, nk, nv, nl = oracle.decode_step(ck, cv, ln, qb[:, 2], qo[:, 2], k[:, 2], v[:, 2],
+                                            *aff, window=g["window"])
+    np.testing.assert_allclose(ob[0, 0], _arr(g["expected_base"])[2], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(oo[0, 0], _arr(g["expected_out"])[2], rtol=0, atol=1e-12)
+    assert nl.tolist() == [3]
+    np.testing.assert_array_equal(nk[0], k[0])
+
+
+# ---------------------------------------------------------------------------------------------
+# Library routine: torch SDPA in float64
+# ---------------------------------------------------------------------------------------------
+def _sdpa(q, k, v, mask=None, causal=False, gqa=False):
+    # q [T, Hq, d], k/v [T, Hkv, d] -> [T, Hq, d]
+    qt = torch.from_numpy(np.ascontiguousarray(q.transpose(1, 0, 2)))[None]
+    kt = torch.from_numpy(np.ascontiguousarray(k.transpose(1, 0, 2)))[None]
+    vt = torch.from_numpy(np.ascontiguousarray(v.transpose(1, 0, 2)))[None]
+    m = None if mask is None else torch.from_numpy(mask)
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=m,
+                                                         is_causal=causal, enable_gqa=gqa)
+    return o[0].numpy().transpose(1, 0, 2)
+
+
+@pytest.mark.parametrize("T,hq,hkv,d", [(37, 4, 1, 16), (50, 4, 2, 8), (64, 3, 3, 32)])
+def test_output_stream_matches_sdpa_causal(T, hq, hkv, d):
+    qb, qo = _rand(1, T, hq, d), _rand(1, T, hq, d)
+    k, v = _rand(1, T, hkv, d), _rand(1, T, hkv, d)
+    aff = _affine(hq, d)
+    _, oo = oracle.forward_pt(qb, qo, k, v, *aff, window=5)
+    q_eff = (aff[2].reshape(hq, d) * qo[0] + aff[3].reshape(hq, d))
+    ref = _sdpa(q_eff, k[0], v[0], causal=True, gqa=hkv != hq)
+    np.testing.assert_allclose(oo[0], ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("T,w,hq,hkv,d", [(40, 1, 2, 1, 8), (40, 7, 4, 2, 16), (33, 32, 2, 2, 8),
+                                          (33, 33, 2, 1, 8), (20, 64, 4, 4, 4)])
+def test_base_stream_matches_sdpa_band(T, w, hq, hkv, d):
+    qb, qo = _rand(1, T, hq, d), _rand(1, T, hq, d)
+    k, v = _rand(1, T, hkv, d), _rand(1, T, hkv, d)
+    aff = _affine(hq, d)
+    ob, _ = oracle.forward_pt(qb, qo, k, v, *aff, window=w)
+    q_eff = (aff[0].reshape(hq, d) * qb[0] + aff[1].reshape(hq, d))
+    t = np.arange(T)[:, None]
+    j = np.arange(T)[None, :]
+    band = (j <= t) & (j > t - w)
+    ref = _sdpa(q_eff, k[0], v[0], mask=band, gqa=hkv != hq)
+    np.testing.assert_allclose(ob[0], ref, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------------------------
+# Closed forms
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("T,w", [(30, 1), (30, 4), (30, 29), (30, 30), (30, 100)])
+def test_zero_keys_give_window_and_prefix_means(T, w):
+    hq, hkv, d = 2, 1, 6
+    qb, qo = _rand(1, T, hq, d), _rand(1, T, hq, d)
+    k = np.zeros((1, T, hkv, d))
+    v = _rand(1, T, hkv, d)
+    ob, oo = oracle.forward_pt(qb, qo, k, v, *_affine(hq, d), window=w)
+    c = np.concatenate([np.zeros((1, d)), np.cumsum(v[0, :, 0], axis=0)], axis=0)
+    for t in range(T):
+        lo = max(0, t - w + 1)
+        np.testing.assert_allclose(ob[0, t, 0], (c[t + 1] - c[lo]) / (t + 1 - lo), atol=1e-12)
+        np.testing.assert_allclose(ob[0, t, 1], (c[t + 1] - c[lo]) / (t + 1 - lo), atol=1e-12)
+        np.testing.assert_allclose(oo[0, t, 1], c[t + 1] / (t + 1), atol=1e-12)
+
+
+def test_window_one_returns_value_row():
+    T, hq, hkv, d = 25, 4, 2, 8
+    qb, qo, k, v = _rand(2, T, hq, d), _rand(2, T, hq, d), _rand(2, T, hkv, d), _rand(2, T, hkv, d)
+    ob, _ = oracle.forward_pt(qb, qo, k, v, *_affine(hq, d), window=1)
+    np.testing.assert_array_equal(ob, np.repeat(v, 2, axis=2))
+
+
+def test_decode_zero_keys_mean_includes_new_token():
+    """Eq. 4/5 upper limit j = t: the decode step's own key belongs to both windows."""
+    B, L, hq, hkv, d, w = 2, 9, 2, 1, 4, 3
+    ck, cv = np.zeros((B, L, hkv, d)), _rand(B, L, hkv, d)
+    vn = _rand(B, hkv, d)
+    ob, oo, _, nv, nl = oracle.decode_step(ck, cv, [L, L - 4], _rand(B, hq, d), _rand(B, hq, d),
+                                           np.zeros((B, hkv, d)), vn, *_affine(hq, d), window=w)
+    for b, Lb in enumerate([L, L - 4]):
+        hist = np.concatenate([cv[b, :Lb, 0], vn[b, 0][None]], axis=0)
+        np.testing.assert_allclose(ob[b, 0], hist[-w:].mean(0), atol=1e-12)
+        np.testing.assert_allclose(oo[b, 1], hist.mean(0), atol=1e-12)
+        assert nl[b] == Lb + 1 and len(nv[b]) == Lb + 1
+
+
+# ---------------------------------------------------------------------------------------------
+# Invariants
+# ---------------------------------------------------------------------------------------------
+def test_window_at_least_T_is_causal_and_streams_coincide():
+    T, hq, hkv, d = 31, 4, 2, 16
+    q, k, v = _rand(1, T, hq, d), _rand(1, T, hkv, d), _rand(1, T, hkv, d)
+    a, b = 1 + 0.1 * _rand(hq * d), 0.1 * _rand(hq * d)
+    ob, oo = oracle.forward_pt(q, q, k, v, a, b, a, b, window=T)
+    np.testing.assert_allclose(ob, oo, rtol=0, atol=1e-13)
+    ob2, _ = oracle.forward_pt(q, q, k, v, a, b, a, b, window=10 * T)
+    np.testing.assert_allclose(ob2, oo, rtol=0, atol=1e-13)
+
+
+def test_identity_affine_is_plain_attention():
+    """alpha = 1, beta = 0 is the paper's ablation without scale-offset (§4.1)."""
+    T, hq, d = 12, 2, 8
+    q, k, v = _rand(1, T, hq, d), _rand(1, T, hq, d), _rand(1, T, hq, d)
+    _, oo = oracle.forward_pt(q, q, k, v, *_affine(hq, d, identity=True), window=3)
+    np.testing.assert_allclose(oo[0], _sdpa(q[0], k[0], v[0], causal=True), atol=1e-12)
+
+
+def test_gqa_equals_mha_with_repeated_kv_heads():
+    T, hq, hkv, d = 20, 8, 2, 8
+    qb, qo, k, v = _rand(1, T, hq, d), _rand(1, T, hq, d), _rand(1, T, hkv, d), _rand(1, T, hkv, d)
+    aff = _affine(hq, d)
+    ob, oo = oracle.forward_pt(qb, qo, k, v, *aff, window=6)
+    G = hq // hkv
+    ob2, oo2 = oracle.forward_pt(qb, qo, np.repeat(k, G, axis=2), np.repeat(v, G, axis=2), *aff,
+                                 window=6)
+    np.testing.assert_array_equal(ob, ob2)
+    np.testing.assert_array_equal(oo, oo2)
+
+
+def test_linear_in_values():
+    T, hq, d = 18, 2, 8
+    qb, qo, k = _rand(1, T, hq, d), _rand(1, T, hq, d), _rand(1, T, hq, d)
+    v1, v2 = _rand(1, T, hq, d), _rand(1, T, hq, d)
+    aff = _affine(hq, d)
+    r1 = oracle.forward_pt(qb, qo, k, v1, *aff, window=5)
+    r2 = oracle.forward_pt(qb, qo, k, v2, *aff, window=5)
+    r3 = oracle.forward_pt(qb, qo, k, 2.0 * v1 - 3.0 * v2, *aff, window=5)
+    for a, b, c in zip(r1, r2, r3):
+        np.testing.assert_allclose(c, 2.0 * a - 3.0 * b, atol=1e-12)
+
+
+def test_weights_form_a_distribution():
+    for n in (1, 2, 17, 300):
+        w = oracle.attention_weights(_rand(16) * 3, _rand(n, 16) * 3, 0.25)
+        assert np.all(w >= 0)
+        assert abs(w.sum() - 1.0) < 1e-12
+
+
+def test_pt_equals_prefill_then_decode():
+    """§3.2: the four regimes are one formulation; batch PT rows equal incremental rows."""
+    B, T, P0, hq, hkv, d, w = 2, 24, 9, 4, 2, 8, 5
+    qb, qo, k, v = _rand(B, T, hq, d), _rand(B, T, hq, d), _rand(B, T, hkv, d), _rand(B, T, hkv, d)
+    aff = _affine(hq, d)
+    ob, oo = oracle.forward_pt(qb, qo, k, v, *aff, window=w)
+    pb, po, ck, cv, ln = oracle.prefill(qb[:, :P0], qo[:, P0 - 1:P0], k[:, :P0], v[:, :P0], *aff,
+                                        window=w)
+    np.testing.assert_allclose(pb, ob[:, :P0], atol=1e-13)
+    np.testing.assert_allclose(po[:, 0], oo[:, P0 - 1], atol=1e-13)
+    hist_k, hist_v, lens = list(ck), list(cv), ln
+    for t in range(P0, T):
+        db, do, hist_k, hist_v, lens = oracle.decode_step(hist_k, hist_v, lens, qb[:, t], qo[:, t],
+                                                          k[:, t], v[:, t], *aff, window=w)
+        np.testing.assert_allclose(db, ob[:, t], atol=1e-13)
+        np.testing.assert_allclose(do, oo[:, t], atol=1e-13)
+    np.testing.assert_array_equal(np.stack(hist_k), k)
+
+
+def test_sft_rows_equal_pt_rows():
+    B, T, hq, hkv, d, w = 1, 20, 2, 1, 8, 4
+    qb, qo, k, v = _rand(B, T, hq, d), _rand(B, T, hq, d), _rand(B, T, hkv, d), _rand(B, T, hkv, d)
+    aff = _affine(hq, d)
+    ob, oo = oracle.forward_pt(qb, qo, k, v, *aff, window=w)
+    pos = [3, 11, 19]
+    sb, so = oracle.forward_sft(qb, qo[:, pos], k, v, pos, *aff, window=w)
+    np.testing.assert_allclose(sb, ob, atol=1e-13)
+    np.testing.assert_allclose(so, oo[:, pos], atol=1e-13)
+
+
+def test_planted_key_dominates_output_row():
+    P, hq, hkv, d, w = 400, 4, 2, 128, 16
+    qb, qo = _rand(1, P, hq, d), _rand(1, 1, hq, d)
+    k, v = _rand(1, P, hkv, d), _rand(1, P, hkv, d)
+    p = 37
+    G = hq // hkv
+    for g in range(hkv):
+        k[0, p, g] = qo[0, 0, g * G]
+    a, b = np.ones(hq * d), np.zeros(hq * d)
+    _, oo, *_ = oracle.prefill(qb, qo, k, v, a, b, a, b, window=w)
+    for g in range(hkv):
+        wts = oracle.attention_weights(qo[0, 0, g * G], k[0, :, g], oracle.default_scale(d))
+        assert int(np.argmax(wts)) == p
+        assert wts[p] > 0.5
+        np.testing.assert_allclose(oo[0, 0, g * G], wts @ v[0, :, g], atol=1e-12)
+
+
+def test_sampled_rows_match_full_evaluation():
+    """Row subsets (used for sampled checks at large sizes) equal the full evaluation."""
+    B, T, hq, hkv, d, w = 1, 30, 2, 2, 8, 7
+    qb, qo, k, v = _rand(B, T, hq, d), _rand(B, 1, hq, d), _rand(B, T, hkv, d), _rand(B, T, hkv, d)
+    aff = _affine(hq, d)
+    full = oracle.prefill(qb, qo, k, v, *aff, window=w)
+    part = oracle.prefill(qb, qo, k, v, *aff, window=w, rows=[0, 6, 7, 29])
+    for t in [0, 6, 7, 29]:
+        np.testing.assert_array_equal(part[0][:, t], full[0][:, t])
+    assert np.isnan(part[0][:, 1]).all()
