@@ -1,0 +1,403 @@
+// C ABI of liborthros.so: argument validation, workspace layout, kernel dispatch and the
+// optional per-stage timing. See include/orthros.h for the contract of every entry point.
+#include "orthros.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <climits>
+#include <cmath>
+#include <vector>
+
+#include "launch.h"
+
+using namespace orthros;
+
+namespace {
+
+constexpr int kMaxSplits = 64;     // split partials reserved per row in the workspace
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kSplitKeys = 4096;   // target keys per split for the few-row kernel
+constexpr size_t kStatusBytes = 256;
+
+struct WsLayout {
+  size_t pm, pl, po, total;
+};
+
+int64_t rows_max(const orthros_shape* s) { return (int64_t)s->batch * s->num_q_heads * 2; }
+
+WsLayout ws_layout(const orthros_shape* s) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  const size_t rows = (size_t)rows_max(s);
+  WsLayout L;
+  L.pm = kStatusBytes;
+  L.pl = L.pm + up(rows * kMaxSplits * sizeof(float));
+  L.po = L.pl + up(rows * kMaxSplits * sizeof(float));
+  L.total = L.po + up(rows * kMaxSplits * (size_t)s->head_dim * sizeof(float));
+  return L;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_shape(const orthros_shape* s) {
+  if (!s) return ORTHROS_E_INVALID;
+  if (s->batch < 1 || s->num_q_heads < 1 || s->num_kv_heads < 1 || s->window < 1 ||
+      s->capacity < 1 || s->reserved != 0)
+    return ORTHROS_E_INVALID;
+  if (s->num_q_heads % s->num_kv_heads) return ORTHROS_E_INVALID;
+  if (!(s->softmax_scale <= 0.f) && !std::isfinite(s->softmax_scale)) return ORTHROS_E_INVALID;
+  if (s->dtype != ORTHROS_F32 && s->dtype != ORTHROS_BF16) return ORTHROS_E_UNSUPPORTED;
+  if (s->head_dim != 64 && s->head_dim != 128) return ORTHROS_E_UNSUPPORTED;
+  if (s->batch > 65535) return ORTHROS_E_UNSUPPORTED;
+  return ORTHROS_OK;
+}
+
+int check_affine(const orthros_affine* a) {
+  if (!a) return ORTHROS_E_INVALID;
+  const void* ps[4] = {a->alpha_base, a->beta_base, a->alpha_out, a->beta_out};
+  for (const void* p : ps)
+    if (!p || !aligned16(p)) return ORTHROS_E_INVALID;
+  return ORTHROS_OK;
+}
+
+int check_ptrs(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (!p || !aligned16(p)) return ORTHROS_E_INVALID;
+  return ORTHROS_OK;
+}
+
+int check_ws(const orthros_shape* s, const void* ws, size_t bytes) {
+  if (!ws || !aligned16(ws)) return ORTHROS_E_WORKSPACE;
+  if (bytes < ws_layout(s).total) return ORTHROS_E_WORKSPACE;
+  return ORTHROS_OK;
+}
+
+float scale_of(const orthros_shape* s) {
+  return s->softmax_scale > 0.f ? s->softmax_scale : 1.f / std::sqrt((float)s->head_dim);
+}
+
+int esize(const orthros_shape* s) { return s->dtype == ORTHROS_BF16 ? 2 : 4; }
+
+// ---------------------------------------------------------------------------------------------
+// Optional timing: event pairs around every launch while enabled.
+struct TimingRec {
+  int stage;
+  hipEvent_t a, b;
+};
+struct Timing {
+  bool on = false;
+  std::vector<TimingRec> recs;
+} g_timing;
+
+template <class F>
+hipError_t run_stage(int stage, hipStream_t st, F&& f) {
+  if (!g_timing.on) return f();
+  TimingRec r{stage, nullptr, nullptr};
+  if (hipEventCreate(&r.a) != hipSuccess || hipEventCreate(&r.b) != hipSuccess) return hipErrorUnknown;
+  (void)hipEventRecord(r.a, st);
+  const hipError_t e = f();
+  (void)hipEventRecord(r.b, st);
+  g_timing.recs.push_back(r);
+  return e;
+}
+
+int launch_rc(hipError_t e) { return e == hipSuccess ? ORTHROS_OK : ORTHROS_E_LAUNCH; }
+
+int nsplit_for(int64_t n, int64_t groups) {
+  // Enough splits for a few work-groups per CU, each covering at least one key tile.
+  int64_t s = (n + kSplitKeys - 1) / kSplitKeys;
+  const int64_t want = (4 * 256 + groups - 1) / groups;  // ~4 groups per compute unit
+  if (s < want) s = want;
+  const int64_t tiles = (n + 63) / 64;
+  if (s > tiles) s = tiles;
+  if (s > kMaxSplits) s = kMaxSplits;
+  if (s < 1) s = 1;
+  return (int)s;
+}
+
+int heads_per_chunk(int G, bool with_base) {
+  const int cap = with_base ? 8 : 16;
+  return G < cap ? G : cap;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t orthros_workspace_bytes(const orthros_shape* shape) {
+  if (check_shape(shape) != ORTHROS_OK) return 0;
+  return ws_layout(shape).total;
+}
+
+const char* orthros_status_string(int code) {
+  switch (code) {
+    case ORTHROS_OK: return "ok";
+    case ORTHROS_E_INVALID: return "invalid argument";
+    case ORTHROS_E_UNSUPPORTED: return "unsupported dtype or shape";
+    case ORTHROS_E_WORKSPACE: return "workspace missing or too small";
+    case ORTHROS_E_CAPACITY: return "sequence longer than the cache capacity";
+    case ORTHROS_E_LAUNCH: return "HIP launch or runtime failure";
+    default: return "unknown status";
+  }
+}
+
+int orthros_prefill(const orthros_shape* s, int64_t P, const void* q_base, const void* q_out,
+                    const void* k, const void* v, const orthros_affine* aff, void* cache_k,
+                    void* cache_v, int32_t* cache_len, void* o_base, void* o_out, void* ws,
+                    size_t ws_bytes, hipStream_t st) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if (P < 1 || P > INT_MAX / 2) return ORTHROS_E_INVALID;
+  if ((rc = check_affine(aff))) return rc;
+  if ((rc = check_ptrs({q_base, q_out, k, v, cache_k, cache_v, cache_len, o_base, o_out}))) return rc;
+  if ((rc = check_ws(s, ws, ws_bytes))) return rc;
+  if (P > s->capacity) return ORTHROS_E_CAPACITY;
+
+  const int B = s->batch, Hq = s->num_q_heads, Hkv = s->num_kv_heads, d = s->head_dim;
+  const int G = Hq / Hkv;
+  const float scale = scale_of(s);
+  const WsLayout L = ws_layout(s);
+  char* wsc = static_cast<char*>(ws);
+
+  CacheWriteParams cw{k, v, cache_k, cache_v, cache_len, B, (int)P, Hkv, d, esize(s), s->capacity};
+  rc = launch_rc(run_stage(ORTHROS_STAGE_CACHE_WRITE, st, [&] { return launch_cache_write(cw, st); }));
+  if (rc) return rc;
+
+  if (s->dtype == ORTHROS_F32) {
+    RowsF32Params r{};
+    r.q = static_cast<const float*>(q_base);
+    r.q_sb = P * Hq * d; r.q_st = (idx_t)Hq * d; r.q_sh = d;
+    r.alpha = aff->alpha_base; r.beta = aff->beta_base;
+    r.k = static_cast<const float*>(k); r.v = static_cast<const float*>(v);
+    r.k_sb = P * Hkv * d; r.k_st = (idx_t)Hkv * d; r.k_sh = d;
+    r.o = static_cast<float*>(o_base);
+    r.o_sb = P * Hq * d; r.o_st = (idx_t)Hq * d; r.o_sh = d;
+    r.B = B; r.Hq = Hq; r.Hkv = Hkv; r.G = G; r.d = d; r.nrows = (int)P; r.t0 = 0;
+    r.window = s->window; r.scale = scale;
+    rc = launch_rc(run_stage(ORTHROS_STAGE_ROWS_F32, st, [&] { return launch_rows_f32(r, st); }));
+    if (rc) return rc;
+    RowsF32Params o = r;
+    o.q = static_cast<const float*>(q_out);
+    o.q_sb = (idx_t)Hq * d; o.q_st = 0;
+    o.alpha = aff->alpha_out; o.beta = aff->beta_out;
+    o.o = static_cast<float*>(o_out);
+    o.o_sb = (idx_t)Hq * d; o.o_st = 0;
+    o.nrows = 1; o.t0 = (int)(P - 1); o.window = INT_MAX;
+    return launch_rc(run_stage(ORTHROS_STAGE_ROWS_F32, st, [&] { return launch_rows_f32(o, st); }));
+  }
+
+  BandParams bp{};
+  bp.q = q_base; bp.q_sb = P * Hq * d; bp.q_st = (idx_t)Hq * d; bp.q_sh = d;
+  bp.alpha = aff->alpha_base; bp.beta = aff->beta_base;
+  bp.k = k; bp.v = v; bp.k_sb = P * Hkv * d; bp.k_st = (idx_t)Hkv * d; bp.k_sh = d;
+  bp.o = o_base; bp.o_sb = P * Hq * d; bp.o_st = (idx_t)Hq * d; bp.o_sh = d;
+  bp.B = B; bp.T = (int)P; bp.Hq = Hq; bp.Hkv = Hkv; bp.G = G;
+  bp.window = s->window < (int)P ? s->window : (int)P;
+  bp.scale_log2 = scale * kLog2e;
+  rc = launch_rc(run_stage(ORTHROS_STAGE_BAND, st, [&] { return launch_band(bp, d, st); }));
+  if (rc) return rc;
+
+  // Output row at the last prompt token over the freshly written cache (head-major).
+  SplitParams sp{};
+  sp.q_out = q_out; sp.q_sb = (idx_t)Hq * d; sp.q_sh = d;
+  sp.a_out = aff->alpha_out; sp.b_out = aff->beta_out;
+  sp.a_base = aff->alpha_base; sp.b_base = aff->beta_base;
+  sp.k = cache_k; sp.v = cache_v;
+  sp.k_sb = (idx_t)Hkv * s->capacity * d; sp.k_sh = s->capacity * d; sp.k_st = d;
+  sp.n_fixed = P;
+  sp.B = B; sp.Hq = Hq; sp.Hkv = Hkv; sp.G = G;
+  sp.HC = heads_per_chunk(G, false);
+  sp.nchunks = (G + sp.HC - 1) / sp.HC;
+  sp.window = s->window; sp.with_base = 0;
+  sp.nsplit = nsplit_for(P, (int64_t)B * Hkv * sp.nchunks);
+  sp.scale_log2 = scale * kLog2e;
+  sp.pm = reinterpret_cast<float*>(wsc + L.pm);
+  sp.pl = reinterpret_cast<float*>(wsc + L.pl);
+  sp.po = reinterpret_cast<float*>(wsc + L.po);
+  rc = launch_rc(run_stage(ORTHROS_STAGE_SPLIT_ROWS, st, [&] { return launch_split_rows(sp, d, st); }));
+  if (rc) return rc;
+  MergeParams mp{};
+  mp.pm = sp.pm; mp.pl = sp.pl; mp.po = sp.po;
+  mp.out0 = o_out; mp.o_sb0 = (idx_t)Hq * d; mp.o_sh0 = d;
+  mp.out1 = nullptr;
+  mp.rows = B * Hq; mp.nsplit = sp.nsplit; mp.d = d; mp.Hq = Hq; mp.nstreams = 1; mp.bf16 = 1;
+  return launch_rc(run_stage(ORTHROS_STAGE_MERGE, st, [&] { return launch_merge(mp, st); }));
+}
+
+int orthros_decode_step(const orthros_shape* s, const void* q_base, const void* q_out,
+                        const void* k_new, const void* v_new, const orthros_affine* aff,
+                        void* cache_k, void* cache_v, int32_t* cache_len, int64_t max_len_hint,
+                        void* o_base, void* o_out, void* ws, size_t ws_bytes, hipStream_t st) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if (max_len_hint < 0) return ORTHROS_E_INVALID;
+  if ((rc = check_affine(aff))) return rc;
+  if ((rc = check_ptrs({q_base, q_out, k_new, v_new, cache_k, cache_v, cache_len, o_base, o_out}))) return rc;
+  if ((rc = check_ws(s, ws, ws_bytes))) return rc;
+
+  const int B = s->batch, Hq = s->num_q_heads, Hkv = s->num_kv_heads, d = s->head_dim;
+  const int G = Hq / Hkv;
+  const float scale = scale_of(s);
+  const WsLayout L = ws_layout(s);
+  char* wsc = static_cast<char*>(ws);
+  int64_t hint = max_len_hint < s->capacity ? max_len_hint : s->capacity;
+
+  if (s->dtype == ORTHROS_F32) {
+    RowsF32Params r{};
+    r.q = static_cast<const float*>(q_base);
+    r.q_sb = (idx_t)Hq * d; r.q_st = 0; r.q_sh = d;
+    r.alpha = aff->alpha_base; r.beta = aff->beta_base;
+    r.k = static_cast<const float*>(cache_k); r.v = static_cast<const float*>(cache_v);
+    r.k_sb = (idx_t)Hkv * s->capacity * d; r.k_st = d; r.k_sh = s->capacity * d;
+    r.knew = static_cast<const float*>(k_new); r.vnew = static_cast<const float*>(v_new);
+    r.kn_sb = (idx_t)Hkv * d; r.kn_sh = d;
+    r.len = cache_len; r.cap = s->capacity;
+    r.o = static_cast<float*>(o_base); r.o_sb = (idx_t)Hq * d; r.o_st = 0; r.o_sh = d;
+    r.B = B; r.Hq = Hq; r.Hkv = Hkv; r.G = G; r.d = d; r.nrows = 1; r.t0 = 0;
+    r.window = s->window; r.scale = scale;
+    rc = launch_rc(run_stage(ORTHROS_STAGE_ROWS_F32, st, [&] { return launch_rows_f32(r, st); }));
+    if (rc) return rc;
+    RowsF32Params o = r;
+    o.q = static_cast<const float*>(q_out);
+    o.alpha = aff->alpha_out; o.beta = aff->beta_out;
+    o.o = static_cast<float*>(o_out);
+    o.window = INT_MAX;
+    rc = launch_rc(run_stage(ORTHROS_STAGE_ROWS_F32, st, [&] { return launch_rows_f32(o, st); }));
+    if (rc) return rc;
+  } else {
+    SplitParams sp{};
+    sp.q_out = q_out; sp.q_base = q_base; sp.q_sb = (idx_t)Hq * d; sp.q_sh = d;
+    sp.a_out = aff->alpha_out; sp.b_out = aff->beta_out;
+    sp.a_base = aff->alpha_base; sp.b_base = aff->beta_base;
+    sp.k = cache_k; sp.v = cache_v;
+    sp.k_sb = (idx_t)Hkv * s->capacity * d; sp.k_sh = s->capacity * d; sp.k_st = d;
+    sp.knew = k_new; sp.vnew = v_new; sp.kn_sb = (idx_t)Hkv * d; sp.kn_sh = d;
+    sp.len = cache_len; sp.cap = s->capacity;
+    sp.B = B; sp.Hq = Hq; sp.Hkv = Hkv; sp.G = G;
+    sp.HC = heads_per_chunk(G, true);
+    sp.nchunks = (G + sp.HC - 1) / sp.HC;
+    sp.window = s->window; sp.with_base = 1;
+    sp.nsplit = nsplit_for(hint + 1, (int64_t)B * Hkv * sp.nchunks);
+    sp.scale_log2 = scale * kLog2e;
+    sp.pm = reinterpret_cast<float*>(wsc + L.pm);
+    sp.pl = reinterpret_cast<float*>(wsc + L.pl);
+    sp.po = reinterpret_cast<float*>(wsc + L.po);
+    rc = launch_rc(run_stage(ORTHROS_STAGE_SPLIT_ROWS, st, [&] { return launch_split_rows(sp, d, st); }));
+    if (rc) return rc;
+    MergeParams mp{};
+    mp.pm = sp.pm; mp.pl = sp.pl; mp.po = sp.po;
+    mp.out0 = o_out; mp.o_sb0 = (idx_t)Hq * d; mp.o_sh0 = d;
+    mp.out1 = o_base; mp.o_sb1 = (idx_t)Hq * d; mp.o_sh1 = d;
+    mp.rows = B * Hq * 2; mp.nsplit = sp.nsplit; mp.d = d; mp.Hq = Hq; mp.nstreams = 2; mp.bf16 = 1;
+    rc = launch_rc(run_stage(ORTHROS_STAGE_MERGE, st, [&] { return launch_merge(mp, st); }));
+    if (rc) return rc;
+  }
+  AppendParams ap{k_new, v_new, cache_k, cache_v, cache_len,
+                  reinterpret_cast<int32_t*>(wsc), B, Hkv, d, esize(s), s->capacity};
+  return launch_rc(run_stage(ORTHROS_STAGE_APPEND, st, [&] { return launch_append(ap, st); }));
+}
+
+int orthros_forward_pt(const orthros_shape* s, int64_t T, const void* q_base, const void* q_out,
+                       const void* k, const void* v, const orthros_affine* aff, void* cache_k,
+                       void* cache_v, int32_t* cache_len, void* o_base, void* o_out, void* ws,
+                       size_t ws_bytes, hipStream_t st) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if (T < 1 || T > INT_MAX / 2) return ORTHROS_E_INVALID;
+  if ((rc = check_affine(aff))) return rc;
+  if ((rc = check_ptrs({q_base, q_out, k, v, o_base, o_out}))) return rc;
+  const bool any_cache = cache_k || cache_v || cache_len;
+  if (any_cache && (rc = check_ptrs({cache_k, cache_v, cache_len}))) return rc;
+  if ((rc = check_ws(s, ws, ws_bytes))) return rc;
+  if (any_cache && T > s->capacity) return ORTHROS_E_CAPACITY;
+
+  const int B = s->batch, Hq = s->num_q_heads, Hkv = s->num_kv_heads, d = s->head_dim;
+  const int G = Hq / Hkv;
+  const float scale = scale_of(s);
+
+  if (any_cache) {
+    CacheWriteParams cw{k, v, cache_k, cache_v, cache_len, B, (int)T, Hkv, d, esize(s), s->capacity};
+    rc = launch_rc(run_stage(ORTHROS_STAGE_CACHE_WRITE, st, [&] { return launch_cache_write(cw, st); }));
+    if (rc) return rc;
+  }
+
+  if (s->dtype == ORTHROS_F32) {
+    RowsF32Params r{};
+    r.q = static_cast<const float*>(q_base);
+    r.q_sb = T * Hq * d; r.q_st = (idx_t)Hq * d; r.q_sh = d;
+    r.alpha = aff->alpha_base; r.beta = aff->beta_base;
+    r.k = static_cast<const float*>(k); r.v = static_cast<const float*>(v);
+    r.k_sb = T * Hkv * d; r.k_st = (idx_t)Hkv * d; r.k_sh = d;
+    r.o = static_cast<float*>(o_base);
+    r.o_sb = T * Hq * d; r.o_st = (idx_t)Hq * d; r.o_sh = d;
+    r.B = B; r.Hq = Hq; r.Hkv = Hkv; r.G = G; r.d = d; r.nrows = (int)T; r.t0 = 0;
+    r.window = s->window; r.scale = scale;
+    rc = launch_rc(run_stage(ORTHROS_STAGE_ROWS_F32, st, [&] { return launch_rows_f32(r, st); }));
+    if (rc) return rc;
+    RowsF32Params o = r;
+    o.q = static_cast<const float*>(q_out);
+    o.alpha = aff->alpha_out; o.beta = aff->beta_out;
+    o.o = static_cast<float*>(o_out);
+    o.window = INT_MAX;
+    return launch_rc(run_stage(ORTHROS_STAGE_ROWS_F32, st, [&] { return launch_rows_f32(o, st); }));
+  }
+
+  BandParams bp{};
+  bp.q = q_base; bp.q_sb = T * Hq * d; bp.q_st = (idx_t)Hq * d; bp.q_sh = d;
+  bp.alpha = aff->alpha_base; bp.beta = aff->beta_base;
+  bp.k = k; bp.v = v; bp.k_sb = T * Hkv * d; bp.k_st = (idx_t)Hkv * d; bp.k_sh = d;
+  bp.o = o_base; bp.o_sb = T * Hq * d; bp.o_st = (idx_t)Hq * d; bp.o_sh = d;
+  bp.B = B; bp.T = (int)T; bp.Hq = Hq; bp.Hkv = Hkv; bp.G = G;
+  bp.window = s->window < (int)T ? s->window : (int)T;
+  bp.scale_log2 = scale * kLog2e;
+  rc = launch_rc(run_stage(ORTHROS_STAGE_BAND, st, [&] { return launch_band(bp, d, st); }));
+  if (rc) return rc;
+  BandParams op = bp;
+  op.q = q_out; op.alpha = aff->alpha_out; op.beta = aff->beta_out; op.o = o_out;
+  op.window = (int)T;  // window >= T: full causal rows (Eq. 5)
+  return launch_rc(run_stage(ORTHROS_STAGE_BAND, st, [&] { return launch_band(op, d, st); }));
+}
+
+int orthros_read_device_status(void* ws, size_t ws_bytes, int32_t* host_status, int clear,
+                               hipStream_t st) {
+  if (!ws || !host_status || ws_bytes < kStatusBytes) return ORTHROS_E_INVALID;
+  if (hipStreamSynchronize(st) != hipSuccess) return ORTHROS_E_LAUNCH;
+  if (hipMemcpy(host_status, ws, sizeof(int32_t), hipMemcpyDeviceToHost) != hipSuccess) return ORTHROS_E_LAUNCH;
+  if (clear) {
+    const int32_t zero = 0;
+    if (hipMemcpy(ws, &zero, sizeof(int32_t), hipMemcpyHostToDevice) != hipSuccess) return ORTHROS_E_LAUNCH;
+  }
+  return ORTHROS_OK;
+}
+
+int orthros_timing_begin(void) {
+  for (auto& r : g_timing.recs) {
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  g_timing.recs.clear();
+  g_timing.on = true;
+  return ORTHROS_OK;
+}
+
+int orthros_timing_end(double* stage_ms, int64_t* stage_launches) {
+  if (!stage_ms || !stage_launches) return ORTHROS_E_INVALID;
+  for (int i = 0; i < ORTHROS_NUM_STAGES; ++i) {
+    stage_ms[i] = 0.0;
+    stage_launches[i] = 0;
+  }
+  int rc = ORTHROS_OK;
+  for (auto& r : g_timing.recs) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess)
+      rc = ORTHROS_E_LAUNCH;
+    stage_ms[r.stage] += ms;
+    stage_launches[r.stage] += 1;
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  g_timing.recs.clear();
+  g_timing.on = false;
+  return rc;
+}
+
+}  // extern "C"

@@ -1,0 +1,322 @@
+// Split-key attention for a few query rows against a long key range, bf16 in, fp32 partials.
+//
+// Serves the output stream's full causal cross-attention ("Orthros: Phase-Aware Heterogeneous
+// Attention for Efficient Transformers", §3.1 Eq. 5) at the prediction positions, and in the
+// decoding regime (§3.2) the decoupled pair at once: for each (sequence, kv head) the output
+// copies of the G query heads (keys 0 .. L) and their base copies (Eq. 4, keys L-w+1 .. L) share
+// one pass over the key/value stream, so every cached byte is read once per step.
+//
+// Layout: one work-group (4 wavefronts) per (split, kv head x head chunk, sequence). The group
+// stages 64-key tiles of K (row-major) and V (transposed, key-contiguous) through LDS with a
+// double buffer; wavefront w owns keys 16w .. 16w+15 of each tile:
+//   S^T[16 keys x 16 rows] = K . Q^T    4 x mfma_f32_16x16x32_bf16 (d = 128)
+//   online softmax over the 16 keys     (exp2 domain; the query carries scale * log2 e)
+//   O^T[d x 16 rows]     += V^T . P^T   8 x mfma_f32_16x16x16_bf16 (P^T straight from S^T)
+// The four wavefronts' (max, sum, O) are merged in LDS and written as one fp32 partial per
+// row and split; merge_kernel combines the splits in a fixed order (deterministic).
+#include "common.h"
+#include "launch.h"
+
+namespace orthros {
+
+namespace {
+constexpr int kTK = 64;      // keys per tile
+constexpr int kRows = 16;    // query rows per work-group (MFMA N)
+
+template <int D>
+struct SplitSmem {
+  static constexpr int KSTR = D + 8;    // K tile row stride (elements), pads LDS banks
+  static constexpr int VSTR = kTK + 8;  // V^T tile row stride (elements)
+  static constexpr int KBUF = kTK * KSTR;
+  static constexpr int VBUF = D * VSTR;
+  static constexpr int TILE_BYTES = 2 * (KBUF + VBUF) * 2;
+  static constexpr int RED_BYTES = 4 * kRows * (D + 2) * 4;
+  static constexpr int BYTES = TILE_BYTES > RED_BYTES ? TILE_BYTES : RED_BYTES;
+};
+}  // namespace
+
+template <int D>
+__global__ __launch_bounds__(256) void split_rows_kernel(SplitParams p) {
+  using SM = SplitSmem<D>;
+  constexpr int KSTR = SM::KSTR, VSTR = SM::VSTR;
+  constexpr int NST = D / 32;   // QK k-steps (32 channels each)
+  constexpr int NMT = D / 16;   // PV output tiles (16 channels each)
+  constexpr int CPR = D / 8;    // 16-byte chunks per row
+  constexpr int KCH = kTK * CPR / 256;       // K chunks per thread
+  constexpr int VIT = (kTK / 2) * CPR / 256; // V (key pair, chunk) items per thread
+  __shared__ __attribute__((aligned(16))) unsigned char smem[SM::BYTES];
+  uint16_t* Ks = reinterpret_cast<uint16_t*>(smem);
+  uint16_t* Vt = Ks + 2 * SM::KBUF;
+
+  const int s = blockIdx.x;
+  const int g = blockIdx.y / p.nchunks;
+  const int chunk = blockIdx.y % p.nchunks;
+  const int b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int nstreams = p.with_base ? 2 : 1;
+
+  int64_t n, Lnew = -1;
+  if (p.len) {
+    // keys 0..L-1 come from the cache, key L from this step's input; a length outside
+    // [0, capacity] is clamped so no read leaves the cache
+    const int64_t L = p.len[b];
+    Lnew = L < 0 ? 0 : (L > p.cap ? p.cap : L);
+    n = Lnew + 1;
+  } else {
+    n = p.n_fixed;
+  }
+  int64_t per = (n + p.nsplit - 1) / p.nsplit;
+  per = (per + kTK - 1) / kTK * kTK;
+  const int64_t kb = (int64_t)s * per;
+  const int64_t ke = kb + per < n ? kb + per : n;
+
+  const int h0 = g * p.G + chunk * p.HC;
+  int nr = p.G - chunk * p.HC;
+  if (nr > p.HC) nr = p.HC;
+
+  // Row slot of this lane (MFMA column) and its key range.
+  const int j = lane & 15;
+  const int kg = lane >> 4;
+  int stream = -1, h = 0;
+  int64_t lo = 1, hi = 0;  // empty
+  if (j < nr) {
+    stream = 0;
+    h = h0 + j;
+    lo = 0;
+    hi = n - 1;
+  } else if (p.with_base && j < 2 * nr) {
+    stream = 1;
+    h = h0 + j - nr;
+    lo = n - p.window > 0 ? n - p.window : 0;
+    hi = n - 1;
+  }
+
+  // Query fragment (B operand of mfma 16x16x32): lane (j, kg) holds channels 32*st + 8*kg + e.
+  bf16x8 qf[NST];
+  {
+    const uint16_t* qsrc = nullptr;
+    const float *al = nullptr, *be = nullptr;
+    if (stream == 0) {
+      qsrc = reinterpret_cast<const uint16_t*>(p.q_out) + (idx_t)b * p.q_sb + (idx_t)h * p.q_sh;
+      al = p.a_out + (idx_t)h * D;
+      be = p.b_out + (idx_t)h * D;
+    } else if (stream == 1) {
+      qsrc = reinterpret_cast<const uint16_t*>(p.q_base) + (idx_t)b * p.q_sb + (idx_t)h * p.q_sh;
+      al = p.a_base + (idx_t)h * D;
+      be = p.b_base + (idx_t)h * D;
+    }
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+      const int c0 = 32 * st + 8 * kg;
+      u32x4 raw = {0u, 0u, 0u, 0u};
+      if (qsrc) raw = *reinterpret_cast<const u32x4*>(qsrc + c0);
+      bf16x8 f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t w = raw[e >> 1];
+        const float x = (e & 1) ? bf16_hi(w) : bf16_lo(w);
+        const float y = qsrc ? (al[c0 + e] * x + be[c0 + e]) * p.scale_log2 : 0.f;
+        f[e] = (__bf16)y;
+      }
+      qf[st] = f;
+    }
+  }
+
+  const uint16_t* kbase = reinterpret_cast<const uint16_t*>(p.k) + (idx_t)b * p.k_sb + (idx_t)g * p.k_sh;
+  const uint16_t* vbase = reinterpret_cast<const uint16_t*>(p.v) + (idx_t)b * p.k_sb + (idx_t)g * p.k_sh;
+  const uint16_t* knew = p.knew ? reinterpret_cast<const uint16_t*>(p.knew) + (idx_t)b * p.kn_sb + (idx_t)g * p.kn_sh : nullptr;
+  const uint16_t* vnew = p.vnew ? reinterpret_cast<const uint16_t*>(p.vnew) + (idx_t)b * p.kn_sb + (idx_t)g * p.kn_sh : nullptr;
+
+  auto krow = [&](int64_t key) -> const uint16_t* {
+    if (key >= ke) key = ke - 1;
+    return key == Lnew ? knew : kbase + key * p.k_st;
+  };
+  auto vrow = [&](int64_t key) -> const uint16_t* {
+    if (key >= ke) key = ke - 1;
+    return key == Lnew ? vnew : vbase + key * p.k_st;
+  };
+
+  f32x4 O[NMT];
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt) O[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = kNegInf, l = 0.f;
+
+  if (kb < ke) {
+    u32x4 kreg[KCH], vreg[VIT][2];
+    auto load_tile = [&](int64_t t0) {
+#pragma unroll
+      for (int i = 0; i < KCH; ++i) {
+        const int ci = tid + 256 * i;
+        const int r = ci / CPR, c = ci % CPR;
+        kreg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(krow(t0 + r) + 8 * c));
+      }
+#pragma unroll
+      for (int i = 0; i < VIT; ++i) {
+        const int it = tid + 256 * i;
+        const int c = it % CPR, kp = it / CPR;
+        vreg[i][0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vrow(t0 + 2 * kp) + 8 * c));
+        vreg[i][1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vrow(t0 + 2 * kp + 1) + 8 * c));
+      }
+    };
+    auto store_tile = [&](int buf) {
+      uint16_t* ks = Ks + buf * SM::KBUF;
+      uint16_t* vt = Vt + buf * SM::VBUF;
+#pragma unroll
+      for (int i = 0; i < KCH; ++i) {
+        const int ci = tid + 256 * i;
+        const int r = ci / CPR, c = ci % CPR;
+        *reinterpret_cast<u32x4*>(ks + r * KSTR + 8 * c) = kreg[i];
+      }
+#pragma unroll
+      for (int i = 0; i < VIT; ++i) {
+        const int it = tid + 256 * i;
+        const int c = it % CPR, kp = it / CPR;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t a = vreg[i][0][e >> 1], bb = vreg[i][1][e >> 1];
+          const uint32_t w = (e & 1) ? ((a >> 16) | (bb & 0xffff0000u)) : ((a & 0xffffu) | (bb << 16));
+          *reinterpret_cast<uint32_t*>(vt + (8 * c + e) * VSTR + 2 * kp) = w;
+        }
+      }
+    };
+
+    load_tile(kb);
+    int buf = 0;
+    for (int64_t t0 = kb; t0 < ke; t0 += kTK) {
+      store_tile(buf);
+      __syncthreads();
+      if (t0 + kTK < ke) load_tile(t0 + kTK);
+      const int64_t wk0 = t0 + 16 * wv;  // this wavefront's first key
+      if (wk0 < ke) {
+        const uint16_t* ks = Ks + buf * SM::KBUF;
+        const uint16_t* vt = Vt + buf * SM::VBUF;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < NST; ++st) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + (16 * wv + j) * KSTR + 32 * st + 8 * kg);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[st], acc, 0, 0, 0);
+        }
+        float sc[4];
+        float mx = kNegInf;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t key = wk0 + 4 * kg + r;
+          const bool ok = key < ke && key >= lo && key <= hi;
+          sc[r] = ok ? acc[r] : kNegInf;
+          mx = fmaxf(mx, sc[r]);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float mn = fmaxf(m, mx);
+        const float alpha = mn == kNegInf ? 1.f : fast_exp2(m - mn);
+        const float ms = mn == kNegInf ? 0.f : mn;
+        float ps = 0.f;
+        s16x4 pb;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float pr = fast_exp2(sc[r] - ms);
+          ps += pr;
+          pb[r] = (short)f32_to_bf16(pr);
+        }
+        l = l * alpha + ps;
+        m = mn;
+#pragma unroll
+        for (int mt = 0; mt < NMT; ++mt) {
+          O[mt] *= alpha;
+          const s16x4 a = *reinterpret_cast<const s16x4*>(vt + (16 * mt + j) * VSTR + 16 * wv + 4 * kg);
+          O[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb, O[mt], 0, 0, 0);
+        }
+      }
+      buf ^= 1;
+    }
+  }
+
+  // Sum of this wavefront's per-lane partial denominators over the 4 lanes of each row.
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+
+  // Merge the 4 wavefronts in LDS: red[w] = {m[16], l[16], O[16][D]}.
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(smem);
+  constexpr int RW = kRows * (D + 2);
+  float* rw = red + wv * RW;
+  if (kg == 0) {
+    rw[j] = m;
+    rw[kRows + j] = l;
+  }
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) rw[2 * kRows + j * D + 16 * mt + 4 * kg + r] = O[mt][r];
+  __syncthreads();
+
+  const int nvalid = p.with_base ? 2 * nr : nr;
+  for (int e = tid; e < nvalid * D; e += 256) {
+    const int jj = e / D, c = e % D;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, red[w * RW + jj]);
+    float o = 0.f, den = 0.f;
+    if (M != kNegInf) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float f = fast_exp2(red[w * RW + jj] - M);
+        o += f * red[w * RW + 2 * kRows + jj * D + c];
+        den += f * red[w * RW + kRows + jj];
+      }
+    }
+    const int st = jj < nr ? 0 : 1;
+    const int hh = h0 + (jj < nr ? jj : jj - nr);
+    const idx_t row = ((idx_t)b * p.Hq + hh) * nstreams + st;
+    p.po[(row * p.nsplit + s) * D + c] = o;
+    if (c == 0) {
+      p.pm[row * p.nsplit + s] = M;
+      p.pl[row * p.nsplit + s] = den;
+    }
+  }
+}
+
+// Combine the split partials of one row: O = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
+__global__ __launch_bounds__(64) void merge_kernel(MergeParams p) {
+  const idx_t row = blockIdx.x;
+  const int st = (int)(row % p.nstreams);
+  const idx_t bh = row / p.nstreams;
+  const int h = (int)(bh % p.Hq);
+  const idx_t b = bh / p.Hq;
+  const float* pm = p.pm + row * p.nsplit;
+  const float* pl = p.pl + row * p.nsplit;
+  float M = kNegInf;
+  for (int s = 0; s < p.nsplit; ++s) M = fmaxf(M, pm[s]);
+  float den = 0.f;
+  for (int s = 0; s < p.nsplit; ++s) den += pm[s] == kNegInf ? 0.f : fast_exp2(pm[s] - M) * pl[s];
+  const float inv = 1.f / den;
+  void* out = st == 0 ? p.out0 : p.out1;
+  const idx_t off = st == 0 ? b * p.o_sb0 + (idx_t)h * p.o_sh0 : b * p.o_sb1 + (idx_t)h * p.o_sh1;
+  for (int c = threadIdx.x; c < p.d; c += blockDim.x) {
+    float o = 0.f;
+    for (int s = 0; s < p.nsplit; ++s) {
+      if (pm[s] != kNegInf) o += fast_exp2(pm[s] - M) * p.po[(row * p.nsplit + s) * p.d + c];
+    }
+    o *= inv;
+    if (p.bf16)
+      reinterpret_cast<uint16_t*>(out)[off + c] = f32_to_bf16(o);
+    else
+      reinterpret_cast<float*>(out)[off + c] = o;
+  }
+}
+
+hipError_t launch_split_rows(const SplitParams& p, int d, hipStream_t s) {
+  dim3 grid(p.nsplit, p.Hkv * p.nchunks, p.B);
+  if (d == 128)
+    hipLaunchKernelGGL(split_rows_kernel<128>, grid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(split_rows_kernel<64>, grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const MergeParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(merge_kernel, dim3(p.rows), dim3(64), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace orthros

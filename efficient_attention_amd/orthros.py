@@ -1,0 +1,254 @@
+"""ctypes binding of liborthros.so (declared in include/orthros.h).
+
+Argument marshalling only: every entry point checks that the torch tensors it is handed have
+the shape, dtype, device and layout the C ABI documents, then passes raw device pointers and
+the current HIP stream. All arithmetic runs in the library's HIP kernels. If the library is not
+built the first call raises; nothing here falls back to another implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+__all__ = [
+    "OK", "E_INVALID", "E_UNSUPPORTED", "E_WORKSPACE", "E_CAPACITY", "E_LAUNCH",
+    "STATUS_CACHE_FULL", "STAGES", "OrthrosError", "Shape", "Affine", "lib", "library_path",
+    "workspace_bytes", "make_workspace", "prefill", "decode_step", "forward_pt",
+    "read_device_status", "status_string", "timing_begin", "timing_end", "EXPORTED_SYMBOLS",
+]
+
+OK, E_INVALID, E_UNSUPPORTED, E_WORKSPACE, E_CAPACITY, E_LAUNCH = 0, -1, -2, -3, -4, -5
+STATUS_CACHE_FULL = 1
+F32, BF16 = 0, 1
+STAGES = ("cache_write", "band", "split_rows", "merge", "append", "rows_f32")
+EXPORTED_SYMBOLS = (
+    "orthros_workspace_bytes", "orthros_prefill", "orthros_decode_step", "orthros_forward_pt",
+    "orthros_read_device_status", "orthros_status_string", "orthros_timing_begin",
+    "orthros_timing_end",
+)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+class OrthrosError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {status_string(code)} ({code})")
+        self.code = code
+
+
+class _CShape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("window", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("capacity", ctypes.c_int64), ("softmax_scale", ctypes.c_float),
+                ("reserved", ctypes.c_int32)]
+
+
+class _CAffine(ctypes.Structure):
+    _fields_ = [("alpha_base", ctypes.c_void_p), ("beta_base", ctypes.c_void_p),
+                ("alpha_out", ctypes.c_void_p), ("beta_out", ctypes.c_void_p)]
+
+
+def library_path() -> str:
+    return os.environ.get("ORTHROS_LIB", os.path.join(_HERE, "liborthros.so"))
+
+
+def lib() -> ctypes.CDLL:
+    """Load liborthros.so (raises if it has not been built)."""
+    global _LIB
+    if _LIB is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with "
+                               "`python -c 'import __graft_entry__ as g; g.build()'`")
+        L = ctypes.CDLL(path)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        sp, ap = ctypes.POINTER(_CShape), ctypes.POINTER(_CAffine)
+        L.orthros_workspace_bytes.argtypes = [sp]
+        L.orthros_workspace_bytes.restype = sz
+        L.orthros_prefill.argtypes = [sp, i64, vp, vp, vp, vp, ap, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.orthros_prefill.restype = ctypes.c_int
+        L.orthros_decode_step.argtypes = [sp, vp, vp, vp, vp, ap, vp, vp, vp, i64, vp, vp, vp, sz, vp]
+        L.orthros_decode_step.restype = ctypes.c_int
+        L.orthros_forward_pt.argtypes = [sp, i64, vp, vp, vp, vp, ap, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.orthros_forward_pt.restype = ctypes.c_int
+        L.orthros_read_device_status.argtypes = [vp, sz, ctypes.POINTER(i32), ctypes.c_int, vp]
+        L.orthros_read_device_status.restype = ctypes.c_int
+        L.orthros_status_string.argtypes = [ctypes.c_int]
+        L.orthros_status_string.restype = ctypes.c_char_p
+        L.orthros_timing_begin.argtypes = []
+        L.orthros_timing_begin.restype = ctypes.c_int
+        L.orthros_timing_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
+        L.orthros_timing_end.restype = ctypes.c_int
+        _LIB = L
+    return _LIB
+
+
+def status_string(code: int) -> str:
+    return lib().orthros_status_string(int(code)).decode()
+
+
+@dataclass(frozen=True)
+class Shape:
+    """Problem shape (the C struct orthros_shape)."""
+    batch: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    window: int
+    dtype: torch.dtype
+    capacity: int
+    softmax_scale: float = 0.0
+
+    def c(self) -> _CShape:
+        code = {torch.float32: F32, torch.bfloat16: BF16}.get(self.dtype, 99)
+        return _CShape(self.batch, self.num_q_heads, self.num_kv_heads, self.head_dim,
+                       self.window, code, self.capacity, self.softmax_scale, 0)
+
+
+@dataclass(frozen=True)
+class Affine:
+    """Scale-offset vectors, fp32 [num_q_heads * head_dim] device tensors."""
+    alpha_base: torch.Tensor
+    beta_base: torch.Tensor
+    alpha_out: torch.Tensor
+    beta_out: torch.Tensor
+
+    def c(self, n: int, device) -> _CAffine:
+        for t in (self.alpha_base, self.beta_base, self.alpha_out, self.beta_out):
+            _check(t, (n,), torch.float32, device, "scale-offset vector")
+        return _CAffine(self.alpha_base.data_ptr(), self.beta_base.data_ptr(),
+                        self.alpha_out.data_ptr(), self.beta_out.data_ptr())
+
+
+def _check(t, shape, dtype, device, what):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{what}: expected {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{what}: expected device {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _rc(code: int, what: str):
+    if code != OK:
+        raise OrthrosError(code, what)
+
+
+def workspace_bytes(shape: Shape) -> int:
+    return int(lib().orthros_workspace_bytes(ctypes.byref(shape.c())))
+
+
+def make_workspace(shape: Shape, device) -> torch.Tensor:
+    """A zero-filled workspace (the status word must start at 0)."""
+    n = workspace_bytes(shape)
+    if n == 0:
+        raise OrthrosError(E_INVALID, "workspace_bytes")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def prefill(shape: Shape, q_base, q_out, k, v, affine: Affine, cache_k, cache_v, cache_len,
+            o_base, o_out, workspace, stream=None):
+    """orthros_prefill: base rows over the prompt, one output row at its last token."""
+    B, Hq, Hkv, d = shape.batch, shape.num_q_heads, shape.num_kv_heads, shape.head_dim
+    P = q_base.shape[1]
+    dev, dt = q_base.device, shape.dtype
+    _check(q_base, (B, P, Hq, d), dt, dev, "q_base")
+    _check(q_out, (B, 1, Hq, d), dt, dev, "q_out")
+    _check(k, (B, P, Hkv, d), dt, dev, "k")
+    _check(v, (B, P, Hkv, d), dt, dev, "v")
+    _check(cache_k, (B, Hkv, shape.capacity, d), dt, dev, "cache_k")
+    _check(cache_v, (B, Hkv, shape.capacity, d), dt, dev, "cache_v")
+    _check(cache_len, (B,), torch.int32, dev, "cache_len")
+    _check(o_base, (B, P, Hq, d), dt, dev, "o_base")
+    _check(o_out, (B, 1, Hq, d), dt, dev, "o_out")
+    aff = affine.c(Hq * d, dev)
+    rc = lib().orthros_prefill(
+        ctypes.byref(shape.c()), P, q_base.data_ptr(), q_out.data_ptr(), k.data_ptr(),
+        v.data_ptr(), ctypes.byref(aff), cache_k.data_ptr(), cache_v.data_ptr(),
+        cache_len.data_ptr(), o_base.data_ptr(), o_out.data_ptr(), workspace.data_ptr(),
+        workspace.numel(), _stream(stream))
+    _rc(rc, "orthros_prefill")
+
+
+def decode_step(shape: Shape, q_base, q_out, k_new, v_new, affine: Affine, cache_k, cache_v,
+                cache_len, max_len_hint: int, o_base, o_out, workspace, stream=None):
+    """orthros_decode_step: one decoupled base/output pair per sequence."""
+    B, Hq, Hkv, d = shape.batch, shape.num_q_heads, shape.num_kv_heads, shape.head_dim
+    dev, dt = q_base.device, shape.dtype
+    _check(q_base, (B, Hq, d), dt, dev, "q_base")
+    _check(q_out, (B, Hq, d), dt, dev, "q_out")
+    _check(k_new, (B, Hkv, d), dt, dev, "k_new")
+    _check(v_new, (B, Hkv, d), dt, dev, "v_new")
+    _check(cache_k, (B, Hkv, shape.capacity, d), dt, dev, "cache_k")
+    _check(cache_v, (B, Hkv, shape.capacity, d), dt, dev, "cache_v")
+    _check(cache_len, (B,), torch.int32, dev, "cache_len")
+    _check(o_base, (B, Hq, d), dt, dev, "o_base")
+    _check(o_out, (B, Hq, d), dt, dev, "o_out")
+    aff = affine.c(Hq * d, dev)
+    rc = lib().orthros_decode_step(
+        ctypes.byref(shape.c()), q_base.data_ptr(), q_out.data_ptr(), k_new.data_ptr(),
+        v_new.data_ptr(), ctypes.byref(aff), cache_k.data_ptr(), cache_v.data_ptr(),
+        cache_len.data_ptr(), int(max_len_hint), o_base.data_ptr(), o_out.data_ptr(),
+        workspace.data_ptr(), workspace.numel(), _stream(stream))
+    _rc(rc, "orthros_decode_step")
+
+
+def forward_pt(shape: Shape, q_base, q_out, k, v, affine: Affine, o_base, o_out, workspace,
+               cache_k=None, cache_v=None, cache_len=None, stream=None):
+    """orthros_forward_pt: every position duplicated (pre-training regime)."""
+    B, Hq, Hkv, d = shape.batch, shape.num_q_heads, shape.num_kv_heads, shape.head_dim
+    T = q_base.shape[1]
+    dev, dt = q_base.device, shape.dtype
+    _check(q_base, (B, T, Hq, d), dt, dev, "q_base")
+    _check(q_out, (B, T, Hq, d), dt, dev, "q_out")
+    _check(k, (B, T, Hkv, d), dt, dev, "k")
+    _check(v, (B, T, Hkv, d), dt, dev, "v")
+    _check(o_base, (B, T, Hq, d), dt, dev, "o_base")
+    _check(o_out, (B, T, Hq, d), dt, dev, "o_out")
+    ck = cv = cl = 0
+    if cache_k is not None or cache_v is not None or cache_len is not None:
+        _check(cache_k, (B, Hkv, shape.capacity, d), dt, dev, "cache_k")
+        _check(cache_v, (B, Hkv, shape.capacity, d), dt, dev, "cache_v")
+        _check(cache_len, (B,), torch.int32, dev, "cache_len")
+        ck, cv, cl = cache_k.data_ptr(), cache_v.data_ptr(), cache_len.data_ptr()
+    aff = affine.c(Hq * d, dev)
+    rc = lib().orthros_forward_pt(
+        ctypes.byref(shape.c()), T, q_base.data_ptr(), q_out.data_ptr(), k.data_ptr(),
+        v.data_ptr(), ctypes.byref(aff), ck or None, cv or None, cl or None, o_base.data_ptr(),
+        o_out.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(stream))
+    _rc(rc, "orthros_forward_pt")
+
+
+def read_device_status(workspace, clear: bool = False, stream=None) -> int:
+    out = ctypes.c_int32(0)
+    rc = lib().orthros_read_device_status(workspace.data_ptr(), workspace.numel(),
+                                          ctypes.byref(out), int(bool(clear)), _stream(stream))
+    _rc(rc, "orthros_read_device_status")
+    return int(out.value)
+
+
+def timing_begin():
+    _rc(lib().orthros_timing_begin(), "orthros_timing_begin")
+
+
+def timing_end():
+    """Returns {stage: (total_ms, launches)} for the calls since timing_begin()."""
+    ms = (ctypes.c_double * len(STAGES))()
+    n = (ctypes.c_int64 * len(STAGES))()
+    _rc(lib().orthros_timing_end(ms, n), "orthros_timing_end")
+    return {name: (ms[i], int(n[i])) for i, name in enumerate(STAGES)}

@@ -1,0 +1,174 @@
+/*
+ * orthros.h — C ABI of the MI355X (gfx950) Orthros attention hot path (liborthros.so).
+ *
+ * Method: "Orthros: Phase-Aware Heterogeneous Attention for Efficient Transformers".
+ *   - Base stream (§3.1 Eq. 4): every base token t attends, with its base query
+ *     q_t = alpha (.) q_raw_t + beta, to the w most recent keys max(0, t-w+1) .. t (0-based,
+ *     itself included) and appends its key/value to a full, never-evicted cache.
+ *   - Output stream (§3.1 Eq. 5): tokens duplicated at prediction positions attend, with the
+ *     output query q'_t = alpha' (.) q'_raw_t + beta', to every key 0 .. t; they never write
+ *     keys or values.
+ *   - Regimes (§3.2): pre-training duplicates every position (orthros_forward_pt);
+ *     prefilling runs the base stream over the prompt and one output row at the last prompt
+ *     token (orthros_prefill); decoding processes one new token per sequence as a base copy
+ *     (cache append + window) and an output copy (full history) (orthros_decode_step).
+ * The key/value and query projections (x W_K, x W_V, x W_Q) and the output projection are the
+ * caller's: the library starts from head-split projections (Algorithm 1, the split-heads step)
+ * and returns the per-head outputs of the two attention calls, before the heads are merged.
+ *
+ * Conventions shared by every call
+ *   - Pointers are device pointers on the current HIP device unless a parameter says "host".
+ *     The caller owns and allocates every buffer, including the workspace; the library never
+ *     allocates, frees or keeps device memory between calls.
+ *   - Every call only enqueues work on `stream` (0 = the null stream) and returns; none
+ *     synchronises except orthros_read_device_status and orthros_timing_end.
+ *   - Tensors are dense and row-major with the shapes given. Queries/keys/values/outputs use
+ *     the head-split layout [batch, tokens, heads, head_dim]. The cache is head-major:
+ *     cache_k/cache_v [batch, kv_heads, capacity, head_dim], so each (sequence, kv head)
+ *     history is one contiguous stream. cache_len is int32 [batch].
+ *   - Element type: shape.dtype for q/k/v/o/cache (fp32 or bf16). Scale-offset vectors are
+ *     always fp32 [num_q_heads * head_dim] (one entry per query head and channel).
+ *   - Grouped queries: query head h reads kv head h / (num_q_heads / num_kv_heads).
+ *   - Every pointer must be 16-byte aligned. Outputs must not alias inputs.
+ *   - bf16 arithmetic: scale-offset in fp32, the query rounded once to bf16 for the matrix
+ *     cores, scores and softmax in fp32, probabilities rounded once to bf16 for the value
+ *     product, fp32 accumulation, output rounded once to bf16 (round to nearest even).
+ *     fp32 calls compute every step in fp32.
+ *   - Return value: ORTHROS_OK (0) or a negative ORTHROS_E_* code. Arguments are validated
+ *     before anything is enqueued, so a call that returns an argument error has no effect.
+ */
+#ifndef ORTHROS_H
+#define ORTHROS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ORTHROS_F32 = 0,
+  ORTHROS_BF16 = 1
+} orthros_dtype;
+
+enum {
+  ORTHROS_OK = 0,
+  ORTHROS_E_INVALID = -1,      /* null pointer, non-positive size, misaligned pointer, ... */
+  ORTHROS_E_UNSUPPORTED = -2,  /* dtype / head_dim / head-group combination not built */
+  ORTHROS_E_WORKSPACE = -3,    /* workspace missing or smaller than orthros_workspace_bytes */
+  ORTHROS_E_CAPACITY = -4,     /* prompt longer than the cache capacity */
+  ORTHROS_E_LAUNCH = -5        /* a HIP launch or runtime call failed */
+};
+
+/* Sticky device status bits, read with orthros_read_device_status. */
+enum {
+  ORTHROS_STATUS_CACHE_FULL = 1  /* a decode step found cache_len == capacity: its token was
+                                    not appended (its attention outputs are still exact) */
+};
+
+/* Problem shape, passed by host pointer. */
+typedef struct {
+  int32_t batch;          /* sequences, >= 1 */
+  int32_t num_q_heads;    /* H_q >= 1 */
+  int32_t num_kv_heads;   /* H_kv >= 1, divides H_q */
+  int32_t head_dim;       /* d: 64 or 128 */
+  int32_t window;         /* w >= 1: keys t-w+1 .. t (Eq. 4); w >= T is plain causal */
+  int32_t dtype;          /* orthros_dtype */
+  int64_t capacity;       /* cache slots per (sequence, kv head), >= 1 */
+  float softmax_scale;    /* score scale; <= 0 selects 1/sqrt(head_dim) */
+  int32_t reserved;       /* must be 0 */
+} orthros_shape;
+
+/* Scale-offset vectors of §3.1 (device pointers, fp32 [num_q_heads * head_dim] each). */
+typedef struct {
+  const float* alpha_base;
+  const float* beta_base;
+  const float* alpha_out;
+  const float* beta_out;
+} orthros_affine;
+
+/* Bytes of workspace every call on this shape needs (0 if the shape is invalid). The
+ * workspace holds split partials and the sticky status word; zero-fill it once when it is
+ * allocated (the status word must start at 0), and never share it between calls that may run
+ * concurrently. */
+size_t orthros_workspace_bytes(const orthros_shape* shape);
+
+/* Prefilling regime (§3.2, T_in = P-1, T_out = 1).
+ *   q_base  [B, P, H_q, d]   base-stream raw queries (before the scale-offset)
+ *   q_out   [B, 1, H_q, d]   raw query of the duplicated last prompt token
+ *   k, v    [B, P, H_kv, d]  keys/values of the prompt
+ *   cache_k, cache_v         [B, H_kv, capacity, d]: rows 0..P-1 are overwritten with k, v
+ *   cache_len [B]            set to P
+ *   o_base  [B, P, H_q, d]   Eq. 4 for every prompt position
+ *   o_out   [B, 1, H_q, d]   Eq. 5 at position P-1 (keys 0..P-1)
+ * Requires 1 <= P <= capacity. */
+int orthros_prefill(const orthros_shape* shape, int64_t P,
+                    const void* q_base, const void* q_out, const void* k, const void* v,
+                    const orthros_affine* affine,
+                    void* cache_k, void* cache_v, int32_t* cache_len,
+                    void* o_base, void* o_out,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Decoding regime (§3.2, one new token per sequence).
+ * For each sequence b with L = cache_len[b] (read on the device):
+ *   the base copy attends over keys max(0, L-w+1) .. L and the output copy over 0 .. L,
+ *   where key L is this step's (k_new, v_new); then (k_new, v_new) is written to cache row L
+ *   and cache_len[b] becomes L+1. If L == capacity the attention outputs are still computed
+ *   (over the L cached keys plus the new one) but nothing is appended, cache_len is left as
+ *   is, and ORTHROS_STATUS_CACHE_FULL is set in the workspace's status word.
+ *   q_base, q_out  [B, H_q, d];  k_new, v_new [B, H_kv, d];  o_base, o_out [B, H_q, d]
+ *   max_len_hint   host upper bound on max_b cache_len[b] before the step; it only sizes the
+ *                  split grid (any value >= 1 is correct; a close bound is fastest). */
+int orthros_decode_step(const orthros_shape* shape,
+                        const void* q_base, const void* q_out,
+                        const void* k_new, const void* v_new,
+                        const orthros_affine* affine,
+                        void* cache_k, void* cache_v, int32_t* cache_len,
+                        int64_t max_len_hint,
+                        void* o_base, void* o_out,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Pre-training regime (§3.2, T_in = 0, T_out = T): every position duplicated.
+ *   q_base, q_out [B, T, H_q, d]; k, v [B, T, H_kv, d]; o_base, o_out [B, T, H_q, d]
+ *   o_base[t] is Eq. 4 with q_base[t]; o_out[t] is Eq. 5 with q_out[t].
+ *   cache_k/cache_v/cache_len: optional (all NULL, or all set with T <= capacity); when set,
+ *   rows 0..T-1 receive k, v and cache_len is set to T. */
+int orthros_forward_pt(const orthros_shape* shape, int64_t T,
+                       const void* q_base, const void* q_out, const void* k, const void* v,
+                       const orthros_affine* affine,
+                       void* cache_k, void* cache_v, int32_t* cache_len,
+                       void* o_base, void* o_out,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Copies the workspace's sticky status word to *host_status (host pointer) after draining
+ * `stream`; clears it on the device afterwards when `clear` is non-zero. Synchronous. */
+int orthros_read_device_status(void* workspace, size_t workspace_bytes, int32_t* host_status,
+                               int clear, hipStream_t stream);
+
+/* Static, human-readable text for a return code. */
+const char* orthros_status_string(int code);
+
+/* Optional kernel timing. After orthros_timing_begin(), every call records a pair of HIP
+ * events around each kernel it launches, on the call's stream. orthros_timing_end() waits for
+ * them and writes, per stage, the summed milliseconds and the launch count (host arrays of
+ * ORTHROS_NUM_STAGES entries), then stops recording. Host-side state; not thread-safe. */
+enum {
+  ORTHROS_STAGE_CACHE_WRITE = 0,  /* bulk cache write (prefill / pt) */
+  ORTHROS_STAGE_BAND = 1,         /* banded flash kernel (Eq. 4 windows, Eq. 5 causal rows) */
+  ORTHROS_STAGE_SPLIT_ROWS = 2,   /* split-key few-row kernel (output rows, decode pair) */
+  ORTHROS_STAGE_MERGE = 3,        /* split merge */
+  ORTHROS_STAGE_APPEND = 4,       /* decode append + length update */
+  ORTHROS_STAGE_ROWS_F32 = 5,     /* fp32 row kernel */
+  ORTHROS_NUM_STAGES = 6
+};
+int orthros_timing_begin(void);
+int orthros_timing_end(double* stage_ms, int64_t* stage_launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ORTHROS_H */

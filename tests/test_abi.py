@@ -1,0 +1,149 @@
+"""CPU checks of the C ABI: the library loads, exports every function include/orthros.h
+declares, and rejects bad arguments before enqueuing anything.
+
+Every call below carries exactly one defect, so it returns at validation and never reaches a
+kernel launch (fake pointers are never dereferenced)."""
+import ctypes
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+from efficient_attention_amd import orthros as ox
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "orthros.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(ox.library_path()),
+                                reason="liborthros.so not built")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(orthros_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_symbols():
+    assert header_functions() == sorted(ox.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", ox.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (orthros_[a-z_]+)$", out, flags=re.M))
+    missing = set(header_functions()) - exported
+    assert not missing, f"declared but not exported: {missing}"
+    L = ox.lib()
+    for name in header_functions():
+        assert hasattr(L, name)
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    code = ("import os; os.environ['ORTHROS_LIB'] = %r\n"
+            "from efficient_attention_amd import orthros as ox\n"
+            "try:\n    ox.lib()\nexcept RuntimeError as e:\n    print('raised', e)\n" %
+            str(tmp_path / "nope.so"))
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT)
+    assert "raised" in r.stdout
+
+
+def _shape(**kw):
+    base = dict(batch=2, num_q_heads=8, num_kv_heads=2, head_dim=128, window=16, dtype=1,
+                capacity=1024, softmax_scale=0.0, reserved=0)
+    base.update(kw)
+    return ox._CShape(**{k: base[k] for k, _ in ox._CShape._fields_})
+
+
+FAKE = 1 << 20  # 16-byte aligned, never dereferenced
+
+
+def _aff(**kw):
+    a = dict(alpha_base=FAKE, beta_base=FAKE, alpha_out=FAKE, beta_out=FAKE)
+    a.update(kw)
+    return ox._CAffine(**a)
+
+
+def _prefill(shape, P=64, aff=None, ws_bytes=None, **ptrs):
+    p = dict(q_base=FAKE, q_out=FAKE, k=FAKE, v=FAKE, cache_k=FAKE, cache_v=FAKE, cache_len=FAKE,
+             o_base=FAKE, o_out=FAKE, ws=FAKE)
+    p.update(ptrs)
+    L = ox.lib()
+    wsb = L.orthros_workspace_bytes(ctypes.byref(shape)) if ws_bytes is None else ws_bytes
+    return L.orthros_prefill(ctypes.byref(shape), P, p["q_base"], p["q_out"], p["k"], p["v"],
+                             ctypes.byref(aff or _aff()), p["cache_k"], p["cache_v"],
+                             p["cache_len"], p["o_base"], p["o_out"], p["ws"], wsb, None)
+
+
+def test_workspace_bytes():
+    L = ox.lib()
+    n = L.orthros_workspace_bytes(ctypes.byref(_shape()))
+    # status + (max, sum) + d partials for B * Hq * 2 rows * 64 splits
+    assert n >= 2 * 8 * 2 * 64 * (128 + 2) * 4
+    assert L.orthros_workspace_bytes(ctypes.byref(_shape(head_dim=96))) == 0
+    assert L.orthros_workspace_bytes(None) == 0
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("batch", 0, ox.E_INVALID), ("num_q_heads", 0, ox.E_INVALID),
+    ("num_kv_heads", 3, ox.E_INVALID), ("window", 0, ox.E_INVALID),
+    ("capacity", 0, ox.E_INVALID), ("reserved", 1, ox.E_INVALID),
+    ("head_dim", 96, ox.E_UNSUPPORTED), ("dtype", 7, ox.E_UNSUPPORTED),
+])
+def test_prefill_rejects_bad_shape(field, value, code):
+    assert _prefill(_shape(**{field: value}), ws_bytes=1 << 30) == code
+
+
+@pytest.mark.parametrize("name", ["q_base", "q_out", "k", "v", "cache_k", "cache_v",
+                                  "cache_len", "o_base", "o_out"])
+def test_prefill_rejects_null_and_misaligned(name):
+    assert _prefill(_shape(), **{name: None}) == ox.E_INVALID
+    assert _prefill(_shape(), **{name: FAKE + 8}) == ox.E_INVALID
+
+
+def test_prefill_rejects_bad_affine_workspace_capacity_and_length():
+    assert _prefill(_shape(), aff=_aff(beta_out=None)) == ox.E_INVALID
+    assert _prefill(_shape(), ws=None) == ox.E_WORKSPACE
+    assert _prefill(_shape(), ws_bytes=100) == ox.E_WORKSPACE
+    assert _prefill(_shape(capacity=63), P=64) == ox.E_CAPACITY
+    assert _prefill(_shape(), P=0) == ox.E_INVALID
+
+
+def test_decode_and_pt_reject_bad_arguments():
+    L = ox.lib()
+    s = _shape()
+    wsb = L.orthros_workspace_bytes(ctypes.byref(s))
+    F = FAKE
+    rc = L.orthros_decode_step(ctypes.byref(s), F, F, None, F, ctypes.byref(_aff()), F, F, F, 10,
+                               F, F, F, wsb, None)
+    assert rc == ox.E_INVALID
+    rc = L.orthros_decode_step(ctypes.byref(s), F, F, F, F, ctypes.byref(_aff()), F, F, F, -1,
+                               F, F, F, wsb, None)
+    assert rc == ox.E_INVALID
+    rc = L.orthros_decode_step(ctypes.byref(s), F, F, F, F, ctypes.byref(_aff()), F, F, F, 10,
+                               F, F, F, wsb - 1, None)
+    assert rc == ox.E_WORKSPACE
+    # pre-training: the cache is all-or-nothing
+    rc = L.orthros_forward_pt(ctypes.byref(s), 64, F, F, F, F, ctypes.byref(_aff()), F, None, None,
+                              F, F, F, wsb, None)
+    assert rc == ox.E_INVALID
+    rc = L.orthros_forward_pt(ctypes.byref(_shape(capacity=32)), 64, F, F, F, F,
+                              ctypes.byref(_aff()), F, F, F, F, F, F, wsb, None)
+    assert rc == ox.E_CAPACITY
+    rc = L.orthros_forward_pt(ctypes.byref(_shape(head_dim=32)), 64, F, F, F, F,
+                              ctypes.byref(_aff()), None, None, None, F, F, F, wsb, None)
+    assert rc == ox.E_UNSUPPORTED
+
+
+def test_status_strings():
+    for code in (ox.OK, ox.E_INVALID, ox.E_UNSUPPORTED, ox.E_WORKSPACE, ox.E_CAPACITY,
+                 ox.E_LAUNCH):
+        assert ox.status_string(code) not in ("", "unknown status")
+    assert ox.status_string(12345) == "unknown status"
+
+
+def test_read_status_rejects_null():
+    out = ctypes.c_int32(0)
+    assert ox.lib().orthros_read_device_status(None, 4096, ctypes.byref(out), 0, None) == ox.E_INVALID
