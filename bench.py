@@ -1,0 +1,257 @@
+"""Benchmark of the Orthros attention hot path on one MI355X.
+
+One step = one orthros_prefill call on the Llama3.1-8B-shaped 131072-token prompt (32 query /
+8 kv heads, d 128, window 4096, bf16, one planted key), i.e. the base stream's windowed rows,
+the cache write and the output row at the last token. `value` is prefill tokens/s over the
+timed steps, with all inputs already resident in HBM.
+
+The same JSON line carries:
+  * roofline: the banded flash kernel (the prefill's dominant kernel): algorithmic FLOPs per
+    launch (4 d per (query, key) pair inside the windows, summed over heads) over its mean
+    launch time, measured with HIP events the library records around each launch on the
+    call's stream during the timed steps; peak = dense bf16 MFMA 2.5 PFLOP/s;
+  * decode: the 16 x 131072-token decode workload, 128 consecutive decode steps, as
+    microseconds per step and the split-key kernel's algorithmic HBM bytes / launch time
+    against 8 TB/s;
+  * cpu_baseline: the float64 oracle (test infrastructure) timed on this host on a bounded
+    sample of the same prefill (base rows at seeded positions, all heads).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--skip-decode] [--skip-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from efficient_attention_amd import orthros as ox  # noqa: E402
+from efficient_attention_amd import synthetic as syn  # noqa: E402
+
+PEAK_BF16_FLOPS = 2.5e15     # MI355X dense bf16 MFMA
+PEAK_HBM_BYTES = 8.0e12      # MI355X HBM3E
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def swa_pairs(T: int, w: int) -> int:
+    """(query, key) pairs inside the windows of Eq. 4 over positions 0..T-1."""
+    w = min(w, T)
+    return w * (w + 1) // 2 + (T - w) * w
+
+
+def prefill_flops(wl) -> float:
+    d, Hq, B = wl.head_dim, wl.q_heads, wl.batch
+    base = 4.0 * d * Hq * B * swa_pairs(wl.length, wl.window)
+    out = 4.0 * d * Hq * B * wl.length  # one output row over P keys
+    return base, out
+
+
+def bench_prefill(wl, steps, warmup, dev):
+    log(f"prefill {wl.name}: generating inputs on {dev}")
+    inp = syn.make_prefill(wl, device=dev)
+    B, P, Hq, d = inp["q_base"].shape
+    Hkv = inp["k"].shape[2]
+    shape = ox.Shape(B, Hq, Hkv, d, wl.window, torch.bfloat16, P)
+    aff = ox.Affine(*inp["affine"])
+    ck = torch.empty(B, Hkv, P, d, dtype=torch.bfloat16, device=dev)
+    cv = torch.empty_like(ck)
+    cl = torch.zeros(B, dtype=torch.int32, device=dev)
+    ob = torch.empty(B, P, Hq, d, dtype=torch.bfloat16, device=dev)
+    oo = torch.empty(B, 1, Hq, d, dtype=torch.bfloat16, device=dev)
+    ws = ox.make_workspace(shape, dev)
+
+    def step():
+        ox.prefill(shape, inp["q_base"], inp["q_out"], inp["k"], inp["v"], aff, ck, cv, cl, ob, oo, ws)
+
+    for i in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"prefill warmup {warmup} done; timing {steps} steps")
+    ox.timing_begin()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    stages = ox.timing_end()
+    ms = (t1 - t0) * 1e3 / steps
+    log(f"prefill {ms:.3f} ms/step; stages {stages}")
+    return dict(ms=ms, stages=stages, inp=inp, planted=inp["planted_pos"])
+
+
+def bench_decode(wl, warmup, dev):
+    S = wl.steps
+    log(f"decode {wl.name}: filling {wl.batch} caches of {wl.length} tokens on {dev}")
+    B, L0, Hq, Hkv, d = wl.batch, wl.length, wl.q_heads, wl.kv_heads, wl.head_dim
+    cap = L0 + S + warmup
+    g = torch.Generator(device=dev)
+    g.manual_seed(wl.seed)
+    ck = torch.empty(B, Hkv, cap, d, dtype=torch.bfloat16, device=dev)
+    cv = torch.empty_like(ck)
+    for t in (ck, cv):  # history rows ~ N(0,1), bf16-rounded; filled per sequence
+        for b in range(B):
+            t[b, :, :L0].copy_(torch.randn(Hkv, L0, d, generator=g, device=dev))
+    mk = lambda *s: torch.randn(*s, generator=g, device=dev).to(torch.bfloat16)  # noqa: E731
+    qb, qo = mk(S, B, Hq, d), mk(S, B, Hq, d)
+    kn, vn = mk(S, B, Hkv, d), mk(S, B, Hkv, d)
+    aff = ox.Affine(*syn.make_affine(Hq, d, g, dev))
+    shape = ox.Shape(B, Hq, Hkv, d, wl.window, torch.bfloat16, cap)
+    cl = torch.full((B,), L0, dtype=torch.int32, device=dev)
+    ob = torch.empty(B, Hq, d, dtype=torch.bfloat16, device=dev)
+    oo = torch.empty_like(ob)
+    ws = ox.make_workspace(shape, dev)
+
+    for i in range(warmup):
+        ox.decode_step(shape, qb[i % S], qo[i % S], kn[i % S], vn[i % S], aff, ck, cv, cl,
+                       L0 + i, ob, oo, ws)
+    cl.fill_(L0)
+    torch.cuda.synchronize()
+    log(f"decode warmup {warmup} done; timing {S} steps")
+    ox.timing_begin()
+    t0 = time.perf_counter()
+    for s in range(S):
+        ox.decode_step(shape, qb[s], qo[s], kn[s], vn[s], aff, ck, cv, cl, L0 + s, ob, oo, ws)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    stages = ox.timing_end()
+    assert cl.cpu().tolist() == [L0 + S] * B
+    assert ox.read_device_status(ws) == 0
+    us = (t1 - t0) * 1e6 / S
+    # algorithmic bytes: every cached key/value row read once, new k/v read + appended,
+    # queries read, outputs written (both streams)
+    kv_row = Hkv * d * 2 * 2
+    cache_read = sum(B * (L0 + s) * kv_row for s in range(S)) / S
+    new_kv = B * kv_row * 2
+    qo_bytes = B * Hq * d * 2 * 2 * 2
+    step_bytes = cache_read + new_kv + qo_bytes
+    split_ms, split_n = stages["split_rows"]
+    split_bytes = cache_read + B * kv_row + B * Hq * d * 2 * 2
+    split_s = split_ms / 1e3 / max(split_n, 1)
+    log(f"decode {us:.1f} us/step; stages {stages}")
+    return dict(us=us, stages=stages, step_bytes=step_bytes, split_bytes=split_bytes,
+                split_s=split_s)
+
+
+def cpu_baseline(inp, wl, budget_s=12.0):
+    """The float64 oracle on host cores: base rows at seeded positions (all heads)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([x.get("num_threads", 1) for x in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    log("cpu baseline: copying inputs to host")
+    K = inp["k"][0].float().cpu().numpy()
+    V = inp["v"][0].float().cpu().numpy()
+    a = [x.cpu().numpy() for x in inp["affine"]]
+    rng = np.random.default_rng(wl.seed)
+    P, w = wl.length, wl.window
+    positions = rng.integers(min(w, P - 1), P, size=4000)
+    Q = inp["q_base"][0].index_select(0, torch.as_tensor(positions, device=inp["q_base"].device))
+    Q = Q.float().cpu().numpy()
+    s = oracle.default_scale(wl.head_dim)
+    n = 0
+    t0 = time.perf_counter()
+    while n < len(positions):
+        t = int(positions[n])
+        oracle.base_row(oracle.scale_offset(Q[n], a[0], a[1]), K, V, t, w, s)
+        n += 1
+        if time.perf_counter() - t0 > budget_s and n >= 8:
+            break
+    dt = time.perf_counter() - t0
+    log(f"cpu baseline: {n} positions in {dt:.1f} s")
+    return dict(value=n / dt, unit="tokens/s", cores=threads, kind="oracle",
+                sample=f"{n} base-stream positions (all {wl.q_heads} heads, window {w}) drawn "
+                       f"uniformly from [{min(w, P - 1)}, {P}) of the {P}-token prompt, "
+                       f"float64 numpy, {dt:.1f} s")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--skip-decode", action="store_true")
+    ap.add_argument("--skip-cpu", action="store_true")
+    ap.add_argument("--workload", default="prefill_8b_128k",
+                    choices=["prefill_8b_128k", "prefill_8b_32k"])
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    ox.lib()
+
+    wl = syn.WORKLOADS[args.workload]
+    pf = bench_prefill(wl, args.steps, args.warmup, dev)
+    base_flops, out_flops = prefill_flops(wl)
+    band_ms, band_n = pf["stages"]["band"]
+    band_s = band_ms / 1e3 / max(band_n, 1)
+    achieved = base_flops / band_s
+    tokens = wl.batch * wl.length
+    value = tokens / (pf["ms"] / 1e3)
+    rec = {
+        "metric": "prefill tokens/s @128K (Llama-8B shape)" if wl.length == 131072
+        else f"prefill tokens/s @{wl.length // 1024}K (Llama-8B shape)",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pf["ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.batch, "prompt_len": wl.length,
+                   "q_heads": wl.q_heads, "kv_heads": wl.kv_heads, "head_dim": wl.head_dim,
+                   "window": wl.window, "planted_key_pos": pf["planted"],
+                   "inputs": "N(0,1) bf16 drawn on cuda:0, seeded"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved / 1e12, 2),
+                     "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_FLOPS, 4), "traffic": None,
+                     "kernel": "band_kernel", "launch_ms": round(band_s * 1e3, 4),
+                     "flops_per_launch": base_flops},
+        "stage_ms_per_step": {k: round(v[0] / max(args.steps, 1), 4)
+                              for k, v in pf["stages"].items() if v[1]},
+    }
+    if not args.skip_decode:
+        dw = syn.WORKLOADS["decode_8b_128k"]
+        dc = bench_decode(dw, 4, dev)
+        ach = dc["split_bytes"] / dc["split_s"]
+        rec["decode"] = {
+            "metric": "decode-step us @128K", "workload": dw.name, "batch": dw.batch,
+            "cache_len": dw.length, "steps": dw.steps, "us_per_step": round(dc["us"], 2),
+            "step_GBps": round(dc["step_bytes"] / (dc["us"] / 1e6) / 1e9, 1),
+            "roofline": {"bound": "hbm", "achieved": round(ach / 1e9, 1),
+                         "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
+                         "frac": round(ach / PEAK_HBM_BYTES, 4), "traffic": None,
+                         "kernel": "split_rows_kernel", "launch_us": round(dc["split_s"] * 1e6, 2),
+                         "bytes_per_launch": dc["split_bytes"]},
+            "stage_us_per_step": {k: round(v[0] * 1e3 / dw.steps, 2)
+                                  for k, v in dc["stages"].items() if v[1]},
+        }
+    if not args.skip_cpu:
+        rec["cpu_baseline"] = cpu_baseline(pf["inp"], wl)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -16,7 +16,6 @@ namespace {
 
 constexpr int kMaxSplits = 64;     // split partials reserved per row in the workspace
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kSplitKeys = 4096;   // target keys per split for the few-row kernel
 constexpr size_t kStatusBytes = 256;
 
 struct WsLayout {
@@ -102,16 +101,24 @@ hipError_t run_stage(int stage, hipStream_t st, F&& f) {
 
 int launch_rc(hipError_t e) { return e == hipSuccess ? ORTHROS_OK : ORTHROS_E_LAUNCH; }
 
+// Split count for the few-row kernel. Two of its work-groups are resident per compute unit
+// (LDS-bound), so a launch runs in waves of kResident groups: pick the split count that
+// minimises (waves x keys per split), preferring splits of ~kSplitKeys keys on ties.
+constexpr int64_t kResident = 2 * 256;
 int nsplit_for(int64_t n, int64_t groups) {
-  // Enough splits for a few work-groups per CU, each covering at least one key tile.
-  int64_t s = (n + kSplitKeys - 1) / kSplitKeys;
-  const int64_t want = (4 * 256 + groups - 1) / groups;  // ~4 groups per compute unit
-  if (s < want) s = want;
   const int64_t tiles = (n + 63) / 64;
-  if (s > tiles) s = tiles;
-  if (s > kMaxSplits) s = kMaxSplits;
-  if (s < 1) s = 1;
-  return (int)s;
+  int best = 1;
+  double best_cost = 1e300;
+  for (int s = 1; s <= kMaxSplits && s <= tiles; ++s) {
+    const int64_t per = ((n + s - 1) / s + 63) / 64 * 64;
+    const int64_t waves = (groups * s + kResident - 1) / kResident;
+    const double cost = (double)waves * (double)per + 64.0 * s;  // + merge work per split
+    if (cost < best_cost * (1 - 1e-9)) {
+      best_cost = cost;
+      best = s;
+    }
+  }
+  return best;
 }
 
 int heads_per_chunk(int G, bool with_base) {

@@ -277,27 +277,44 @@ __global__ __launch_bounds__(256) void split_rows_kernel(SplitParams p) {
 }
 
 // Combine the split partials of one row: O = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
+// One wavefront per row: lane s holds split s's (max, sum); the weights go through LDS and each
+// lane then accumulates its channels over the splits in split order (deterministic).
 __global__ __launch_bounds__(64) void merge_kernel(MergeParams p) {
+  __shared__ float wgt[64];
   const idx_t row = blockIdx.x;
+  const int lane = threadIdx.x;
   const int st = (int)(row % p.nstreams);
   const idx_t bh = row / p.nstreams;
   const int h = (int)(bh % p.Hq);
   const idx_t b = bh / p.Hq;
   const float* pm = p.pm + row * p.nsplit;
   const float* pl = p.pl + row * p.nsplit;
-  float M = kNegInf;
-  for (int s = 0; s < p.nsplit; ++s) M = fmaxf(M, pm[s]);
-  float den = 0.f;
-  for (int s = 0; s < p.nsplit; ++s) den += pm[s] == kNegInf ? 0.f : fast_exp2(pm[s] - M) * pl[s];
+  const float ms = lane < p.nsplit ? pm[lane] : kNegInf;
+  const float ls = lane < p.nsplit ? pl[lane] : 0.f;
+  float M = ms;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+  const float f = (ms == kNegInf) ? 0.f : fast_exp2(ms - M);
+  float den = f * ls;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) den += __shfl_xor(den, off, 64);
+  wgt[lane] = f;
+  __syncthreads();
   const float inv = 1.f / den;
   void* out = st == 0 ? p.out0 : p.out1;
   const idx_t off = st == 0 ? b * p.o_sb0 + (idx_t)h * p.o_sh0 : b * p.o_sb1 + (idx_t)h * p.o_sh1;
-  for (int c = threadIdx.x; c < p.d; c += blockDim.x) {
-    float o = 0.f;
-    for (int s = 0; s < p.nsplit; ++s) {
-      if (pm[s] != kNegInf) o += fast_exp2(pm[s] - M) * p.po[(row * p.nsplit + s) * p.d + c];
+  const float* po = p.po + row * p.nsplit * p.d;
+  for (int c = lane; c < p.d; c += 64) {
+    float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+    int s = 0;
+    for (; s + 4 <= p.nsplit; s += 4) {
+      o0 += wgt[s] * po[(idx_t)s * p.d + c];
+      o1 += wgt[s + 1] * po[(idx_t)(s + 1) * p.d + c];
+      o2 += wgt[s + 2] * po[(idx_t)(s + 2) * p.d + c];
+      o3 += wgt[s + 3] * po[(idx_t)(s + 3) * p.d + c];
     }
-    o *= inv;
+    for (; s < p.nsplit; ++s) o0 += wgt[s] * po[(idx_t)s * p.d + c];
+    const float o = ((o0 + o1) + (o2 + o3)) * inv;
     if (p.bf16)
       reinterpret_cast<uint16_t*>(out)[off + c] = f32_to_bf16(o);
     else
