@@ -7,14 +7,15 @@
 // with the score scale and log2 e, and rounded once to bf16.
 //
 // Work-group: 8 wavefronts (2 per SIMD) = HPW query heads sharing one kv head x (8 / HPW)
-// position blocks of 32 rows; one kv head's 64-key K/V tiles are staged through LDS (double
-// buffered, K row-major, V transposed to key-contiguous) and read by all 8 wavefronts. Per
-// wavefront and tile, with the transposed score layout S^T (keys x queries) so each lane owns
-// one query and its softmax reductions stay in registers:
+// position blocks of 32 rows. One kv head's 64-key K and V tiles are staged through LDS
+// (double buffered, row-major, 16-byte slots XOR-swizzled per row so the reads below hit all
+// 64 banks) and read by all 8 wavefronts. Per wavefront and tile, with the transposed score
+// layout S^T (keys x queries) so each lane owns one query and its softmax stays in registers:
 //   S^T[64 x 32]  = K . Q^T        16 x mfma_f32_32x32x16_bf16 (d = 128)
-//   mask (edge tiles only), online softmax with a lazily rescaled running max
+//   mask (edge tiles only), online softmax in the exp2 domain with a lazily rescaled max
 //   O^T[d x 32]  += V^T . P^T      16 x mfma_f32_32x32x16_bf16; P^T comes straight from the
-//                                  S^T registers, V^T's keys permuted to match their order
+//                                  S^T registers; V^T is read with the LDS transpose read
+//                                  (ds_read_b64_tr_b16) in the key order of those registers
 // Tiles are visited from the diagonal downwards, so each row's first tile holds its own key.
 // Tiles outside a wavefront's band are skipped; tiles inside every row's band run unmasked.
 #include "common.h"
@@ -23,43 +24,31 @@
 namespace orthros {
 
 namespace {
-constexpr int kTK = 64;   // keys per tile
-constexpr int kQW = 32;   // query rows per wavefront
-constexpr int kNW = 8;    // wavefronts per work-group
+constexpr int kTK = 64;      // keys per tile
+constexpr int kQW = 32;      // query rows per wavefront
+constexpr int kNW = 8;       // wavefronts per work-group
 constexpr float kTau = 8.f;  // rescale only when the running max grows by more than 2^8
 
-template <int D>
-struct BandSmem {
-  static constexpr int KSTR = D + 8;
-  static constexpr int VSTR = kTK + 8;
-  static constexpr int KBUF = kTK * KSTR;
-  static constexpr int VBUF = D * VSTR;
-  static constexpr int BYTES = 2 * (KBUF + VBUF) * 2;
-};
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// Position of key k (0..63) inside a V^T row: within every 16 keys the groups of 4 are stored
-// in the order 0, 2, 1, 3, which is the key order a 32x32 score tile hands the PV product.
-__device__ __forceinline__ int vpos(int k) {
-  const int grp = (k >> 2) & 3;
-  const int pg = (grp == 1) ? 2 : (grp == 2 ? 1 : grp);
-  return (k & ~15) | (pg << 2) | (k & 3);
+__device__ __forceinline__ bf16x8 cat_tr(s16x4 lo, s16x4 hi) {
+  s16x4 v8[2] = {lo, hi};
+  return __builtin_bit_cast(bf16x8, v8);
 }
 }  // namespace
 
 template <int D, int HPW>
 __global__ __launch_bounds__(512) void band_kernel(BandParams p) {
-  using SM = BandSmem<D>;
-  constexpr int KSTR = SM::KSTR, VSTR = SM::VSTR;
+  constexpr int NCH = D / 8;             // 16-byte slots per row
+  constexpr int ROWB = D * 2;            // bytes per K/V row
+  constexpr int TILEB = kTK * ROWB;      // bytes per K (or V) tile
+  constexpr int STAGEB = 2 * TILEB;      // K + V
   constexpr int PB = kNW / HPW;          // position blocks per work-group
   constexpr int BMP = kQW * PB;          // positions per work-group
   constexpr int NKS = D / 16;            // QK k-steps
   constexpr int NDT = D / 32;            // O^T tiles
-  constexpr int CPR = D / 8;             // 16-byte chunks per row
-  constexpr int KCH = kTK * CPR / 512;   // K chunks per thread
-  constexpr int VITEMS = (kTK / 2) * CPR;  // (key pair, chunk) items per tile
-  __shared__ __attribute__((aligned(16))) unsigned char smem[SM::BYTES];
-  uint16_t* Ks = reinterpret_cast<uint16_t*>(smem);
-  uint16_t* Vt = Ks + 2 * SM::KBUF;
+  constexpr int SCH = kTK * NCH / 512;   // staged chunks per thread per tile (K and V each)
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGEB];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int nhc = p.G / HPW;
@@ -95,17 +84,23 @@ __global__ __launch_bounds__(512) void band_kernel(BandParams p) {
                          (idx_t)(ok ? tq : 0) * p.q_st + (idx_t)h * p.q_sh;
     const float* al = p.alpha + (idx_t)h * D;
     const float* be = p.beta + (idx_t)h * D;
+    const float sc = ok ? p.scale_log2 : 0.f;
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
       const int c0 = 16 * s + 8 * hh;
-      u32x4 raw = {0u, 0u, 0u, 0u};
-      if (ok) raw = *reinterpret_cast<const u32x4*>(qr + c0);
+      const u32x4 raw = *reinterpret_cast<const u32x4*>(qr + c0);
+      const f32x4 a0 = *reinterpret_cast<const f32x4*>(al + c0);
+      const f32x4 a1 = *reinterpret_cast<const f32x4*>(al + c0 + 4);
+      const f32x4 b0 = *reinterpret_cast<const f32x4*>(be + c0);
+      const f32x4 b1 = *reinterpret_cast<const f32x4*>(be + c0 + 4);
       bf16x8 f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const uint32_t w = raw[e >> 1];
         const float x = (e & 1) ? bf16_hi(w) : bf16_lo(w);
-        f[e] = (__bf16)(ok ? (al[c0 + e] * x + be[c0 + e]) * p.scale_log2 : 0.f);
+        const float a = e < 4 ? a0[e] : a1[e - 4];
+        const float bb = e < 4 ? b0[e] : b1[e - 4];
+        f[e] = (__bf16)((a * x + bb) * sc);
       }
       qf[s] = f;
     }
@@ -124,46 +119,55 @@ __global__ __launch_bounds__(512) void band_kernel(BandParams p) {
   const uint16_t* kbase = reinterpret_cast<const uint16_t*>(p.k) + (idx_t)b * p.k_sb + (idx_t)g * p.k_sh;
   const uint16_t* vbase = reinterpret_cast<const uint16_t*>(p.v) + (idx_t)b * p.k_sb + (idx_t)g * p.k_sh;
 
-  u32x4 kreg[KCH];
-  u32x4 vreg[2];
+  // Staging: thread tid moves chunks ci = tid + 512 i (row ci / NCH, slot ci % NCH) of the K
+  // and V tiles. K slot c of row r lives at c ^ (r % NCH); V slot c at c ^ 4((r >> 1) % (NCH/4)).
+  int srow[SCH], scol[SCH], skoff[SCH], svoff[SCH];
+#pragma unroll
+  for (int i = 0; i < SCH; ++i) {
+    const int ci = tid + 512 * i;
+    const int r = ci / NCH, c = ci % NCH;
+    srow[i] = r;
+    scol[i] = 8 * c;
+    skoff[i] = r * ROWB + 16 * (c ^ (r % NCH));
+    svoff[i] = TILEB + r * ROWB + 16 * (c ^ (4 * ((r >> 1) % (NCH / 4))));
+  }
+  u32x4 kreg[SCH], vreg[SCH];
   auto load_tile = [&](int tb) {
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int ci = tid + 512 * i;
-      const int r = ci / CPR, c = ci % CPR;
-      int key = tb + r;
+    for (int i = 0; i < SCH; ++i) {
+      int key = tb + srow[i];
       if (key > p.T - 1) key = p.T - 1;
-      kreg[i] = *reinterpret_cast<const u32x4*>(kbase + (idx_t)key * p.k_st + 8 * c);
-    }
-    if (tid < VITEMS) {
-      const int c = tid % CPR, kp = tid / CPR;
-      int k0 = tb + 2 * kp, k1 = k0 + 1;
-      if (k0 > p.T - 1) k0 = p.T - 1;
-      if (k1 > p.T - 1) k1 = p.T - 1;
-      vreg[0] = *reinterpret_cast<const u32x4*>(vbase + (idx_t)k0 * p.k_st + 8 * c);
-      vreg[1] = *reinterpret_cast<const u32x4*>(vbase + (idx_t)k1 * p.k_st + 8 * c);
+      kreg[i] = *reinterpret_cast<const u32x4*>(kbase + (idx_t)key * p.k_st + scol[i]);
+      vreg[i] = *reinterpret_cast<const u32x4*>(vbase + (idx_t)key * p.k_st + scol[i]);
     }
   };
-  auto store_tile = [&](int buf) {
-    uint16_t* ks = Ks + buf * SM::KBUF;
-    uint16_t* vt = Vt + buf * SM::VBUF;
+  auto store_tile = [&](int stage) {
+    unsigned char* st = smem + stage * STAGEB;
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int ci = tid + 512 * i;
-      const int r = ci / CPR, c = ci % CPR;
-      *reinterpret_cast<u32x4*>(ks + r * KSTR + 8 * c) = kreg[i];
-    }
-    if (tid < VITEMS) {
-      const int c = tid % CPR, kp = tid / CPR;
-      const int pos = vpos(2 * kp);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t a = vreg[0][e >> 1], bb = vreg[1][e >> 1];
-        const uint32_t wd = (e & 1) ? ((a >> 16) | (bb & 0xffff0000u)) : ((a & 0xffffu) | (bb << 16));
-        *reinterpret_cast<uint32_t*>(vt + (8 * c + e) * VSTR + pos) = wd;
-      }
+    for (int i = 0; i < SCH; ++i) {
+      *reinterpret_cast<u32x4*>(st + skoff[i]) = kreg[i];
+      *reinterpret_cast<u32x4*>(st + svoff[i]) = vreg[i];
     }
   };
+
+  // Per-lane LDS read offsets (bytes within a stage).
+  // QK A operand: key row 32 mt + j, channel slot 2 s + hh.
+  int qk_off[NKS];
+#pragma unroll
+  for (int s = 0; s < NKS; ++s) qk_off[s] = j * ROWB + 16 * ((2 * s + hh) ^ (j % NCH));
+  // PV A operand (transpose read): lane group G = lane / 16 supplies, from its lane L, key row
+  // 16 ks + 8 h2 + 4 (G / 2) + L / 4 at channels 32 dt + 16 (G % 2) + 4 (L % 4) .. + 3.
+  int pv_off[NDT];
+  {
+    const int G = lane >> 4, L = lane & 15;
+    const int row = 4 * (G >> 1) + (L >> 2);  // + 16 ks + 8 h2 (row-independent swizzle)
+    const int fv = 4 * ((row >> 1) % (NCH / 4));
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const int chunk = 4 * dt + 2 * (G & 1) + ((L & 3) >> 1);
+      pv_off[dt] = TILEB + row * ROWB + 16 * (chunk ^ fv) + 8 * (L & 1);
+    }
+  }
 
   f32x16 O[NDT];
 #pragma unroll
@@ -172,81 +176,93 @@ __global__ __launch_bounds__(512) void band_kernel(BandParams p) {
     for (int r = 0; r < 16; ++r) O[dt][r] = 0.f;
   float m = kNegInf, l = 0.f;
 
-  load_tile(tile_hi);
-  int buf = 0;
-  for (int tb = tile_hi; tb >= tile_lo; tb -= kTK) {
-    store_tile(buf);
-    __syncthreads();
-    if (tb - kTK >= tile_lo) load_tile(tb - kTK);
-
-    const bool skip = !wactive || tb > wmax || tb + kTK - 1 < wlo;
-    if (!skip) {
-      const uint16_t* ks = Ks + buf * SM::KBUF;
-      const uint16_t* vt = Vt + buf * SM::VBUF;
-      f32x16 S0, S1;
+  auto compute = [&](unsigned char* st, int tb) {
+    f32x16 S0, S1;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      S0[r] = 0.f;
+      S1[r] = 0.f;
+    }
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(st + qk_off[s]);
+      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(st + qk_off[s] + 32 * ROWB);
+      S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[s], S0, 0, 0, 0);
+      S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[s], S1, 0, 0, 0);
+    }
+    // Unmasked only if every key of the tile lies in every row's window.
+    const bool full = (tb + kTK - 1 <= t0w) && (tb >= wmax - w + 1) && (tb + kTK - 1 <= p.T - 1);
+    if (!full) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        S0[r] = 0.f;
-        S1[r] = 0.f;
-      }
-#pragma unroll
-      for (int s = 0; s < NKS; ++s) {
-        const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(ks + j * KSTR + 16 * s + 8 * hh);
-        const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(ks + (32 + j) * KSTR + 16 * s + 8 * hh);
-        S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[s], S0, 0, 0, 0);
-        S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[s], S1, 0, 0, 0);
-      }
-      // Unmasked only if every key of the tile lies in every row's window.
-      const bool full = (tb + kTK - 1 <= t0w) && (tb >= wmax - w + 1) && (tb + kTK - 1 <= p.T - 1);
-      if (!full) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int k0 = tb + 8 * (r >> 2) + 4 * hh + (r & 3);
-          const int k1 = k0 + 32;
-          const bool ok0 = k0 <= tq && k0 > tq - w && k0 < p.T;
-          const bool ok1 = k1 <= tq && k1 > tq - w && k1 < p.T;
-          S0[r] = ok0 ? S0[r] : kNegInf;
-          S1[r] = ok1 ? S1[r] : kNegInf;
-        }
-      }
-      float mx = kNegInf;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(S0[r], S1[r]));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mn = fmaxf(m, mx);
-      const bool need = mn > m + kTau;
-      if (__builtin_amdgcn_ballot_w64(need)) {
-        const float alpha = need ? fast_exp2(m - mn) : 1.f;
-        m = need ? mn : m;
-        l *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) O[dt] *= alpha;
-      }
-      const float ms = m == kNegInf ? 0.f : m;
-      float ps = 0.f;
-      bf16x8 P[4];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p0 = fast_exp2(S0[r] - ms);
-        const float p1 = fast_exp2(S1[r] - ms);
-        ps += p0 + p1;
-        P[r >> 3][r & 7] = (__bf16)p0;
-        P[2 + (r >> 3)][r & 7] = (__bf16)p1;
-      }
-      l += ps;
-#pragma unroll
-      for (int ks4 = 0; ks4 < 4; ++ks4) {
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(vt + (32 * dt + j) * VSTR + 16 * ks4 + 8 * hh);
-          O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, P[ks4], O[dt], 0, 0, 0);
-        }
+        const int k0 = tb + 8 * (r >> 2) + 4 * hh + (r & 3);
+        const int k1 = k0 + 32;
+        const bool ok0 = k0 <= tq && k0 > tq - w && k0 < p.T;
+        const bool ok1 = k1 <= tq && k1 > tq - w && k1 < p.T;
+        S0[r] = ok0 ? S0[r] : kNegInf;
+        S1[r] = ok1 ? S1[r] : kNegInf;
       }
     }
-    buf ^= 1;
+    float mx = fmaxf(S0[0], S1[0]);
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(S0[r], S1[r]));
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    const float mn = fmaxf(m, mx);
+    const bool need = mn > m + kTau;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float alpha = need ? fast_exp2(m - mn) : 1.f;
+      m = need ? mn : m;
+      l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) O[dt] *= alpha;
+    }
+    const float ms = m == kNegInf ? 0.f : m;
+    bf16x8 P[4];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      P[r >> 3][r & 7] = (__bf16)fast_exp2(S0[r] - ms);
+      P[2 + (r >> 3)][r & 7] = (__bf16)fast_exp2(S1[r] - ms);
+    }
+    // Row sum of the rounded probabilities (the same values the value product uses).
+    float ps = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ps += (float)P[q][e];
+    l += ps;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        unsigned char* base = st + pv_off[dt] + (16 * ks) * ROWB;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + 8 * ROWB));
+        O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cat_tr(lo, hi), P[ks], O[dt], 0, 0, 0);
+      }
+    }
+  };
+
+  load_tile(tile_hi);
+  store_tile(0);
+  __syncthreads();
+  if (tile_hi - kTK >= tile_lo) load_tile(tile_hi - kTK);
+  int stage = 0;
+  for (int tb = tile_hi; tb >= tile_lo; tb -= kTK) {
+    const bool skip = !wactive || tb > wmax || tb + kTK - 1 < wlo;
+    if (!skip) compute(smem + stage * STAGEB, tb);
+    if (tb - kTK >= tile_lo) {
+      store_tile(stage ^ 1);
+      if (tb - 2 * kTK >= tile_lo) load_tile(tb - 2 * kTK);
+    }
+    __syncthreads();
+    stage ^= 1;
   }
 
-  const float lt = l + __shfl_xor(l, 32, 64);  // both lane halves of each query column
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l), __float_as_uint(l), false, false);
+  const float lt = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);  // both lane halves
   if (wactive && tq < p.T) {
     const float inv = 1.f / lt;
     uint16_t* orow = reinterpret_cast<uint16_t*>(p.o) + (idx_t)b * p.o_sb + (idx_t)tq * p.o_st + (idx_t)h * p.o_sh;
