@@ -27,6 +27,9 @@ def hipcc() -> str:
 def _flags():
     return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # No NaN is ever produced on purpose, so max/min need no NaN quieting (IEEE mode
+            # off); infinities, used for masking, keep their meaning.
+            "-fno-honor-nans", "-mno-amdgpu-ieee",
             "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-Wall", "-Wno-unused-lambda-capture"]
 
 

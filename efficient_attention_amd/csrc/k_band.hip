@@ -6,18 +6,20 @@
 // (§3.1, q = alpha (.) q_raw + beta) is applied while the query fragment is loaded, together
 // with the score scale and log2 e, and rounded once to bf16.
 //
-// Work-group: 8 wavefronts (2 per SIMD) = HPW query heads sharing one kv head x (8 / HPW)
-// position blocks of 32 rows. One kv head's 64-key K and V tiles are staged through LDS
-// (double buffered, row-major, 16-byte slots XOR-swizzled per row so the reads below hit all
-// 64 banks) and read by all 8 wavefronts. Per wavefront and tile, with the transposed score
-// layout S^T (keys x queries) so each lane owns one query and its softmax stays in registers:
-//   S^T[64 x 32]  = K . Q^T        16 x mfma_f32_32x32x16_bf16 (d = 128)
-//   mask (edge tiles only), online softmax in the exp2 domain with a lazily rescaled max
-//   O^T[d x 32]  += V^T . P^T      16 x mfma_f32_32x32x16_bf16; P^T comes straight from the
-//                                  S^T registers; V^T is read with the LDS transpose read
-//                                  (ds_read_b64_tr_b16) in the key order of those registers
-// Tiles are visited from the diagonal downwards, so each row's first tile holds its own key.
-// Tiles outside a wavefront's band are skipped; tiles inside every row's band run unmasked.
+// Work-group: 8 wavefronts (two per SIMD), HPW query heads sharing one kv head x (8 / HPW)
+// position blocks of 32 rows. One kv head's 64-key K and V tiles are copied straight from
+// global memory into a 4-slot LDS ring (row-major, 16-byte slots XOR-swizzled per row so the
+// operand reads hit all 64 banks) and read by all eight wavefronts. With the transposed score
+// layout S^T (keys x queries) each lane owns one query and its softmax stays in registers:
+//   S^T[64 x 32]  = K . Q^T - m    16 x mfma_f32_32x32x16_bf16 (d = 128); the reference max m
+//                                  enters as the accumulator input (no per-score subtract)
+//   online softmax in the exp2 domain; the reference moves only when a half-tile's
+//   probabilities could exceed 2^8 (their sum does), so the common path computes no maximum
+//   O^T[d x 32]  += V^T . P^T      16 x mfma_f32_32x32x16_bf16; P^T straight from the S^T
+//                                  registers; V^T through the LDS transpose read
+// The tile loop is software-pipelined over key halves so the vector work issues in the shadow
+// of the matrix cores (see the pipeline comment below). Tiles are visited from the diagonal
+// downwards.
 #include "common.h"
 #include "launch.h"
 
@@ -26,19 +28,43 @@ namespace orthros {
 namespace {
 constexpr int kTK = 64;      // keys per tile
 constexpr int kQW = 32;      // query rows per wavefront
-constexpr int kNW = 8;       // wavefronts per work-group
-constexpr float kTau = 8.f;  // rescale only when the running max grows by more than 2^8
+constexpr int kNW = 8;       // wavefronts per work-group (two per SIMD)
+constexpr int kThreads = 64 * kNW;
+constexpr int kStages = 4;   // LDS ring depth
+constexpr float kLazyBound = 256.f;  // largest tolerated sum of a half's probabilities
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ bf16x8 cat_tr(s16x4 lo, s16x4 hi) {
   s16x4 v8[2] = {lo, hi};
   return __builtin_bit_cast(bf16x8, v8);
 }
+__device__ __forceinline__ float lane_pair_max(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+__device__ __forceinline__ float lane_pair_sum(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+
+// Scheduling hint for one region: NPRE LDS reads first, then NM times {1 MFMA, NDS LDS reads,
+// NV vector instructions}, so the vector work issues in the shadow of the matrix cores.
+template <int NM, int NPRE, int NDS, int NV>
+__device__ __forceinline__ void interleave() {
+  __builtin_amdgcn_sched_group_barrier(0x100, NPRE, 0);
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, NDS, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);
+  }
+}
 }  // namespace
 
 template <int D, int HPW>
-__global__ __launch_bounds__(512) void band_kernel(BandParams p) {
+__global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
   constexpr int NCH = D / 8;             // 16-byte slots per row
   constexpr int ROWB = D * 2;            // bytes per K/V row
   constexpr int TILEB = kTK * ROWB;      // bytes per K (or V) tile
@@ -47,8 +73,7 @@ __global__ __launch_bounds__(512) void band_kernel(BandParams p) {
   constexpr int BMP = kQW * PB;          // positions per work-group
   constexpr int NKS = D / 16;            // QK k-steps
   constexpr int NDT = D / 32;            // O^T tiles
-  constexpr int SCH = kTK * NCH / 512;   // staged chunks per thread per tile (K and V each)
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGEB];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kStages * STAGEB];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int nhc = p.G / HPW;
@@ -72,18 +97,19 @@ __global__ __launch_bounds__(512) void band_kernel(BandParams p) {
   const int t0 = pb * BMP;
   const int h = g * p.G + hc * HPW + (wv % HPW);
   const int t0w = t0 + kQW * (wv / HPW);
-  const int j = lane & 31;   // query column of this lane
+  const int j = lane & 31;   // query column of this lane within a column tile
   const int hh = lane >> 5;  // lane half
-  const int tq = t0w + j;    // this lane's query position
 
-  // Query fragment (B operand of 32x32x16): lane (j, hh) holds channels 16*s + 8*hh + e.
+  // Query fragments (B operand of 32x32x16): lane (j, hh) holds query t0w + j, channels
+  // 16 s + 8 hh + e.
   bf16x8 qf[NKS];
   {
+    const float* al = p.alpha + (idx_t)h * D;
+    const float* be = p.beta + (idx_t)h * D;
+    const int tq = t0w + j;
     const bool ok = tq < p.T;
     const uint16_t* qr = reinterpret_cast<const uint16_t*>(p.q) + (idx_t)b * p.q_sb +
                          (idx_t)(ok ? tq : 0) * p.q_st + (idx_t)h * p.q_sh;
-    const float* al = p.alpha + (idx_t)h * D;
-    const float* be = p.beta + (idx_t)h * D;
     const float sc = ok ? p.scale_log2 : 0.f;
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
@@ -104,54 +130,69 @@ __global__ __launch_bounds__(512) void band_kernel(BandParams p) {
       }
       qf[s] = f;
     }
+    // Keep the fragments materialised here, outside the tile loop.
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) asm volatile("" : "+v"(qf[s]));
   }
 
-  // Key range of the work-group and of this wavefront.
+  // Key range of the work-group (tiles tile_hi, tile_hi - 64, ..., tile_lo) and of this wave.
   const int w = p.window;
   const int glo = t0 - w + 1 > 0 ? t0 - w + 1 : 0;
   const int ghi = (t0 + BMP - 1 < p.T - 1) ? t0 + BMP - 1 : p.T - 1;
   const int tile_lo = glo / kTK * kTK;
   const int tile_hi = ghi / kTK * kTK;
+  const int ntiles = (tile_hi - tile_lo) / kTK + 1;
   const bool wactive = t0w < p.T;
   const int wmax = (t0w + kQW - 1 < p.T - 1) ? t0w + kQW - 1 : p.T - 1;  // last valid row
   const int wlo = t0w - w + 1;  // lowest key any row of this wavefront needs (may be < 0)
+  auto tile_key = [&](int e) { return tile_hi - kTK * e; };
+  // This wavefront's tiles: ea (holds its last row) .. eb (holds its lowest key), contiguous.
+  const int ea = tile_hi > wmax ? (tile_hi - wmax + kTK - 1) / kTK : 0;
+  const int eb_w = (tile_hi + kTK - 1 - wlo) / kTK;
+  const int eb = eb_w < ntiles - 1 ? eb_w : ntiles - 1;
+  // Unmasked only if every key of the tile lies in every row's window.
+  auto full = [&](int e) {
+    const int tb = tile_key(e);
+    return (tb + kTK - 1 <= t0w) && (tb >= wmax - w + 1) && (tb + kTK - 1 <= p.T - 1);
+  };
 
   const uint16_t* kbase = reinterpret_cast<const uint16_t*>(p.k) + (idx_t)b * p.k_sb + (idx_t)g * p.k_sh;
   const uint16_t* vbase = reinterpret_cast<const uint16_t*>(p.v) + (idx_t)b * p.k_sb + (idx_t)g * p.k_sh;
 
-  // Staging: thread tid moves chunks ci = tid + 512 i (row ci / NCH, slot ci % NCH) of the K
-  // and V tiles. K slot c of row r lives at c ^ (r % NCH); V slot c at c ^ 4((r >> 1) % (NCH/4)).
-  int srow[SCH], scol[SCH], skoff[SCH], svoff[SCH];
+  // Staging straight from global memory into LDS: one wave instruction fills 64 x 16 B, i.e.
+  // LROWS consecutive rows, lane i writing slot i % NCH of row i / NCH (the LDS address of a
+  // lane is fixed by its index). The swizzle is therefore applied on the global side: the lane
+  // that fills K slot c of row r fetches channel chunk c ^ (r % NCH), and for V chunk
+  // c ^ 4((r >> 1) % (NCH/4)). Wave wv fills rows (wv NINST + i) LROWS .. of every tile.
+  constexpr int LROWS = 1024 / ROWB;
+  constexpr int NINST = kTK / LROWS / kNW;
+  static_assert(NINST >= 1 && NINST * LROWS * kNW == kTK, "staging covers a tile exactly");
+  int srow[NINST], skcol[NINST], svcol[NINST];
 #pragma unroll
-  for (int i = 0; i < SCH; ++i) {
-    const int ci = tid + 512 * i;
-    const int r = ci / NCH, c = ci % NCH;
+  for (int i = 0; i < NINST; ++i) {
+    const int r = (wv * NINST + i) * LROWS + lane / NCH;
+    const int c = lane % NCH;
     srow[i] = r;
-    scol[i] = 8 * c;
-    skoff[i] = r * ROWB + 16 * (c ^ (r % NCH));
-    svoff[i] = TILEB + r * ROWB + 16 * (c ^ (4 * ((r >> 1) % (NCH / 4))));
+    skcol[i] = 8 * (c ^ (r % NCH));
+    svcol[i] = 8 * (c ^ (4 * ((r >> 1) % (NCH / 4))));
   }
-  u32x4 kreg[SCH], vreg[SCH];
-  auto load_tile = [&](int tb) {
+  auto load_tile = [&](int e) {
+    const int tb = tile_key(e);
+    unsigned char* st = smem + (e % kStages) * STAGEB;
 #pragma unroll
-    for (int i = 0; i < SCH; ++i) {
+    for (int i = 0; i < NINST; ++i) {
       int key = tb + srow[i];
       if (key > p.T - 1) key = p.T - 1;
-      kreg[i] = *reinterpret_cast<const u32x4*>(kbase + (idx_t)key * p.k_st + scol[i]);
-      vreg[i] = *reinterpret_cast<const u32x4*>(vbase + (idx_t)key * p.k_st + scol[i]);
-    }
-  };
-  auto store_tile = [&](int stage) {
-    unsigned char* st = smem + stage * STAGEB;
-#pragma unroll
-    for (int i = 0; i < SCH; ++i) {
-      *reinterpret_cast<u32x4*>(st + skoff[i]) = kreg[i];
-      *reinterpret_cast<u32x4*>(st + svoff[i]) = vreg[i];
+      const idx_t ro = (idx_t)key * p.k_st;
+      lds_void* kd = (lds_void*)(st + (wv * NINST + i) * 1024);
+      lds_void* vd = (lds_void*)(st + TILEB + (wv * NINST + i) * 1024);
+      __builtin_amdgcn_global_load_lds((const void*)(kbase + ro + skcol[i]), kd, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(vbase + ro + svcol[i]), vd, 16, 0, 0);
     }
   };
 
   // Per-lane LDS read offsets (bytes within a stage).
-  // QK A operand: key row 32 mt + j, channel slot 2 s + hh.
+  // QK A operand: key row 32 m + j, channel slot 2 s + hh.
   int qk_off[NKS];
 #pragma unroll
   for (int s = 0; s < NKS; ++s) qk_off[s] = j * ROWB + 16 * ((2 * s + hh) ^ (j % NCH));
@@ -174,95 +215,160 @@ __global__ __launch_bounds__(512) void band_kernel(BandParams p) {
   for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) O[dt][r] = 0.f;
-  float m = kNegInf, l = 0.f;
-
-  auto compute = [&](unsigned char* st, int tb) {
-    f32x16 S0, S1;
+  // This lane's query t0w + j: reference max (scores are kept relative to it, exp2 domain),
+  // this lane's part of the row sum (its half of the keys), whether the query has met a key of
+  // its window, and -mref in every slot (the QK accumulator's initial value).
+  float mref = 0.f, l = 0.f;
+  bool started = false;
+  f32x16 negm;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      S0[r] = 0.f;
-      S1[r] = 0.f;
-    }
+  for (int r = 0; r < 16; ++r) negm[r] = 0.f;
+
+  // ---- building blocks ----------------------------------------------------------------------
+  // Scores of key half m of tile e (8 MFMAs): S = K rows 32 m .. 32 m + 31 . Q^T - mref.
+  auto qk = [&](f32x16& S, int e, int m) {
+    const unsigned char* st = smem + (e % kStages) * STAGEB + 32 * m * ROWB;
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
-      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(st + qk_off[s]);
-      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(st + qk_off[s] + 32 * ROWB);
-      S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[s], S0, 0, 0, 0);
-      S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[s], S1, 0, 0, 0);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(st + qk_off[s]);
+      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], s == 0 ? negm : S, 0, 0, 0);
     }
-    // Unmasked only if every key of the tile lies in every row's window.
-    const bool full = (tb + kTK - 1 <= t0w) && (tb >= wmax - w + 1) && (tb + kTK - 1 <= p.T - 1);
-    if (!full) {
+  };
+  // O^T += V^T . P^T over key half m of tile e (2 16-key steps x NDT MFMAs).
+  auto pv = [&](const bf16x8* Ph, int e, int m) {
+    unsigned char* st = smem + (e % kStages) * STAGEB;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int k0 = tb + 8 * (r >> 2) + 4 * hh + (r & 3);
-        const int k1 = k0 + 32;
-        const bool ok0 = k0 <= tq && k0 > tq - w && k0 < p.T;
-        const bool ok1 = k1 <= tq && k1 > tq - w && k1 < p.T;
-        S0[r] = ok0 ? S0[r] : kNegInf;
-        S1[r] = ok1 ? S1[r] : kNegInf;
-      }
-    }
-    float mx = fmaxf(S0[0], S1[0]);
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(S0[r], S1[r]));
-    {
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-    }
-    const float mn = fmaxf(m, mx);
-    const bool need = mn > m + kTau;
-    if (__builtin_amdgcn_ballot_w64(need)) {
-      const float alpha = need ? fast_exp2(m - mn) : 1.f;
-      m = need ? mn : m;
-      l *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) O[dt] *= alpha;
-    }
-    const float ms = m == kNegInf ? 0.f : m;
-    bf16x8 P[4];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      P[r >> 3][r & 7] = (__bf16)fast_exp2(S0[r] - ms);
-      P[2 + (r >> 3)][r & 7] = (__bf16)fast_exp2(S1[r] - ms);
-    }
-    // Row sum of the rounded probabilities (the same values the value product uses).
-    float ps = 0.f;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ps += (float)P[q][e];
-    l += ps;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int k2 = 0; k2 < 2; ++k2) {
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        unsigned char* base = st + pv_off[dt] + (16 * ks) * ROWB;
+        unsigned char* base = st + pv_off[dt] + (16 * (2 * m + k2)) * ROWB;
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base));
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + 8 * ROWB));
-        O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cat_tr(lo, hi), P[ks], O[dt], 0, 0, 0);
+        O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cat_tr(lo, hi), Ph[k2], O[dt], 0, 0, 0);
       }
     }
   };
+  // Keys outside the query's window (or past the sequence) of half m of tile e -> -inf.
+  auto mask = [&](f32x16& S, int e, int m) {
+    const int kb = tile_key(e) + 32 * m + 4 * hh;
+    const int tq = t0w + j;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int k = kb + 8 * (r >> 2) + (r & 3);
+      const bool ok = k <= tq && k > tq - w && k < p.T;
+      S[r] = ok ? S[r] : kNegInf;
+    }
+  };
+  // Probabilities of one half against the current reference (bf16, as the PV operand) and
+  // this lane's sum of them.
+  auto expo = [&](const f32x16& S, bf16x8* Ph) {
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      const float p0 = fast_exp2(S[r]);
+      const float p1 = fast_exp2(S[r + 1]);
+      s0 += p0;
+      s1 += p1;
+      Ph[r >> 3][r & 7] = (__bf16)p0;
+      Ph[r >> 3][(r & 7) + 1] = (__bf16)p1;
+    }
+    return s0 + s1;
+  };
+  // After the tentative probabilities of a half: the reference moves only if a probability of
+  // the query could exceed 2^8 (their sum over both lane halves does) or the query meets its
+  // first key. Then O and l are rescaled, this half's scores and the next half's (already
+  // accumulating against the old reference) shifted, and this half's probabilities redone;
+  // the new reference is the exact maximum, so they end up <= 1.
+  auto settle = [&](f32x16& S, f32x16& Snext, bf16x8* Ph, float ps) {
+    const float tot = lane_pair_sum(ps);
+    const bool need = !(tot <= kLazyBound) || !started;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      float a0 = fmaxf(S[0], S[1]), a1 = fmaxf(S[2], S[3]);
+#pragma unroll
+      for (int r = 4; r < 16; r += 4) {
+        a0 = fmaxf(a0, fmaxf(S[r], S[r + 1]));
+        a1 = fmaxf(a1, fmaxf(S[r + 2], S[r + 3]));
+      }
+      const float mx = lane_pair_max(fmaxf(a0, a1));
+      const bool move = need && mx != kNegInf;
+      const float dlt = move ? mx : 0.f;
+      const float alpha = started ? fast_exp2(-dlt) : 0.f;  // nothing accumulated yet: O, l = 0
+      started = started || move;
+      mref += dlt;
+      l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) O[dt] *= alpha;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        negm[r] = -mref;
+        S[r] -= dlt;
+        Snext[r] -= dlt;
+      }
+      ps = expo(S, Ph);
+    }
+    l += ps;
+  };
 
-  load_tile(tile_hi);
-  store_tile(0);
+  // ---- pipeline -----------------------------------------------------------------------------
+  // Per tile e, in two regions that are each one basic block, so the matrix cores and the
+  // vector ALUs work side by side:
+  //   A: MFMA scores of keys 32..63 of e and PV of keys 32..63 of e-1 | softmax of keys 0..31 of e
+  //   B: MFMA scores of keys 0..31 of e+1 and PV of keys 0..31 of e  | softmax of keys 32..63 of e
+  // PV of tile e-1 in A is why the LDS ring holds four tiles.
+  // Tiles 0 and 1 before the loop; tile e + 2 is requested at the top of iteration e into the
+  // slot tile e - 2 left (free since the previous barrier) and has landed by the barrier that
+  // ends iteration e (the barrier waits for outstanding loads).
+  load_tile(0);
+  if (ntiles > 1) load_tile(1);
   __syncthreads();
-  if (tile_hi - kTK >= tile_lo) load_tile(tile_hi - kTK);
-  int stage = 0;
-  for (int tb = tile_hi; tb >= tile_lo; tb -= kTK) {
-    const bool skip = !wactive || tb > wmax || tb + kTK - 1 < wlo;
-    if (!skip) compute(smem + stage * STAGEB, tb);
-    if (tb - kTK >= tile_lo) {
-      store_tile(stage ^ 1);
-      if (tb - 2 * kTK >= tile_lo) load_tile(tb - 2 * kTK);
+
+  f32x16 S0 = negm, S1 = negm;
+  bf16x8 P0[2], P1[2];
+  for (int e = 0; e < ntiles; ++e) {
+    if (e + 2 < ntiles) load_tile(e + 2);
+    if (wactive && e >= ea && e <= eb) {
+      const bool prev = e > ea, next = e < eb, fl = full(e);
+      if (!prev) qk(S0, e, 0);
+      float ps;
+      if (prev && fl) {
+        qk(S1, e, 1);
+        pv(P1, e - 1, 1);
+        ps = expo(S0, P0);
+        interleave<16, 4, 2, 3>();
+      } else if (prev) {
+        qk(S1, e, 1);
+        pv(P1, e - 1, 1);
+        mask(S0, e, 0);
+        ps = expo(S0, P0);
+      } else {
+        qk(S1, e, 1);
+        mask(S0, e, 0);
+        ps = expo(S0, P0);
+      }
+      settle(S0, S1, P0, ps);
+      if (next && fl) {
+        qk(S0, e + 1, 0);
+        pv(P0, e, 0);
+        ps = expo(S1, P1);
+        interleave<16, 4, 2, 3>();
+      } else if (next) {
+        qk(S0, e + 1, 0);
+        pv(P0, e, 0);
+        mask(S1, e, 1);
+        ps = expo(S1, P1);
+      } else {
+        pv(P0, e, 0);
+        mask(S1, e, 1);
+        ps = expo(S1, P1);
+      }
+      settle(S1, S0, P1, ps);
+      if (!next) pv(P1, e, 1);
     }
     __syncthreads();
-    stage ^= 1;
   }
 
-  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l), __float_as_uint(l), false, false);
-  const float lt = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);  // both lane halves
+  const int tq = t0w + j;
+  const float lt = lane_pair_sum(l);  // both lane halves of the query column
   if (wactive && tq < p.T) {
     const float inv = 1.f / lt;
     uint16_t* orow = reinterpret_cast<uint16_t*>(p.o) + (idx_t)b * p.o_sb + (idx_t)tq * p.o_st + (idx_t)h * p.o_sh;
@@ -287,7 +393,7 @@ hipError_t launch_band(const BandParams& p, int d, hipStream_t s) {
   const int bmp = kQW * (kNW / hpw);
   const int npb = (p.T + bmp - 1) / bmp;
   const uint32_t total = (uint32_t)p.B * p.Hkv * (p.G / hpw) * npb;
-  dim3 grid(total), block(512);
+  dim3 grid(total), block(kThreads);
 #define ORTHROS_BAND(DD, HH) hipLaunchKernelGGL((band_kernel<DD, HH>), grid, block, 0, s, p)
   if (d == 128) {
     if (hpw == 8) ORTHROS_BAND(128, 8);
