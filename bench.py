@@ -17,6 +17,7 @@ The same JSON line carries:
     sample of the same prefill (base rows at seeded positions, all heads).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--skip-decode] [--skip-cpu]
+       [--copy-calibration]
 """
 from __future__ import annotations
 
@@ -38,6 +39,46 @@ from efficient_attention_amd import synthetic as syn  # noqa: E402
 
 PEAK_BF16_FLOPS = 2.5e15     # MI355X dense bf16 MFMA
 PEAK_HBM_BYTES = 8.0e12      # MI355X HBM3E
+CSRC = os.path.join(ROOT, "efficient_attention_amd", "csrc")
+
+# HBM bytes per launch from two rocprofv3 counter runs (FETCH_SIZE, then WRITE_SIZE) of
+# `bench.py --copy-calibration`, each scaled by what the counter reads for the 1 GiB device copy
+# in the same run. Recorded with the sha256 of the kernel's sources: when they change, the
+# figure no longer describes the kernel and `traffic` is reported as null.
+TRAFFIC = {
+    "band_kernel": {"sha": "9f75e101f64ef74e", "bytes_per_launch": 2.7152e9},
+    "split_rows_kernel": {"sha": "a6d36c46cb0cdbb4", "bytes_per_launch": 8.5975e9},
+}
+
+
+def kernel_sources_sha(kernel: str) -> str:
+    import hashlib
+    files = {"band_kernel": ["k_band.hip"], "split_rows_kernel": ["k_split.hip"]}[kernel]
+    h = hashlib.sha256()
+    for f in files + ["common.h", "launch.h"]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel: str):
+    rec = TRAFFIC.get(kernel)
+    if rec is None or rec["sha"] != kernel_sources_sha(kernel):
+        return None
+    return rec["bytes_per_launch"]
+
+
+def copy_calibration(dev, gib=1, reps=3):
+    """A plain device copy of known size, for scaling the HBM byte counters."""
+    n = gib << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copy calibration: {reps} copies of {n} bytes (read {n}, write {n} each)")
+    del src, dst
 
 
 def log(*a):
@@ -185,6 +226,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--skip-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a 1 GiB device copy (reference for HBM byte counters)")
     ap.add_argument("--workload", default="prefill_8b_128k",
                     choices=["prefill_8b_128k", "prefill_8b_32k"])
     args = ap.parse_args()
@@ -198,6 +241,8 @@ def main():
     dev = torch.device("cuda:0")
     ox.lib()
 
+    if args.copy_calibration:
+        copy_calibration(dev)
     wl = syn.WORKLOADS[args.workload]
     pf = bench_prefill(wl, args.steps, args.warmup, dev)
     base_flops, out_flops = prefill_flops(wl)
@@ -226,7 +271,8 @@ def main():
                    "inputs": "N(0,1) bf16 drawn on cuda:0, seeded"},
         "roofline": {"bound": "mfma", "achieved": round(achieved / 1e12, 2),
                      "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_FLOPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_BF16_FLOPS, 4),
+                     "traffic": traffic_for("band_kernel"),
                      "kernel": "band_kernel", "launch_ms": round(band_s * 1e3, 4),
                      "flops_per_launch": base_flops},
         "stage_ms_per_step": {k: round(v[0] / max(args.steps, 1), 4)
@@ -242,7 +288,8 @@ def main():
             "step_GBps": round(dc["step_bytes"] / (dc["us"] / 1e6) / 1e9, 1),
             "roofline": {"bound": "hbm", "achieved": round(ach / 1e9, 1),
                          "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
-                         "frac": round(ach / PEAK_HBM_BYTES, 4), "traffic": None,
+                         "frac": round(ach / PEAK_HBM_BYTES, 4),
+                         "traffic": traffic_for("split_rows_kernel"),
                          "kernel": "split_rows_kernel", "launch_us": round(dc["split_s"] * 1e6, 2),
                          "bytes_per_launch": dc["split_bytes"]},
             "stage_us_per_step": {k: round(v[0] * 1e3 / dw.steps, 2)
