@@ -137,17 +137,10 @@ def bench_decode(wl, warmup, dev):
     log(f"decode {wl.name}: filling {wl.batch} caches of {wl.length} tokens on {dev}")
     B, L0, Hq, Hkv, d = wl.batch, wl.length, wl.q_heads, wl.kv_heads, wl.head_dim
     cap = L0 + S + warmup
-    g = torch.Generator(device=dev)
-    g.manual_seed(wl.seed)
-    ck = torch.empty(B, Hkv, cap, d, dtype=torch.bfloat16, device=dev)
-    cv = torch.empty_like(ck)
-    for t in (ck, cv):  # history rows ~ N(0,1), bf16-rounded; filled per sequence
-        for b in range(B):
-            t[b, :, :L0].copy_(torch.randn(Hkv, L0, d, generator=g, device=dev))
-    mk = lambda *s: torch.randn(*s, generator=g, device=dev).to(torch.bfloat16)  # noqa: E731
-    qb, qo = mk(S, B, Hq, d), mk(S, B, Hq, d)
-    kn, vn = mk(S, B, Hkv, d), mk(S, B, Hkv, d)
-    aff = ox.Affine(*syn.make_affine(Hq, d, g, dev))
+    inp = syn.make_decode_resident(wl, dev, cap)
+    ck, cv = inp["cache_k"], inp["cache_v"]
+    qb, qo, kn, vn = inp["q_base"], inp["q_out"], inp["k_new"], inp["v_new"]
+    aff = ox.Affine(*inp["affine"])
     shape = ox.Shape(B, Hq, Hkv, d, wl.window, torch.bfloat16, cap)
     cl = torch.full((B,), L0, dtype=torch.int32, device=dev)
     ob = torch.empty(B, Hq, d, dtype=torch.bfloat16, device=dev)

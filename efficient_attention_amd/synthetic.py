@@ -30,7 +30,7 @@ from dataclasses import dataclass, field, replace
 import torch
 
 __all__ = ["Workload", "WORKLOADS", "make_affine", "make_prefill", "make_pt", "make_decode",
-           "make_sft", "bf16_round"]
+           "make_decode_resident", "make_sft", "bf16_round"]
 
 
 @dataclass(frozen=True)
@@ -170,3 +170,29 @@ def make_decode(w: Workload, device="cpu", lengths=None):
     lens = [L0] * B if lengths is None else list(lengths)
     return dict(k=k, v=v, q_base=q_base, q_out=q_out, k_new=k_new, v_new=v_new, affine=aff,
                 lengths=lens)
+
+
+def make_decode_resident(w: Workload, device, capacity: int):
+    """Decode inputs drawn straight into a device-resident head-major cache.
+
+    For the full-size decode workload (16 x 131072 tokens) a token-major prefix plus a copy
+    would double the 8.6 GB footprint, so the history is drawn per sequence into
+    cache_k, cache_v [B, H_kv, capacity, d] (rows 0..L0-1; the rest left unset), in the order
+    k then v for each sequence, each ~ N(0, 1) rounded once to the storage dtype. Then the
+    per-step q_base, q_out [S, B, H_q, d], k_new, v_new [S, B, H_kv, d] and the affine vectors.
+    """
+    g = _gen(w.seed, device)
+    B, L0, S, Hq, Hkv, d = w.batch, w.length, w.steps, w.q_heads, w.kv_heads, w.head_dim
+    dt = _dtype(w.dtype)
+    ck = torch.empty(B, Hkv, capacity, d, dtype=dt, device=device)
+    cv = torch.empty_like(ck)
+    for t in (ck, cv):
+        for b in range(B):
+            t[b, :, :L0].copy_(torch.randn(Hkv, L0, d, generator=g, device=device))
+    q_base = _normal((S, B, Hq, d), g, device).to(dt)
+    q_out = _normal((S, B, Hq, d), g, device).to(dt)
+    k_new = _normal((S, B, Hkv, d), g, device).to(dt)
+    v_new = _normal((S, B, Hkv, d), g, device).to(dt)
+    aff = make_affine(Hq, d, g, device)
+    return dict(cache_k=ck, cache_v=cv, q_base=q_base, q_out=q_out, k_new=k_new, v_new=v_new,
+                affine=aff, lengths=[L0] * B)

@@ -1,0 +1,175 @@
+"""GPU parity at the full benchmark sizes, in the launch configuration bench.py times.
+
+The four bf16 workloads run whole on the GPU exactly as the benchmark runs them (same shapes,
+capacity, workspace and inputs drawn on the device from the same seeds). The float64 oracle
+then evaluates a seeded sample of rows, one at a time, on host copies of the same bf16 values:
+edge positions (first keys, the window boundary, the last rows) plus random ones, every query
+head. Cache contents are compared bit for bit in full.
+
+Tolerances: max-abs 1.5e-2 and mean relative error 3e-3 over the sampled outputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from efficient_attention_amd import orthros as ox
+from efficient_attention_amd import synthetic as syn
+from tests import helpers as H
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _say(*a):
+    print("[gpu case]", *a, flush=True)
+
+
+def _positions(T, w, n_random, seed):
+    """Edge rows (start, window boundary, tile boundaries, end) plus seeded random rows."""
+    edges = {0, 1, 2, 63, 64, 65, w - 2, w - 1, w, w + 1, T - 65, T - 64, T - 2, T - 1}
+    rng = np.random.default_rng(seed)
+    pos = edges | set(rng.integers(0, T, size=n_random).tolist())
+    return sorted(p for p in pos if 0 <= p < T)
+
+
+def _base_rows_ok(q_rows, K, V, positions, alpha, beta, w, gpu_rows, what):
+    """Oracle base rows (Eq. 4) at `positions` against the GPU's rows (all heads)."""
+    s = oracle.default_scale(K.shape[-1])
+    ref = np.stack([oracle.base_row(oracle.scale_offset(q_rows[i], alpha, beta), K, V, t, w, s)
+                    for i, t in enumerate(positions)])
+    return H.assert_close(gpu_rows, ref, torch.bfloat16, what)
+
+
+def _run_prefill_fullsize(name, n_random):
+    wl = syn.WORKLOADS[name]
+    _say("full-size prefill", wl)
+    inp = syn.make_prefill(wl, device=DEV)
+    B, P, Hq, d = inp["q_base"].shape
+    Hkv = inp["k"].shape[2]
+    shape = ox.Shape(B, Hq, Hkv, d, wl.window, torch.bfloat16, P)
+    ck = H.nan_like((B, Hkv, P, d), torch.bfloat16, DEV)
+    cv = H.nan_like((B, Hkv, P, d), torch.bfloat16, DEV)
+    cl = torch.full((B,), -7, dtype=torch.int32, device=DEV)
+    ob = H.nan_like((B, P, Hq, d), torch.bfloat16, DEV)
+    oo = H.nan_like((B, 1, Hq, d), torch.bfloat16, DEV)
+    ws = ox.make_workspace(shape, DEV)
+    ox.prefill(shape, inp["q_base"], inp["q_out"], inp["k"], inp["v"], ox.Affine(*inp["affine"]),
+               ck, cv, cl, ob, oo, ws)
+    torch.cuda.synchronize()
+    assert cl.cpu().tolist() == [P] * B
+    assert torch.equal(ck.permute(0, 2, 1, 3), inp["k"]), "cache_k differs from k"
+    assert torch.equal(cv.permute(0, 2, 1, 3), inp["v"]), "cache_v differs from v"
+    assert not torch.isnan(ob).any().item(), "unwritten base row"
+
+    a_b, b_b, a_o, b_o = H.affine64(inp["affine"])
+    pos = _positions(P, wl.window, n_random, wl.seed)
+    idx = torch.as_tensor(pos, device=DEV)
+    K = H.to64(inp["k"][0])
+    V = H.to64(inp["v"][0])
+    q_rows = H.to64(inp["q_base"][0].index_select(0, idx))
+    gpu_rows = H.to64(ob[0].index_select(0, idx))
+    mb = _base_rows_ok(q_rows, K, V, pos, a_b, b_b, wl.window, gpu_rows, f"{name} o_base")
+    s = oracle.default_scale(d)
+    ref_out = oracle.output_row(oracle.scale_offset(H.to64(inp["q_out"][0, 0]), a_o, b_o),
+                                K, V, P - 1, s)
+    mo = H.assert_close(H.to64(oo[0, 0]), ref_out, torch.bfloat16, f"{name} o_out")
+    _say(f"{name}: {len(pos)} base rows x {Hq} heads max-abs {mb[0]:.2e} mean-rel {mb[1]:.2e}; "
+         f"output row max-abs {mo[0]:.2e} mean-rel {mo[1]:.2e}")
+    return wl, inp, K, V, oo
+
+
+def test_prefill_8b_32k_fullsize():
+    _run_prefill_fullsize("prefill_8b_32k", 40)
+
+
+def test_prefill_8b_128k_planted_fullsize():
+    wl, inp, K, V, oo = _run_prefill_fullsize("prefill_8b_128k", 40)
+    p = inp["planted_pos"]
+    P = wl.length
+    assert p is not None and 0 <= p < P - wl.window
+    # The planted key is outside every base window that the output row's own position would
+    # see, and it dominates the output row of each head h = g G: the oracle's weights put
+    # their maximum on it, and the GPU row agrees with the oracle row (checked above).
+    G = wl.q_heads // wl.kv_heads
+    a_o, b_o = H.to64(inp["affine"][2]), H.to64(inp["affine"][3])
+    q_o = oracle.scale_offset(H.to64(inp["q_out"][0, 0]), a_o, b_o)
+    s = oracle.default_scale(wl.head_dim)
+    for g in range(wl.kv_heads):
+        wts = oracle.attention_weights(q_o[g * G], K[:, g, :], s)
+        assert int(np.argmax(wts)) == p
+
+
+def test_pt_1p3b_2k_fullsize():
+    wl = syn.WORKLOADS["pt_1p3b_2k"]
+    _say("full-size pt", wl)
+    inp = syn.make_pt(wl, device=DEV)
+    B, T, Hq, d = inp["q_base"].shape
+    Hkv = inp["k"].shape[2]
+    shape = ox.Shape(B, Hq, Hkv, d, wl.window, torch.bfloat16, T)
+    ob = H.nan_like((B, T, Hq, d), torch.bfloat16, DEV)
+    oo = H.nan_like((B, T, Hq, d), torch.bfloat16, DEV)
+    ws = ox.make_workspace(shape, DEV)
+    ox.forward_pt(shape, inp["q_base"], inp["q_out"], inp["k"], inp["v"],
+                  ox.Affine(*inp["affine"]), ob, oo, ws)
+    torch.cuda.synchronize()
+    assert not torch.isnan(ob).any().item() and not torch.isnan(oo).any().item()
+    a_b, b_b, a_o, b_o = H.affine64(inp["affine"])
+    s = oracle.default_scale(d)
+    worst = [0.0, 0.0]
+    for b in range(B):
+        pos = _positions(T, wl.window, 12, wl.seed + b)
+        idx = torch.as_tensor(pos, device=DEV)
+        K = H.to64(inp["k"][b])
+        V = H.to64(inp["v"][b])
+        mb = _base_rows_ok(H.to64(inp["q_base"][b].index_select(0, idx)), K, V, pos, a_b, b_b,
+                           wl.window, H.to64(ob[b].index_select(0, idx)), f"pt o_base b{b}")
+        qo = H.to64(inp["q_out"][b].index_select(0, idx))
+        ref = np.stack([oracle.output_row(oracle.scale_offset(qo[i], a_o, b_o), K, V, t, s)
+                        for i, t in enumerate(pos)])
+        mo = H.assert_close(H.to64(oo[b].index_select(0, idx)), ref, torch.bfloat16,
+                            f"pt o_out b{b}")
+        worst = [max(worst[0], mb[0], mo[0]), max(worst[1], mb[1], mo[1])]
+    _say(f"pt_1p3b_2k: max-abs {worst[0]:.2e} mean-rel {worst[1]:.2e}")
+
+
+def test_decode_8b_128k_fullsize():
+    """Two consecutive steps of the 16 x 131072 decode workload; three sequences checked."""
+    wl = syn.WORKLOADS["decode_8b_128k"]
+    _say("full-size decode", wl)
+    steps = 2
+    B, L0, Hq, Hkv, d = wl.batch, wl.length, wl.q_heads, wl.kv_heads, wl.head_dim
+    cap = L0 + wl.steps + 4  # as the benchmark sizes it
+    inp = syn.make_decode_resident(wl, DEV, cap)
+    ck, cv = inp["cache_k"], inp["cache_v"]
+    shape = ox.Shape(B, Hq, Hkv, d, wl.window, torch.bfloat16, cap)
+    cl = torch.full((B,), L0, dtype=torch.int32, device=DEV)
+    ws = ox.make_workspace(shape, DEV)
+    aff = ox.Affine(*inp["affine"])
+    check = [0, 7, 15]
+    hist = {b: (H.to64(ck[b, :, :L0].permute(1, 0, 2)), H.to64(cv[b, :, :L0].permute(1, 0, 2)))
+            for b in check}
+    a64 = H.affine64(inp["affine"])
+    for s in range(steps):
+        ob = H.nan_like((B, Hq, d), torch.bfloat16, DEV)
+        oo = H.nan_like((B, Hq, d), torch.bfloat16, DEV)
+        ox.decode_step(shape, inp["q_base"][s], inp["q_out"][s], inp["k_new"][s], inp["v_new"][s],
+                       aff, ck, cv, cl, L0 + s, ob, oo, ws)
+        torch.cuda.synchronize()
+        assert not torch.isnan(ob).any().item() and not torch.isnan(oo).any().item()
+        for b in check:
+            hk, hv = hist[b]
+            rb, ro, nk, nv, _ = oracle.decode_step(
+                [hk], [hv], np.array([L0 + s]), H.to64(inp["q_base"][s, b:b + 1]),
+                H.to64(inp["q_out"][s, b:b + 1]), H.to64(inp["k_new"][s, b:b + 1]),
+                H.to64(inp["v_new"][s, b:b + 1]), *a64, window=wl.window)
+            mb = H.assert_close(H.to64(ob[b:b + 1]), rb, torch.bfloat16, f"o_base step {s} seq {b}")
+            mo = H.assert_close(H.to64(oo[b:b + 1]), ro, torch.bfloat16, f"o_out step {s} seq {b}")
+            hist[b] = (nk[0], nv[0])
+            _say(f"decode step {s} seq {b}: base max-abs {mb[0]:.2e} rel {mb[1]:.2e}; "
+                 f"out max-abs {mo[0]:.2e} rel {mo[1]:.2e}")
+    assert cl.cpu().tolist() == [L0 + steps] * B
+    assert ox.read_device_status(ws) == 0
+    for s in range(steps):  # appended rows, bit for bit
+        assert torch.equal(ck[:, :, L0 + s], inp["k_new"][s])
+        assert torch.equal(cv[:, :, L0 + s], inp["v_new"][s])
