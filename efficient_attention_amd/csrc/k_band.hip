@@ -9,11 +9,11 @@
 // Work-group: 8 wavefronts (two per SIMD), HPW query heads sharing one kv head x (8 / HPW)
 // position blocks of 32 rows. One kv head's 64-key K and V tiles are copied straight from
 // global memory into a 4-slot LDS ring (row-major, 16-byte slots XOR-swizzled per row so the
-// operand reads hit all 64 banks) and read by all eight wavefronts. With the transposed score
+// operand reads hit all 64 banks) and read by all eight wavefronts. The copies are waited for
+// only at the barrier that publishes them, never by the reads of the other slots. With the transposed score
 // layout S^T (keys x queries) each lane owns one query and its softmax stays in registers:
-//   S^T[64 x 32]  = K . Q^T - m    16 x mfma_f32_32x32x16_bf16 (d = 128); the reference max m
-//                                  enters as the accumulator input (no per-score subtract)
-//   online softmax in the exp2 domain; the reference moves only when a half-tile's
+//   S^T[64 x 32]  = K . Q^T        16 x mfma_f32_32x32x16_bf16 (d = 128)
+//   online softmax in the exp2 domain, p = exp2(s - m); the reference m moves only when a half-tile's
 //   probabilities could exceed 2^8 (their sum does), so the common path computes no maximum
 //   O^T[d x 32]  += V^T . P^T      16 x mfma_f32_32x32x16_bf16; P^T straight from the S^T
 //                                  registers; V^T through the LDS transpose read
@@ -48,6 +48,25 @@ __device__ __forceinline__ float lane_pair_sum(float x) {
   const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 }
+
+// One wave-wide 16-byte-per-lane copy from global memory straight into LDS (lane i fills
+// bytes 16 i .. 16 i + 15 from the address `lds`). Issued as inline assembly so the compiler does
+// not make every later LDS read wait for it (it cannot tell the copy's destination slot from the
+// slots being read); the kernel waits for these copies itself before the barrier that publishes
+// them. M0, which carries the LDS address, is restored afterwards.
+__device__ __forceinline__ void copy_to_lds(const void* g, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(g)
+      : "memory");
+}
+__device__ __forceinline__ void wait_lds_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Scheduling hint for one region: NPRE LDS reads first, then NM times {1 MFMA, NDS LDS reads,
 // NV vector instructions}, so the vector work issues in the shadow of the matrix cores.
@@ -167,27 +186,42 @@ __global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
   constexpr int LROWS = 1024 / ROWB;
   constexpr int NINST = kTK / LROWS / kNW;
   static_assert(NINST >= 1 && NINST * LROWS * kNW == kTK, "staging covers a tile exactly");
-  int srow[NINST], skcol[NINST], svcol[NINST];
+  // Each lane's byte offsets within a tile are fixed; a tile's base address is a scalar, so a
+  // load is one instruction with no address arithmetic. In the tile holding the last key, rows
+  // past the sequence end re-read the last row (every read stays inside K and V).
+  const uint32_t rowb = (uint32_t)p.k_st * 2u;  // bytes between consecutive keys
+  uint32_t skoff[NINST], svoff[NINST];
+  int srow[NINST];
 #pragma unroll
   for (int i = 0; i < NINST; ++i) {
     const int r = (wv * NINST + i) * LROWS + lane / NCH;
     const int c = lane % NCH;
     srow[i] = r;
-    skcol[i] = 8 * (c ^ (r % NCH));
-    svcol[i] = 8 * (c ^ (4 * ((r >> 1) % (NCH / 4))));
+    skoff[i] = (uint32_t)r * rowb + 16u * (uint32_t)(c ^ (r % NCH));
+    svoff[i] = (uint32_t)r * rowb + 16u * (uint32_t)(c ^ (4 * ((r >> 1) % (NCH / 4))));
   }
+  const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) unsigned char*)smem);
   auto load_tile = [&](int e) {
     const int tb = tile_key(e);
+    const unsigned char* kt = reinterpret_cast<const unsigned char*>(kbase) + (idx_t)tb * rowb;
+    const unsigned char* vt = reinterpret_cast<const unsigned char*>(vbase) + (idx_t)tb * rowb;
     unsigned char* st = smem + (e % kStages) * STAGEB;
+    if (tb + kTK <= p.T) {
 #pragma unroll
-    for (int i = 0; i < NINST; ++i) {
-      int key = tb + srow[i];
-      if (key > p.T - 1) key = p.T - 1;
-      const idx_t ro = (idx_t)key * p.k_st;
-      lds_void* kd = (lds_void*)(st + (wv * NINST + i) * 1024);
-      lds_void* vd = (lds_void*)(st + TILEB + (wv * NINST + i) * 1024);
-      __builtin_amdgcn_global_load_lds((const void*)(kbase + ro + skcol[i]), kd, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(vbase + ro + svcol[i]), vd, 16, 0, 0);
+      for (int i = 0; i < NINST; ++i) {
+        const uint32_t kd = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(st - smem) + (wv * NINST + i) * 1024);
+        copy_to_lds(kt + skoff[i], kd);
+        copy_to_lds(vt + svoff[i], kd + TILEB);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NINST; ++i) {
+        const int over = srow[i] - (p.T - 1 - tb);
+        const uint32_t back = over > 0 ? (uint32_t)over * rowb : 0u;
+        const uint32_t kd = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(st - smem) + (wv * NINST + i) * 1024);
+        copy_to_lds(kt + (skoff[i] - back), kd);
+        copy_to_lds(vt + (svoff[i] - back), kd + TILEB);
+      }
     }
   };
 
@@ -220,9 +254,9 @@ __global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
   // its window, and -mref in every slot (the QK accumulator's initial value).
   float mref = 0.f, l = 0.f;
   bool started = false;
-  f32x16 negm;
+  f32x16 zero16;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) negm[r] = 0.f;
+  for (int r = 0; r < 16; ++r) zero16[r] = 0.f;
 
   // ---- building blocks ----------------------------------------------------------------------
   // Scores of key half m of tile e (8 MFMAs): S = K rows 32 m .. 32 m + 31 . Q^T - mref.
@@ -231,7 +265,7 @@ __global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(st + qk_off[s]);
-      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], s == 0 ? negm : S, 0, 0, 0);
+      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], s == 0 ? zero16 : S, 0, 0, 0);
     }
   };
   // O^T += V^T . P^T over key half m of tile e (2 16-key steps x NDT MFMAs).
@@ -265,8 +299,8 @@ __global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
     float s0 = 0.f, s1 = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
-      const float p0 = fast_exp2(S[r]);
-      const float p1 = fast_exp2(S[r + 1]);
+      const float p0 = fast_exp2(S[r] - mref);
+      const float p1 = fast_exp2(S[r + 1] - mref);
       s0 += p0;
       s1 += p1;
       Ph[r >> 3][r & 7] = (__bf16)p0;
@@ -276,10 +310,11 @@ __global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
   };
   // After the tentative probabilities of a half: the reference moves only if a probability of
   // the query could exceed 2^8 (their sum over both lane halves does) or the query meets its
-  // first key. Then O and l are rescaled, this half's scores and the next half's (already
-  // accumulating against the old reference) shifted, and this half's probabilities redone;
-  // the new reference is the exact maximum, so they end up <= 1.
-  auto settle = [&](f32x16& S, f32x16& Snext, bf16x8* Ph, float ps) {
+  // first key. Then O and l are rescaled, this half's probabilities redone from its shifted
+  // scores (S itself is dead afterwards and is not rewritten), and the next half's scores,
+  // already accumulated against the old reference, recomputed by `redo_next`. The new
+  // reference is the exact maximum, so the probabilities end up <= 1.
+  auto settle = [&](const f32x16& S, bf16x8* Ph, float ps) {
     const float tot = lane_pair_sum(ps);
     const bool need = !(tot <= kLazyBound) || !started;
     if (__builtin_amdgcn_ballot_w64(need)) {
@@ -289,7 +324,7 @@ __global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
         a0 = fmaxf(a0, fmaxf(S[r], S[r + 1]));
         a1 = fmaxf(a1, fmaxf(S[r + 2], S[r + 3]));
       }
-      const float mx = lane_pair_max(fmaxf(a0, a1));
+      const float mx = lane_pair_max(fmaxf(a0, a1)) - mref;
       const bool move = need && mx != kNegInf;
       const float dlt = move ? mx : 0.f;
       const float alpha = started ? fast_exp2(-dlt) : 0.f;  // nothing accumulated yet: O, l = 0
@@ -298,12 +333,6 @@ __global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
       l *= alpha;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) O[dt] *= alpha;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        negm[r] = -mref;
-        S[r] -= dlt;
-        Snext[r] -= dlt;
-      }
       ps = expo(S, Ph);
     }
     l += ps;
@@ -320,9 +349,10 @@ __global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
   // ends iteration e (the barrier waits for outstanding loads).
   load_tile(0);
   if (ntiles > 1) load_tile(1);
+  wait_lds_copies();
   __syncthreads();
 
-  f32x16 S0 = negm, S1 = negm;
+  f32x16 S0 = zero16, S1 = zero16;
   bf16x8 P0[2], P1[2];
   for (int e = 0; e < ntiles; ++e) {
     if (e + 2 < ntiles) load_tile(e + 2);
@@ -345,7 +375,7 @@ __global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
         mask(S0, e, 0);
         ps = expo(S0, P0);
       }
-      settle(S0, S1, P0, ps);
+      settle(S0, P0, ps);
       if (next && fl) {
         qk(S0, e + 1, 0);
         pv(P0, e, 0);
@@ -361,9 +391,10 @@ __global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
         mask(S1, e, 1);
         ps = expo(S1, P1);
       }
-      settle(S1, S0, P1, ps);
+      settle(S1, P1, ps);
       if (!next) pv(P1, e, 1);
     }
+    wait_lds_copies();  // tile e + 2 has landed before the barrier publishes it
     __syncthreads();
   }
 
