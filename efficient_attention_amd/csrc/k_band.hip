@@ -249,9 +249,9 @@ __global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
   for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) O[dt][r] = 0.f;
-  // This lane's query t0w + j: reference max (scores are kept relative to it, exp2 domain),
-  // this lane's part of the row sum (its half of the keys), whether the query has met a key of
-  // its window, and -mref in every slot (the QK accumulator's initial value).
+  // This lane's query t0w + j: reference max (probabilities are exp2(score - mref)), this lane's
+  // part of the row sum (its half of the keys), and whether the query has met a key of its
+  // window.
   float mref = 0.f, l = 0.f;
   bool started = false;
   f32x16 zero16;
@@ -259,7 +259,7 @@ __global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
   for (int r = 0; r < 16; ++r) zero16[r] = 0.f;
 
   // ---- building blocks ----------------------------------------------------------------------
-  // Scores of key half m of tile e (8 MFMAs): S = K rows 32 m .. 32 m + 31 . Q^T - mref.
+  // Scores of key half m of tile e (NKS MFMAs): S = K rows 32 m .. 32 m + 31 . Q^T.
   auto qk = [&](f32x16& S, int e, int m) {
     const unsigned char* st = smem + (e % kStages) * STAGEB + 32 * m * ROWB;
 #pragma unroll
