@@ -22,11 +22,13 @@ struct WsLayout {
   size_t pm, pl, po, total;
 };
 
-int64_t rows_max(const orthros_shape* s) { return (int64_t)s->batch * s->num_q_heads * 2; }
+constexpr int64_t kSftSplitRows = 16;  // SFT: up to this many response rows use split-key rows
 
-WsLayout ws_layout(const orthros_shape* s) {
+// rows_per_head: split-partial rows reserved per (sequence, query head); 2 covers prefill's
+// output row and decode's pair, SFT reserves one per response row when it uses split rows.
+WsLayout ws_layout(const orthros_shape* s, int64_t rows_per_head = 2) {
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
-  const size_t rows = (size_t)rows_max(s);
+  const size_t rows = (size_t)s->batch * s->num_q_heads * (size_t)rows_per_head;
   WsLayout L;
   L.pm = kStatusBytes;
   L.pl = L.pm + up(rows * kMaxSplits * sizeof(float));
@@ -64,11 +66,13 @@ int check_ptrs(std::initializer_list<const void*> ps) {
   return ORTHROS_OK;
 }
 
-int check_ws(const orthros_shape* s, const void* ws, size_t bytes) {
+int check_ws(const orthros_shape* s, const void* ws, size_t bytes, int64_t rows_per_head = 2) {
   if (!ws || !aligned16(ws)) return ORTHROS_E_WORKSPACE;
-  if (bytes < ws_layout(s).total) return ORTHROS_E_WORKSPACE;
+  if (bytes < ws_layout(s, rows_per_head).total) return ORTHROS_E_WORKSPACE;
   return ORTHROS_OK;
 }
+
+int64_t sft_rows_per_head(int64_t R) { return R <= kSftSplitRows ? (R > 2 ? R : 2) : 2; }
 
 float scale_of(const orthros_shape* s) {
   return s->softmax_scale > 0.f ? s->softmax_scale : 1.f / std::sqrt((float)s->head_dim);
@@ -135,6 +139,11 @@ size_t orthros_workspace_bytes(const orthros_shape* shape) {
   return ws_layout(shape).total;
 }
 
+size_t orthros_sft_workspace_bytes(const orthros_shape* shape, int64_t R) {
+  if (check_shape(shape) != ORTHROS_OK || R < 1) return 0;
+  return ws_layout(shape, sft_rows_per_head(R)).total;
+}
+
 const char* orthros_status_string(int code) {
   switch (code) {
     case ORTHROS_OK: return "ok";
@@ -197,7 +206,8 @@ int orthros_prefill(const orthros_shape* s, int64_t P, const void* q_base, const
   bp.alpha = aff->alpha_base; bp.beta = aff->beta_base;
   bp.k = k; bp.v = v; bp.k_sb = P * Hkv * d; bp.k_st = (idx_t)Hkv * d; bp.k_sh = d;
   bp.o = o_base; bp.o_sb = P * Hq * d; bp.o_st = (idx_t)Hq * d; bp.o_sh = d;
-  bp.B = B; bp.T = (int)P; bp.Hq = Hq; bp.Hkv = Hkv; bp.G = G;
+  bp.B = B; bp.nrows = (int)P; bp.nkeys = (int)P; bp.t_first = 0; bp.pos = nullptr;
+  bp.Hq = Hq; bp.Hkv = Hkv; bp.G = G;
   bp.window = s->window < (int)P ? s->window : (int)P;
   bp.scale_log2 = scale * kLog2e;
   rc = launch_rc(run_stage(ORTHROS_STAGE_BAND, st, [&] { return launch_band(bp, d, st); }));
@@ -353,7 +363,8 @@ int orthros_forward_pt(const orthros_shape* s, int64_t T, const void* q_base, co
   bp.alpha = aff->alpha_base; bp.beta = aff->beta_base;
   bp.k = k; bp.v = v; bp.k_sb = T * Hkv * d; bp.k_st = (idx_t)Hkv * d; bp.k_sh = d;
   bp.o = o_base; bp.o_sb = T * Hq * d; bp.o_st = (idx_t)Hq * d; bp.o_sh = d;
-  bp.B = B; bp.T = (int)T; bp.Hq = Hq; bp.Hkv = Hkv; bp.G = G;
+  bp.B = B; bp.nrows = (int)T; bp.nkeys = (int)T; bp.t_first = 0; bp.pos = nullptr;
+  bp.Hq = Hq; bp.Hkv = Hkv; bp.G = G;
   bp.window = s->window < (int)T ? s->window : (int)T;
   bp.scale_log2 = scale * kLog2e;
   rc = launch_rc(run_stage(ORTHROS_STAGE_BAND, st, [&] { return launch_band(bp, d, st); }));
@@ -362,6 +373,198 @@ int orthros_forward_pt(const orthros_shape* s, int64_t T, const void* q_base, co
   op.q = q_out; op.alpha = aff->alpha_out; op.beta = aff->beta_out; op.o = o_out;
   op.window = (int)T;  // window >= T: full causal rows (Eq. 5)
   return launch_rc(run_stage(ORTHROS_STAGE_BAND, st, [&] { return launch_band(op, d, st); }));
+}
+
+int orthros_prefill_chunk(const orthros_shape* s, int64_t past_len, int64_t C,
+                          const void* q_base, const void* q_out, const void* k, const void* v,
+                          const orthros_affine* aff, void* cache_k, void* cache_v,
+                          int32_t* cache_len, void* o_base, void* o_out, void* ws,
+                          size_t ws_bytes, hipStream_t st) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if (past_len < 0 || C < 1 || C > INT_MAX / 2 || past_len > INT_MAX / 2) return ORTHROS_E_INVALID;
+  if ((rc = check_affine(aff))) return rc;
+  if ((rc = check_ptrs({q_base, q_out, k, v, cache_k, cache_v, cache_len, o_base, o_out}))) return rc;
+  if ((rc = check_ws(s, ws, ws_bytes))) return rc;
+  if (past_len + C > s->capacity) return ORTHROS_E_CAPACITY;
+
+  const int B = s->batch, Hq = s->num_q_heads, Hkv = s->num_kv_heads, d = s->head_dim;
+  const int G = Hq / Hkv;
+  const float scale = scale_of(s);
+  const WsLayout L = ws_layout(s);
+  char* wsc = static_cast<char*>(ws);
+  const int64_t n = past_len + C;  // keys after this chunk
+  const idx_t c_sb = (idx_t)Hkv * s->capacity * d, c_sh = (idx_t)s->capacity * d;
+
+  CacheWriteParams cw{k, v, cache_k, cache_v, cache_len, B, (int)C, Hkv, d, esize(s), s->capacity,
+                      past_len};
+  rc = launch_rc(run_stage(ORTHROS_STAGE_CACHE_WRITE, st, [&] { return launch_cache_write(cw, st); }));
+  if (rc) return rc;
+
+  if (s->dtype == ORTHROS_F32) {
+    RowsF32Params r{};
+    r.q = static_cast<const float*>(q_base);
+    r.q_sb = C * Hq * d; r.q_st = (idx_t)Hq * d; r.q_sh = d;
+    r.alpha = aff->alpha_base; r.beta = aff->beta_base;
+    r.k = static_cast<const float*>(cache_k); r.v = static_cast<const float*>(cache_v);
+    r.k_sb = c_sb; r.k_st = d; r.k_sh = c_sh;
+    r.o = static_cast<float*>(o_base);
+    r.o_sb = C * Hq * d; r.o_st = (idx_t)Hq * d; r.o_sh = d;
+    r.B = B; r.Hq = Hq; r.Hkv = Hkv; r.G = G; r.d = d; r.nrows = (int)C; r.t0 = (int)past_len;
+    r.window = s->window; r.scale = scale;
+    rc = launch_rc(run_stage(ORTHROS_STAGE_ROWS_F32, st, [&] { return launch_rows_f32(r, st); }));
+    if (rc) return rc;
+    RowsF32Params o = r;
+    o.q = static_cast<const float*>(q_out);
+    o.q_sb = (idx_t)Hq * d; o.q_st = 0;
+    o.alpha = aff->alpha_out; o.beta = aff->beta_out;
+    o.o = static_cast<float*>(o_out);
+    o.o_sb = (idx_t)Hq * d; o.o_st = 0;
+    o.nrows = 1; o.t0 = (int)(n - 1); o.window = INT_MAX;
+    return launch_rc(run_stage(ORTHROS_STAGE_ROWS_F32, st, [&] { return launch_rows_f32(o, st); }));
+  }
+
+  // Base rows of the chunk (positions past_len .. n-1) over the cache, which now holds them.
+  BandParams bp{};
+  bp.q = q_base; bp.q_sb = C * Hq * d; bp.q_st = (idx_t)Hq * d; bp.q_sh = d;
+  bp.alpha = aff->alpha_base; bp.beta = aff->beta_base;
+  bp.k = cache_k; bp.v = cache_v; bp.k_sb = c_sb; bp.k_st = d; bp.k_sh = c_sh;
+  bp.o = o_base; bp.o_sb = C * Hq * d; bp.o_st = (idx_t)Hq * d; bp.o_sh = d;
+  bp.B = B; bp.nrows = (int)C; bp.nkeys = (int)n; bp.t_first = (int)past_len; bp.pos = nullptr;
+  bp.Hq = Hq; bp.Hkv = Hkv; bp.G = G;
+  bp.window = s->window < (int)n ? s->window : (int)n;
+  bp.scale_log2 = scale * kLog2e;
+  rc = launch_rc(run_stage(ORTHROS_STAGE_BAND, st, [&] { return launch_band(bp, d, st); }));
+  if (rc) return rc;
+
+  // Output row at the chunk's last token over the whole cache.
+  SplitParams sp{};
+  sp.q_out = q_out; sp.q_sb = (idx_t)Hq * d; sp.q_sh = d;
+  sp.a_out = aff->alpha_out; sp.b_out = aff->beta_out;
+  sp.a_base = aff->alpha_base; sp.b_base = aff->beta_base;
+  sp.k = cache_k; sp.v = cache_v;
+  sp.k_sb = c_sb; sp.k_sh = c_sh; sp.k_st = d;
+  sp.n_fixed = n;
+  sp.R = 1;
+  sp.B = B; sp.Hq = Hq; sp.Hkv = Hkv; sp.G = G;
+  sp.HC = heads_per_chunk(G, false);
+  sp.nchunks = (G + sp.HC - 1) / sp.HC;
+  sp.window = s->window; sp.with_base = 0;
+  sp.nsplit = nsplit_for(n, (int64_t)B * Hkv * sp.nchunks);
+  sp.scale_log2 = scale * kLog2e;
+  sp.pm = reinterpret_cast<float*>(wsc + L.pm);
+  sp.pl = reinterpret_cast<float*>(wsc + L.pl);
+  sp.po = reinterpret_cast<float*>(wsc + L.po);
+  rc = launch_rc(run_stage(ORTHROS_STAGE_SPLIT_ROWS, st, [&] { return launch_split_rows(sp, d, st); }));
+  if (rc) return rc;
+  MergeParams mp{};
+  mp.pm = sp.pm; mp.pl = sp.pl; mp.po = sp.po;
+  mp.out0 = o_out; mp.o_sb0 = (idx_t)Hq * d; mp.o_sh0 = d;
+  mp.rows = B * Hq; mp.nsplit = sp.nsplit; mp.d = d; mp.Hq = Hq; mp.nstreams = 1; mp.bf16 = 1;
+  return launch_rc(run_stage(ORTHROS_STAGE_MERGE, st, [&] { return launch_merge(mp, st); }));
+}
+
+int orthros_forward_sft(const orthros_shape* s, int64_t T, const void* q_base, const void* q_out,
+                        const int32_t* out_pos, int64_t R, const void* k, const void* v,
+                        const orthros_affine* aff, void* cache_k, void* cache_v,
+                        int32_t* cache_len, void* o_base, void* o_out, void* ws,
+                        size_t ws_bytes, hipStream_t st) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if (T < 1 || T > INT_MAX / 2 || R < 1 || R > INT_MAX / 2) return ORTHROS_E_INVALID;
+  if ((rc = check_affine(aff))) return rc;
+  if ((rc = check_ptrs({q_base, q_out, k, v, o_base, o_out}))) return rc;
+  if (!out_pos || ((uintptr_t)out_pos & 3u)) return ORTHROS_E_INVALID;
+  const bool any_cache = cache_k || cache_v || cache_len;
+  if (any_cache && (rc = check_ptrs({cache_k, cache_v, cache_len}))) return rc;
+  if ((rc = check_ws(s, ws, ws_bytes, sft_rows_per_head(R)))) return rc;
+  if (any_cache && T > s->capacity) return ORTHROS_E_CAPACITY;
+
+  const int B = s->batch, Hq = s->num_q_heads, Hkv = s->num_kv_heads, d = s->head_dim;
+  const int G = Hq / Hkv;
+  const float scale = scale_of(s);
+  const WsLayout L = ws_layout(s, sft_rows_per_head(R));
+  char* wsc = static_cast<char*>(ws);
+
+  if (any_cache) {
+    CacheWriteParams cw{k, v, cache_k, cache_v, cache_len, B, (int)T, Hkv, d, esize(s), s->capacity};
+    rc = launch_rc(run_stage(ORTHROS_STAGE_CACHE_WRITE, st, [&] { return launch_cache_write(cw, st); }));
+    if (rc) return rc;
+  }
+
+  if (s->dtype == ORTHROS_F32) {
+    RowsF32Params r{};
+    r.q = static_cast<const float*>(q_base);
+    r.q_sb = T * Hq * d; r.q_st = (idx_t)Hq * d; r.q_sh = d;
+    r.alpha = aff->alpha_base; r.beta = aff->beta_base;
+    r.k = static_cast<const float*>(k); r.v = static_cast<const float*>(v);
+    r.k_sb = T * Hkv * d; r.k_st = (idx_t)Hkv * d; r.k_sh = d;
+    r.o = static_cast<float*>(o_base);
+    r.o_sb = T * Hq * d; r.o_st = (idx_t)Hq * d; r.o_sh = d;
+    r.B = B; r.Hq = Hq; r.Hkv = Hkv; r.G = G; r.d = d; r.nrows = (int)T; r.t0 = 0;
+    r.window = s->window; r.scale = scale; r.nkeys = T;
+    rc = launch_rc(run_stage(ORTHROS_STAGE_ROWS_F32, st, [&] { return launch_rows_f32(r, st); }));
+    if (rc) return rc;
+    RowsF32Params o = r;
+    o.q = static_cast<const float*>(q_out);
+    o.q_sb = R * Hq * d; o.q_st = (idx_t)Hq * d;
+    o.alpha = aff->alpha_out; o.beta = aff->beta_out;
+    o.o = static_cast<float*>(o_out);
+    o.o_sb = R * Hq * d; o.o_st = (idx_t)Hq * d;
+    o.nrows = (int)R; o.pos = out_pos; o.window = INT_MAX;
+    return launch_rc(run_stage(ORTHROS_STAGE_ROWS_F32, st, [&] { return launch_rows_f32(o, st); }));
+  }
+
+  // Base rows: Eq. 4 at every position.
+  BandParams bp{};
+  bp.q = q_base; bp.q_sb = T * Hq * d; bp.q_st = (idx_t)Hq * d; bp.q_sh = d;
+  bp.alpha = aff->alpha_base; bp.beta = aff->beta_base;
+  bp.k = k; bp.v = v; bp.k_sb = T * Hkv * d; bp.k_st = (idx_t)Hkv * d; bp.k_sh = d;
+  bp.o = o_base; bp.o_sb = T * Hq * d; bp.o_st = (idx_t)Hq * d; bp.o_sh = d;
+  bp.B = B; bp.nrows = (int)T; bp.nkeys = (int)T; bp.t_first = 0; bp.pos = nullptr;
+  bp.Hq = Hq; bp.Hkv = Hkv; bp.G = G;
+  bp.window = s->window < (int)T ? s->window : (int)T;
+  bp.scale_log2 = scale * kLog2e;
+  rc = launch_rc(run_stage(ORTHROS_STAGE_BAND, st, [&] { return launch_band(bp, d, st); }));
+  if (rc) return rc;
+
+  if (R > kSftSplitRows) {
+    // Many response rows: the banded kernel with the row positions, full causal windows.
+    BandParams op = bp;
+    op.q = q_out; op.q_sb = R * Hq * d; op.q_st = (idx_t)Hq * d;
+    op.alpha = aff->alpha_out; op.beta = aff->beta_out;
+    op.o = o_out; op.o_sb = R * Hq * d; op.o_st = (idx_t)Hq * d;
+    op.nrows = (int)R; op.pos = out_pos;
+    op.window = (int)T;
+    return launch_rc(run_stage(ORTHROS_STAGE_BAND, st, [&] { return launch_band(op, d, st); }));
+  }
+
+  // Few response rows: split-key rows, each (row, head) pair over keys 0 .. pos[row].
+  SplitParams sp{};
+  sp.q_out = q_out; sp.q_sb = R * Hq * d; sp.q_st = (idx_t)Hq * d; sp.q_sh = d;
+  sp.a_out = aff->alpha_out; sp.b_out = aff->beta_out;
+  sp.a_base = aff->alpha_base; sp.b_base = aff->beta_base;
+  sp.k = k; sp.v = v;
+  sp.k_sb = T * Hkv * d; sp.k_sh = d; sp.k_st = (idx_t)Hkv * d;
+  sp.n_fixed = T;
+  sp.pos = out_pos; sp.R = (int)R;
+  sp.B = B; sp.Hq = Hq; sp.Hkv = Hkv; sp.G = G;
+  sp.HC = 16;
+  sp.nchunks = (int)((R * G + 15) / 16);
+  sp.window = s->window; sp.with_base = 0;
+  sp.nsplit = nsplit_for(T, (int64_t)B * Hkv * sp.nchunks);
+  sp.scale_log2 = scale * kLog2e;
+  sp.pm = reinterpret_cast<float*>(wsc + L.pm);
+  sp.pl = reinterpret_cast<float*>(wsc + L.pl);
+  sp.po = reinterpret_cast<float*>(wsc + L.po);
+  rc = launch_rc(run_stage(ORTHROS_STAGE_SPLIT_ROWS, st, [&] { return launch_split_rows(sp, d, st); }));
+  if (rc) return rc;
+  MergeParams mp{};
+  mp.pm = sp.pm; mp.pl = sp.pl; mp.po = sp.po;
+  mp.out0 = o_out; mp.o_sb0 = R * Hq * d; mp.o_st0 = (idx_t)Hq * d; mp.o_sh0 = d;
+  mp.rows = (int)(B * Hq * R); mp.nsplit = sp.nsplit; mp.d = d; mp.Hq = Hq;
+  mp.nstreams = (int)R; mp.rows_out0 = 1; mp.bf16 = 1;
+  return launch_rc(run_stage(ORTHROS_STAGE_MERGE, st, [&] { return launch_merge(mp, st); }));
 }
 
 int orthros_read_device_status(void* ws, size_t ws_bytes, int32_t* host_status, int clear,

@@ -96,10 +96,10 @@ __global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int nhc = p.G / HPW;
-  const int npb = (p.T + BMP - 1) / BMP;
+  const int npb = (p.nrows + BMP - 1) / BMP;
   const uint32_t total = (uint32_t)p.B * p.Hkv * nhc * npb;
   const uint32_t lid = xcd_swizzle(blockIdx.x, total);
-  const bool causal = p.window >= p.T;
+  const bool causal = p.window >= p.nkeys;
   int pb, rest;
   if (causal) {  // longest rows first
     const int inner = p.B * p.Hkv * nhc;
@@ -113,23 +113,61 @@ __global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
   rest /= nhc;
   const int g = rest % p.Hkv;
   const int b = rest / p.Hkv;
-  const int t0 = pb * BMP;
+  const int r0 = pb * BMP;                     // first row of the work-group
   const int h = g * p.G + hc * HPW + (wv % HPW);
-  const int t0w = t0 + kQW * (wv / HPW);
+  const int r0w = r0 + kQW * (wv / HPW);       // first row of this wavefront
   const int j = lane & 31;   // query column of this lane within a column tile
   const int hh = lane >> 5;  // lane half
+  const int row = r0w + j;
+  const bool rvalid = row < p.nrows;
+  const bool wactive = r0w < p.nrows;
 
-  // Query fragments (B operand of 32x32x16): lane (j, hh) holds query t0w + j, channels
+  // Row positions: the lowest and highest of this wavefront's rows and of the work-group's.
+  int qmin_w, qmax_w, qmin_b, qmax_b, tq;
+  if (!p.pos) {
+    const int last_w = r0w + kQW - 1 < p.nrows - 1 ? r0w + kQW - 1 : p.nrows - 1;
+    const int last_b = r0 + BMP - 1 < p.nrows - 1 ? r0 + BMP - 1 : p.nrows - 1;
+    qmin_w = p.t_first + r0w;
+    qmax_w = p.t_first + last_w;
+    qmin_b = p.t_first + r0;
+    qmax_b = p.t_first + last_b;
+    tq = rvalid ? p.t_first + row : qmax_w;
+  } else {
+    __shared__ int wrange[2 * kNW];
+    int mine = rvalid ? p.pos[row] : 0;
+    mine = mine < 0 ? 0 : (mine > p.nkeys - 1 ? p.nkeys - 1 : mine);  // clamped into [0, nkeys)
+    int lo = rvalid ? mine : 0x7fffffff, hi = rvalid ? mine : -1;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      lo = min(lo, __shfl_xor(lo, off, 64));
+      hi = max(hi, __shfl_xor(hi, off, 64));
+    }
+    qmin_w = __builtin_amdgcn_readfirstlane(lo);
+    qmax_w = __builtin_amdgcn_readfirstlane(hi);
+    if (lane == 0) {
+      wrange[2 * wv] = qmin_w;
+      wrange[2 * wv + 1] = qmax_w;
+    }
+    __syncthreads();
+    qmin_b = 0x7fffffff;
+    qmax_b = -1;
+#pragma unroll
+    for (int i = 0; i < kNW; ++i) {
+      qmin_b = min(qmin_b, wrange[2 * i]);
+      qmax_b = max(qmax_b, wrange[2 * i + 1]);
+    }
+    tq = rvalid ? mine : qmax_w;  // rows past the end compute on a valid position, unstored
+  }
+
+  // Query fragments (B operand of 32x32x16): lane (j, hh) holds query row r0w + j, channels
   // 16 s + 8 hh + e.
   bf16x8 qf[NKS];
   {
     const float* al = p.alpha + (idx_t)h * D;
     const float* be = p.beta + (idx_t)h * D;
-    const int tq = t0w + j;
-    const bool ok = tq < p.T;
     const uint16_t* qr = reinterpret_cast<const uint16_t*>(p.q) + (idx_t)b * p.q_sb +
-                         (idx_t)(ok ? tq : 0) * p.q_st + (idx_t)h * p.q_sh;
-    const float sc = ok ? p.scale_log2 : 0.f;
+                         (idx_t)(rvalid ? row : 0) * p.q_st + (idx_t)h * p.q_sh;
+    const float sc = rvalid ? p.scale_log2 : 0.f;
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
       const int c0 = 16 * s + 8 * hh;
@@ -156,23 +194,22 @@ __global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
 
   // Key range of the work-group (tiles tile_hi, tile_hi - 64, ..., tile_lo) and of this wave.
   const int w = p.window;
-  const int glo = t0 - w + 1 > 0 ? t0 - w + 1 : 0;
-  const int ghi = (t0 + BMP - 1 < p.T - 1) ? t0 + BMP - 1 : p.T - 1;
+  const int nk = p.nkeys;
+  const int glo = qmin_b - w + 1 > 0 ? qmin_b - w + 1 : 0;
+  const int ghi = qmax_b < nk - 1 ? qmax_b : nk - 1;
   const int tile_lo = glo / kTK * kTK;
   const int tile_hi = ghi / kTK * kTK;
   const int ntiles = (tile_hi - tile_lo) / kTK + 1;
-  const bool wactive = t0w < p.T;
-  const int wmax = (t0w + kQW - 1 < p.T - 1) ? t0w + kQW - 1 : p.T - 1;  // last valid row
-  const int wlo = t0w - w + 1;  // lowest key any row of this wavefront needs (may be < 0)
+  const int wlo = qmin_w - w + 1;  // lowest key any row of this wavefront needs (may be < 0)
   auto tile_key = [&](int e) { return tile_hi - kTK * e; };
-  // This wavefront's tiles: ea (holds its last row) .. eb (holds its lowest key), contiguous.
-  const int ea = tile_hi > wmax ? (tile_hi - wmax + kTK - 1) / kTK : 0;
+  // This wavefront's tiles: ea (holds its highest row) .. eb (holds its lowest key), contiguous.
+  const int ea = tile_hi > qmax_w ? (tile_hi - qmax_w + kTK - 1) / kTK : 0;
   const int eb_w = (tile_hi + kTK - 1 - wlo) / kTK;
   const int eb = eb_w < ntiles - 1 ? eb_w : ntiles - 1;
   // Unmasked only if every key of the tile lies in every row's window.
   auto full = [&](int e) {
     const int tb = tile_key(e);
-    return (tb + kTK - 1 <= t0w) && (tb >= wmax - w + 1) && (tb + kTK - 1 <= p.T - 1);
+    return (tb + kTK - 1 <= qmin_w) && (tb >= qmax_w - w + 1) && (tb + kTK - 1 <= nk - 1);
   };
 
   const uint16_t* kbase = reinterpret_cast<const uint16_t*>(p.k) + (idx_t)b * p.k_sb + (idx_t)g * p.k_sh;
@@ -206,7 +243,7 @@ __global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
     const unsigned char* kt = reinterpret_cast<const unsigned char*>(kbase) + (idx_t)tb * rowb;
     const unsigned char* vt = reinterpret_cast<const unsigned char*>(vbase) + (idx_t)tb * rowb;
     unsigned char* st = smem + (e % kStages) * STAGEB;
-    if (tb + kTK <= p.T) {
+    if (tb + kTK <= nk) {
 #pragma unroll
       for (int i = 0; i < NINST; ++i) {
         const uint32_t kd = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(st - smem) + (wv * NINST + i) * 1024);
@@ -216,7 +253,7 @@ __global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
     } else {
 #pragma unroll
       for (int i = 0; i < NINST; ++i) {
-        const int over = srow[i] - (p.T - 1 - tb);
+        const int over = srow[i] - (nk - 1 - tb);
         const uint32_t back = over > 0 ? (uint32_t)over * rowb : 0u;
         const uint32_t kd = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(st - smem) + (wv * NINST + i) * 1024);
         copy_to_lds(kt + (skoff[i] - back), kd);
@@ -249,7 +286,7 @@ __global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
   for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) O[dt][r] = 0.f;
-  // This lane's query t0w + j: reference max (probabilities are exp2(score - mref)), this lane's
+  // This lane's query row r0w + j: reference max (probabilities are exp2(score - mref)), this lane's
   // part of the row sum (its half of the keys), and whether the query has met a key of its
   // window.
   float mref = 0.f, l = 0.f;
@@ -285,11 +322,10 @@ __global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
   // Keys outside the query's window (or past the sequence) of half m of tile e -> -inf.
   auto mask = [&](f32x16& S, int e, int m) {
     const int kb = tile_key(e) + 32 * m + 4 * hh;
-    const int tq = t0w + j;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int k = kb + 8 * (r >> 2) + (r & 3);
-      const bool ok = k <= tq && k > tq - w && k < p.T;
+      const bool ok = k <= tq && k > tq - w && k < nk;
       S[r] = ok ? S[r] : kNegInf;
     }
   };
@@ -398,11 +434,10 @@ __global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
     __syncthreads();
   }
 
-  const int tq = t0w + j;
   const float lt = lane_pair_sum(l);  // both lane halves of the query column
-  if (wactive && tq < p.T) {
+  if (rvalid) {
     const float inv = 1.f / lt;
-    uint16_t* orow = reinterpret_cast<uint16_t*>(p.o) + (idx_t)b * p.o_sb + (idx_t)tq * p.o_st + (idx_t)h * p.o_sh;
+    uint16_t* orow = reinterpret_cast<uint16_t*>(p.o) + (idx_t)b * p.o_sb + (idx_t)row * p.o_st + (idx_t)h * p.o_sh;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -422,7 +457,7 @@ hipError_t launch_band(const BandParams& p, int d, hipStream_t s) {
   else if (p.G % 4 == 0) hpw = 4;
   else if (p.G % 2 == 0) hpw = 2;
   const int bmp = kQW * (kNW / hpw);
-  const int npb = (p.T + bmp - 1) / bmp;
+  const int npb = (p.nrows + bmp - 1) / bmp;
   const uint32_t total = (uint32_t)p.B * p.Hkv * (p.G / hpw) * npb;
   dim3 grid(total), block(kThreads);
 #define ORTHROS_BAND(DD, HH) hipLaunchKernelGGL((band_kernel<DD, HH>), grid, block, 0, s, p)

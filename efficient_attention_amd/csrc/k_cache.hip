@@ -24,12 +24,12 @@ __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteParams p) {
     r /= p.Hkv;
     const idx_t t = r % p.T;
     const idx_t b = r / p.T;
-    const idx_t dst = ((b * p.Hkv + g) * p.cap + t) * cpr + c;
+    const idx_t dst = ((b * p.Hkv + g) * p.cap + p.t_first + t) * cpr + c;
     kdst[dst] = __builtin_nontemporal_load(ksrc + i);
     vdst[dst] = __builtin_nontemporal_load(vsrc + i);
   }
   if (blockIdx.x == 0) {
-    for (int b = threadIdx.x; b < p.B; b += blockDim.x) p.len[b] = p.T;
+    for (int b = threadIdx.x; b < p.B; b += blockDim.x) p.len[b] = (int32_t)(p.t_first + p.T);
   }
 }
 

@@ -26,6 +26,9 @@ __global__ __launch_bounds__(64) void rows_f32_kernel(RowsF32Params p) {
     const int64_t L = p.len[b];
     Lnew = L < 0 ? 0 : (L > p.cap ? p.cap : L);  // clamped: no read leaves the cache
     t = Lnew;
+  } else if (p.pos) {
+    const int64_t pr = p.pos[row];
+    t = pr < 0 ? 0 : (pr > p.nkeys - 1 ? p.nkeys - 1 : pr);  // no read leaves k / v
   } else {
     t = (int64_t)p.t0 + row;
   }

@@ -71,15 +71,31 @@ __global__ __launch_bounds__(256) void split_rows_kernel(SplitParams p) {
   const int64_t ke = kb + per < n ? kb + per : n;
 
   const int h0 = g * p.G + chunk * p.HC;
-  int nr = p.G - chunk * p.HC;
-  if (nr > p.HC) nr = p.HC;
+  int nr;  // occupied row slots of this chunk (output stream)
+  if (p.pos) {
+    nr = p.R * p.G - chunk * kRows;
+    if (nr > kRows) nr = kRows;
+  } else {
+    nr = p.G - chunk * p.HC;
+    if (nr > p.HC) nr = p.HC;
+  }
 
   // Row slot of this lane (MFMA column) and its key range.
   const int j = lane & 15;
   const int kg = lane >> 4;
-  int stream = -1, h = 0;
+  int stream = -1, h = 0, rr = 0;
   int64_t lo = 1, hi = 0;  // empty
-  if (j < nr) {
+  if (p.pos) {
+    if (j < nr) {
+      const int gr = chunk * kRows + j;
+      rr = gr / p.G;
+      h = g * p.G + gr % p.G;
+      stream = 0;
+      lo = 0;
+      const int64_t t = p.pos[rr];
+      hi = t < 0 ? 0 : (t > n - 1 ? n - 1 : t);  // positions outside [0, n) are clamped
+    }
+  } else if (j < nr) {
     stream = 0;
     h = h0 + j;
     lo = 0;
@@ -97,7 +113,8 @@ __global__ __launch_bounds__(256) void split_rows_kernel(SplitParams p) {
     const uint16_t* qsrc = nullptr;
     const float *al = nullptr, *be = nullptr;
     if (stream == 0) {
-      qsrc = reinterpret_cast<const uint16_t*>(p.q_out) + (idx_t)b * p.q_sb + (idx_t)h * p.q_sh;
+      qsrc = reinterpret_cast<const uint16_t*>(p.q_out) + (idx_t)b * p.q_sb + (idx_t)rr * p.q_st +
+             (idx_t)h * p.q_sh;
       al = p.a_out + (idx_t)h * D;
       be = p.b_out + (idx_t)h * D;
     } else if (stream == 1) {
@@ -265,9 +282,15 @@ __global__ __launch_bounds__(256) void split_rows_kernel(SplitParams p) {
         den += f * red[w * RW + kRows + jj];
       }
     }
-    const int st = jj < nr ? 0 : 1;
-    const int hh = h0 + (jj < nr ? jj : jj - nr);
-    const idx_t row = ((idx_t)b * p.Hq + hh) * nstreams + st;
+    idx_t row;
+    if (p.pos) {  // (head, response row) pair
+      const int gr = chunk * kRows + jj;
+      row = ((idx_t)b * p.Hq + g * p.G + gr % p.G) * p.R + gr / p.G;
+    } else {
+      const int st = jj < nr ? 0 : 1;
+      const int hh = h0 + (jj < nr ? jj : jj - nr);
+      row = ((idx_t)b * p.Hq + hh) * nstreams + st;
+    }
     p.po[(row * p.nsplit + s) * D + c] = o;
     if (c == 0) {
       p.pm[row * p.nsplit + s] = M;
@@ -301,8 +324,10 @@ __global__ __launch_bounds__(64) void merge_kernel(MergeParams p) {
   wgt[lane] = f;
   __syncthreads();
   const float inv = 1.f / den;
-  void* out = st == 0 ? p.out0 : p.out1;
-  const idx_t off = st == 0 ? b * p.o_sb0 + (idx_t)h * p.o_sh0 : b * p.o_sb1 + (idx_t)h * p.o_sh1;
+  void* out = (st == 0 || p.rows_out0) ? p.out0 : p.out1;
+  const idx_t off = p.rows_out0 ? b * p.o_sb0 + (idx_t)st * p.o_st0 + (idx_t)h * p.o_sh0
+                    : st == 0  ? b * p.o_sb0 + (idx_t)h * p.o_sh0
+                               : b * p.o_sb1 + (idx_t)h * p.o_sh1;
   const float* po = p.po + row * p.nsplit * p.d;
   for (int c = lane; c < p.d; c += 64) {
     float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;

@@ -10,6 +10,7 @@ typedef int64_t idx_t;
 
 // Bulk cache write (prefill / pre-training): k, v [B, T, Hkv, d] -> cache [B, Hkv, cap, d],
 // len[b] = T for every sequence.
+// Rows t of k, v go to cache rows t_first + t; len[b] = t_first + T afterwards.
 struct CacheWriteParams {
   const void* k;
   const void* v;
@@ -18,6 +19,7 @@ struct CacheWriteParams {
   int32_t* len;
   int B, T, Hkv, d, esize;
   int64_t cap;
+  int64_t t_first;
 };
 
 // Decode append: cache row len[b] <- (k_new, v_new)[b]; len[b]++ unless the cache is full.
@@ -51,7 +53,13 @@ struct SplitParams {
   idx_t kn_sb, kn_sh;    // decode: new key/value strides (batch, kv head)
   const int32_t* len;    // decode: device lengths (keys 0..len-1 cached, key len new)
   int64_t cap;           // decode: cache capacity (device lengths are clamped to it)
-  int64_t n_fixed;       // prefill: number of keys
+  int64_t n_fixed;       // prefill / SFT: number of keys
+  // SFT rows: when pos is set, the output rows of one kv head are the R x G pairs
+  // (response row r, head of the group), row r at position pos[r] (keys 0 .. pos[r]), its
+  // query at q_out + b q_sb + r q_st + h q_sh; chunks of 16 pairs.
+  const int32_t* pos;
+  int R;
+  idx_t q_st;
   int B, Hq, Hkv, G, HC, nchunks, window, nsplit, with_base;
   float scale_log2;
   float* pm;  // [rows][nsplit]
@@ -59,18 +67,22 @@ struct SplitParams {
   float* po;  // [rows][nsplit][d]
 };
 
-// Split merge: row r = (b * Hq + h) * nstreams + stream.
+// Split merge: row r = (b * Hq + h) * nstreams + stream. With rows_out0 set, every "stream" is
+// a row index written to out0 + b o_sb0 + stream o_st0 + h o_sh0 (SFT response rows).
 struct MergeParams {
   const float* pm;
   const float* pl;
   const float* po;
   void* out0;  // stream 0 (output stream)
   void* out1;  // stream 1 (base stream, decode)
-  idx_t o_sb0, o_sh0, o_sb1, o_sh1;
-  int rows, nsplit, d, Hq, nstreams, bf16;
+  idx_t o_sb0, o_sh0, o_sb1, o_sh1, o_st0;
+  int rows, nsplit, d, Hq, nstreams, bf16, rows_out0;
 };
 
-// Banded flash attention (bf16): rows t of q attend to keys max(0, t-w+1) .. t.
+// Banded flash attention (bf16). Query row r (0 <= r < nrows; q and o are indexed by r) sits at
+// position t_r = pos[r] if pos is set, else t_first + r, and attends to keys
+// max(0, t_r - w + 1) .. t_r of k / v, which are indexed by position (keys 0 .. nkeys - 1 exist;
+// every t_r must be below nkeys).
 struct BandParams {
   const void* q;
   idx_t q_sb, q_st, q_sh;
@@ -81,7 +93,8 @@ struct BandParams {
   idx_t k_sb, k_st, k_sh;
   void* o;
   idx_t o_sb, o_st, o_sh;
-  int B, T, Hq, Hkv, G, window;
+  const int32_t* pos;  // optional device row positions (nrows of them)
+  int B, nrows, nkeys, t_first, Hq, Hkv, G, window;
   float scale_log2;
 };
 
@@ -99,6 +112,8 @@ struct RowsF32Params {
   idx_t kn_sb, kn_sh;
   const int32_t* len;  // decode: row position = len[b]
   int64_t cap;         // decode: cache capacity (device lengths are clamped to it)
+  const int32_t* pos;  // optional row positions (row r at pos[r], clamped to [0, nkeys))
+  int64_t nkeys;       // with pos: keys available
   float* o;
   idx_t o_sb, o_st, o_sh;
   int B, Hq, Hkv, G, d, nrows, t0, window;

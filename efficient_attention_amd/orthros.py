@@ -16,8 +16,9 @@ import torch
 __all__ = [
     "OK", "E_INVALID", "E_UNSUPPORTED", "E_WORKSPACE", "E_CAPACITY", "E_LAUNCH",
     "STATUS_CACHE_FULL", "STAGES", "OrthrosError", "Shape", "Affine", "lib", "library_path",
-    "workspace_bytes", "make_workspace", "prefill", "decode_step", "forward_pt",
-    "read_device_status", "status_string", "timing_begin", "timing_end", "EXPORTED_SYMBOLS",
+    "workspace_bytes", "sft_workspace_bytes", "make_workspace", "prefill", "prefill_chunk",
+    "decode_step", "forward_pt", "forward_sft", "read_device_status", "status_string",
+    "timing_begin", "timing_end", "EXPORTED_SYMBOLS",
 ]
 
 OK, E_INVALID, E_UNSUPPORTED, E_WORKSPACE, E_CAPACITY, E_LAUNCH = 0, -1, -2, -3, -4, -5
@@ -25,7 +26,8 @@ STATUS_CACHE_FULL = 1
 F32, BF16 = 0, 1
 STAGES = ("cache_write", "band", "split_rows", "merge", "append", "rows_f32")
 EXPORTED_SYMBOLS = (
-    "orthros_workspace_bytes", "orthros_prefill", "orthros_decode_step", "orthros_forward_pt",
+    "orthros_workspace_bytes", "orthros_sft_workspace_bytes", "orthros_prefill",
+    "orthros_prefill_chunk", "orthros_decode_step", "orthros_forward_pt", "orthros_forward_sft",
     "orthros_read_device_status", "orthros_status_string", "orthros_timing_begin",
     "orthros_timing_end",
 )
@@ -76,6 +78,14 @@ def lib() -> ctypes.CDLL:
         L.orthros_decode_step.restype = ctypes.c_int
         L.orthros_forward_pt.argtypes = [sp, i64, vp, vp, vp, vp, ap, vp, vp, vp, vp, vp, vp, sz, vp]
         L.orthros_forward_pt.restype = ctypes.c_int
+        L.orthros_sft_workspace_bytes.argtypes = [sp, i64]
+        L.orthros_sft_workspace_bytes.restype = sz
+        L.orthros_forward_sft.argtypes = [sp, i64, vp, vp, vp, i64, vp, vp, ap, vp, vp, vp, vp,
+                                          vp, vp, sz, vp]
+        L.orthros_forward_sft.restype = ctypes.c_int
+        L.orthros_prefill_chunk.argtypes = [sp, i64, i64, vp, vp, vp, vp, ap, vp, vp, vp, vp, vp,
+                                            vp, sz, vp]
+        L.orthros_prefill_chunk.restype = ctypes.c_int
         L.orthros_read_device_status.argtypes = [vp, sz, ctypes.POINTER(i32), ctypes.c_int, vp]
         L.orthros_read_device_status.restype = ctypes.c_int
         L.orthros_status_string.argtypes = [ctypes.c_int]
@@ -153,9 +163,14 @@ def workspace_bytes(shape: Shape) -> int:
     return int(lib().orthros_workspace_bytes(ctypes.byref(shape.c())))
 
 
-def make_workspace(shape: Shape, device) -> torch.Tensor:
-    """A zero-filled workspace (the status word must start at 0)."""
-    n = workspace_bytes(shape)
+def sft_workspace_bytes(shape: Shape, R: int) -> int:
+    return int(lib().orthros_sft_workspace_bytes(ctypes.byref(shape.c()), int(R)))
+
+
+def make_workspace(shape: Shape, device, sft_rows: int = 0) -> torch.Tensor:
+    """A zero-filled workspace (the status word must start at 0); sft_rows > 0 sizes it for
+    orthros_forward_sft with that many response rows."""
+    n = sft_workspace_bytes(shape, sft_rows) if sft_rows > 0 else workspace_bytes(shape)
     if n == 0:
         raise OrthrosError(E_INVALID, "workspace_bytes")
     return torch.zeros(n, dtype=torch.uint8, device=device)
@@ -183,6 +198,30 @@ def prefill(shape: Shape, q_base, q_out, k, v, affine: Affine, cache_k, cache_v,
         cache_len.data_ptr(), o_base.data_ptr(), o_out.data_ptr(), workspace.data_ptr(),
         workspace.numel(), _stream(stream))
     _rc(rc, "orthros_prefill")
+
+
+def prefill_chunk(shape: Shape, past_len: int, q_base, q_out, k, v, affine: Affine, cache_k,
+                  cache_v, cache_len, o_base, o_out, workspace, stream=None):
+    """orthros_prefill_chunk: C more prompt tokens after past_len already cached ones."""
+    B, Hq, Hkv, d = shape.batch, shape.num_q_heads, shape.num_kv_heads, shape.head_dim
+    C = q_base.shape[1]
+    dev, dt = q_base.device, shape.dtype
+    _check(q_base, (B, C, Hq, d), dt, dev, "q_base")
+    _check(q_out, (B, 1, Hq, d), dt, dev, "q_out")
+    _check(k, (B, C, Hkv, d), dt, dev, "k")
+    _check(v, (B, C, Hkv, d), dt, dev, "v")
+    _check(cache_k, (B, Hkv, shape.capacity, d), dt, dev, "cache_k")
+    _check(cache_v, (B, Hkv, shape.capacity, d), dt, dev, "cache_v")
+    _check(cache_len, (B,), torch.int32, dev, "cache_len")
+    _check(o_base, (B, C, Hq, d), dt, dev, "o_base")
+    _check(o_out, (B, 1, Hq, d), dt, dev, "o_out")
+    aff = affine.c(Hq * d, dev)
+    rc = lib().orthros_prefill_chunk(
+        ctypes.byref(shape.c()), int(past_len), C, q_base.data_ptr(), q_out.data_ptr(),
+        k.data_ptr(), v.data_ptr(), ctypes.byref(aff), cache_k.data_ptr(), cache_v.data_ptr(),
+        cache_len.data_ptr(), o_base.data_ptr(), o_out.data_ptr(), workspace.data_ptr(),
+        workspace.numel(), _stream(stream))
+    _rc(rc, "orthros_prefill_chunk")
 
 
 def decode_step(shape: Shape, q_base, q_out, k_new, v_new, affine: Affine, cache_k, cache_v,
@@ -232,6 +271,34 @@ def forward_pt(shape: Shape, q_base, q_out, k, v, affine: Affine, o_base, o_out,
         v.data_ptr(), ctypes.byref(aff), ck or None, cv or None, cl or None, o_base.data_ptr(),
         o_out.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(stream))
     _rc(rc, "orthros_forward_pt")
+
+
+def forward_sft(shape: Shape, q_base, q_out, out_pos, k, v, affine: Affine, o_base, o_out,
+                workspace, cache_k=None, cache_v=None, cache_len=None, stream=None):
+    """orthros_forward_sft: base rows everywhere, output rows at the response positions."""
+    B, Hq, Hkv, d = shape.batch, shape.num_q_heads, shape.num_kv_heads, shape.head_dim
+    T, R = q_base.shape[1], q_out.shape[1]
+    dev, dt = q_base.device, shape.dtype
+    _check(q_base, (B, T, Hq, d), dt, dev, "q_base")
+    _check(q_out, (B, R, Hq, d), dt, dev, "q_out")
+    _check(out_pos, (R,), torch.int32, dev, "out_pos")
+    _check(k, (B, T, Hkv, d), dt, dev, "k")
+    _check(v, (B, T, Hkv, d), dt, dev, "v")
+    _check(o_base, (B, T, Hq, d), dt, dev, "o_base")
+    _check(o_out, (B, R, Hq, d), dt, dev, "o_out")
+    ck = cv = cl = 0
+    if cache_k is not None or cache_v is not None or cache_len is not None:
+        _check(cache_k, (B, Hkv, shape.capacity, d), dt, dev, "cache_k")
+        _check(cache_v, (B, Hkv, shape.capacity, d), dt, dev, "cache_v")
+        _check(cache_len, (B,), torch.int32, dev, "cache_len")
+        ck, cv, cl = cache_k.data_ptr(), cache_v.data_ptr(), cache_len.data_ptr()
+    aff = affine.c(Hq * d, dev)
+    rc = lib().orthros_forward_sft(
+        ctypes.byref(shape.c()), T, q_base.data_ptr(), q_out.data_ptr(), out_pos.data_ptr(), R,
+        k.data_ptr(), v.data_ptr(), ctypes.byref(aff), ck or None, cv or None, cl or None,
+        o_base.data_ptr(), o_out.data_ptr(), workspace.data_ptr(), workspace.numel(),
+        _stream(stream))
+    _rc(rc, "orthros_forward_sft")
 
 
 def read_device_status(workspace, clear: bool = False, stream=None) -> int:

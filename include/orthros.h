@@ -9,9 +9,11 @@
  *     output query q'_t = alpha' (.) q'_raw_t + beta', to every key 0 .. t; they never write
  *     keys or values.
  *   - Regimes (§3.2): pre-training duplicates every position (orthros_forward_pt);
+ *     supervised fine-tuning duplicates the response positions only (orthros_forward_sft);
  *     prefilling runs the base stream over the prompt and one output row at the last prompt
- *     token (orthros_prefill); decoding processes one new token per sequence as a base copy
- *     (cache append + window) and an output copy (full history) (orthros_decode_step).
+ *     token (orthros_prefill, or orthros_prefill_chunk for a prompt arriving in chunks);
+ *     decoding processes one new token per sequence as a base copy (cache append + window)
+ *     and an output copy (full history) (orthros_decode_step).
  * The key/value and query projections (x W_K, x W_V, x W_Q) and the output projection are the
  * caller's: the library starts from head-split projections (Algorithm 1, the split-heads step)
  * and returns the per-head outputs of the two attention calls, before the heads are merged.
@@ -142,6 +144,49 @@ int orthros_forward_pt(const orthros_shape* shape, int64_t T,
                        void* cache_k, void* cache_v, int32_t* cache_len,
                        void* o_base, void* o_out,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace orthros_forward_sft needs for R response rows per sequence (0 if the
+ * shape is invalid or R < 1); at least orthros_workspace_bytes(shape). */
+size_t orthros_sft_workspace_bytes(const orthros_shape* shape, int64_t R);
+
+/* Supervised fine-tuning regime (§3.2, T_in = T - T_out, T_out = R >= 1): base rows at every
+ * position, output rows only at the R response positions.
+ *   q_base   [B, T, H_q, d]   base-stream raw queries
+ *   q_out    [B, R, H_q, d]   raw queries of the duplicated response tokens, row r for position
+ *                             out_pos[r]
+ *   out_pos  int32 [R]        device array of positions in [0, T) (the same for every
+ *                             sequence; any order, sorted is fastest; values outside [0, T)
+ *                             are clamped into it)
+ *   k, v     [B, T, H_kv, d]
+ *   o_base   [B, T, H_q, d]   Eq. 4 at every position
+ *   o_out    [B, R, H_q, d]   Eq. 5 at position out_pos[r] (keys 0 .. out_pos[r])
+ *   cache_k/cache_v/cache_len: optional, as for orthros_forward_pt.
+ *   workspace: at least orthros_sft_workspace_bytes(shape, R) bytes. */
+int orthros_forward_sft(const orthros_shape* shape, int64_t T,
+                        const void* q_base, const void* q_out,
+                        const int32_t* out_pos, int64_t R,
+                        const void* k, const void* v,
+                        const orthros_affine* affine,
+                        void* cache_k, void* cache_v, int32_t* cache_len,
+                        void* o_base, void* o_out,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Prefilling regime (§3.2) for a prompt that arrives in chunks: the cache already holds
+ * past_len tokens of each sequence (cache_len[b] must equal past_len on entry) and C more are
+ * prefilled. The chunk's keys/values go to cache rows past_len .. past_len+C-1 and cache_len
+ * becomes past_len + C; the chunk's base rows attend over windows that reach back into the
+ * cached tokens, and the output row at the chunk's last token (position past_len + C - 1)
+ * attends over the whole cache. With past_len = 0 this is orthros_prefill.
+ *   q_base  [B, C, H_q, d]; q_out [B, 1, H_q, d]; k, v [B, C, H_kv, d]
+ *   o_base  [B, C, H_q, d]  Eq. 4 at positions past_len .. past_len+C-1
+ *   o_out   [B, 1, H_q, d]  Eq. 5 at position past_len + C - 1
+ * Requires past_len >= 0, C >= 1, past_len + C <= capacity. */
+int orthros_prefill_chunk(const orthros_shape* shape, int64_t past_len, int64_t C,
+                          const void* q_base, const void* q_out, const void* k, const void* v,
+                          const orthros_affine* affine,
+                          void* cache_k, void* cache_v, int32_t* cache_len,
+                          void* o_base, void* o_out,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Copies the workspace's sticky status word to *host_status (host pointer) after draining
  * `stream`; clears it on the device afterwards when `clear` is non-zero. Synchronous. */

@@ -18,6 +18,9 @@ Efficient Transformers":
     at the last prompt token) and Decoding (one new token, duplicated into a base copy that
     updates the cache and runs the window, and an output copy that attends to the history).
   * §3.2 SFT regime: output rows only at the response positions.
+  * §3.2 Prefilling with the prompt arriving in chunks: the chunk's base tokens append their
+    keys/values after the cached ones and run their windows over history plus chunk; one
+    output row at the chunk's last token sees every key.
 
 Readings where the pages are silent or garbled (all listed in the repository's design notes):
   * scale: the extracted equations lost the square root and the division; the scale is the
@@ -47,6 +50,7 @@ __all__ = [
     "decode_step",
     "forward_pt",
     "forward_sft",
+    "prefill_chunk",
 ]
 
 
@@ -229,3 +233,33 @@ def forward_sft(q_base, q_out, k, v, out_positions, alpha_b, beta_b, alpha_o, be
             o_out[b, r] = output_row(scale_offset(q_out[b, r], alpha_o, beta_o), k[b], v[b],
                                      int(t), s)
     return o_base, o_out
+
+
+def prefill_chunk(hist_k, hist_v, past_len, q_base, q_out, k, v, alpha_b, beta_b, alpha_o,
+                  beta_o, window, scale=None):
+    """§3.2 Prefilling for C more prompt tokens of sequences that already hold past_len.
+
+    hist_k, hist_v: [B, >=past_len, H_kv, d] cached history (rows 0 .. past_len-1 are used);
+    q_base [B, C, H_q, d]; q_out [B, 1, H_q, d] (the duplicated last token of the chunk);
+    k, v [B, C, H_kv, d]. The chunk's keys/values follow the history at positions
+    past_len .. past_len+C-1; base row i (position past_len + i) runs Eq. 4 over the joined
+    sequence, and the output row runs Eq. 5 at position past_len + C - 1.
+    Returns (o_base [B, C, H_q, d], o_out [B, 1, H_q, d], cache_k, cache_v, cache_len) with the
+    joined [B, past_len + C, H_kv, d] history.
+    """
+    k = _f64(k)
+    v = _f64(v)
+    B, C = k.shape[0], k.shape[1]
+    d = k.shape[-1]
+    s = default_scale(d) if scale is None else scale
+    Kj = np.concatenate([_f64(hist_k)[:, :past_len], k], axis=1)
+    Vj = np.concatenate([_f64(hist_v)[:, :past_len], v], axis=1)
+    o_base = np.empty(np.shape(q_base))
+    o_out = np.empty(np.shape(q_out))
+    for b in range(B):
+        for i in range(C):
+            o_base[b, i] = base_row(scale_offset(q_base[b, i], alpha_b, beta_b), Kj[b], Vj[b],
+                                    past_len + i, window, s)
+        o_out[b, 0] = output_row(scale_offset(q_out[b, 0], alpha_o, beta_o), Kj[b], Vj[b],
+                                 past_len + C - 1, s)
+    return o_base, o_out, Kj, Vj, np.full(B, past_len + C, dtype=np.int64)

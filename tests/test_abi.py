@@ -147,3 +147,70 @@ def test_status_strings():
 def test_read_status_rejects_null():
     out = ctypes.c_int32(0)
     assert ox.lib().orthros_read_device_status(None, 4096, ctypes.byref(out), 0, None) == ox.E_INVALID
+
+
+def test_sft_workspace_bytes():
+    L = ox.lib()
+    s = _shape()
+    base = L.orthros_workspace_bytes(ctypes.byref(s))
+    assert L.orthros_sft_workspace_bytes(ctypes.byref(s), 1) == base
+    # up to 16 response rows use split-key rows: one partial row per (head, response row)
+    assert L.orthros_sft_workspace_bytes(ctypes.byref(s), 16) > base
+    assert L.orthros_sft_workspace_bytes(ctypes.byref(s), 17) == base  # banded path: no partials
+    assert L.orthros_sft_workspace_bytes(ctypes.byref(s), 0) == 0
+    assert L.orthros_sft_workspace_bytes(ctypes.byref(_shape(head_dim=96)), 4) == 0
+
+
+def _sft(shape, T=64, R=4, ws_bytes=None, aff=None, **ptrs):
+    p = dict(q_base=FAKE, q_out=FAKE, pos=FAKE, k=FAKE, v=FAKE, cache_k=None, cache_v=None,
+             cache_len=None, o_base=FAKE, o_out=FAKE, ws=FAKE)
+    p.update(ptrs)
+    L = ox.lib()
+    wsb = L.orthros_sft_workspace_bytes(ctypes.byref(shape), max(R, 1)) if ws_bytes is None else ws_bytes
+    return L.orthros_forward_sft(ctypes.byref(shape), T, p["q_base"], p["q_out"], p["pos"], R,
+                                 p["k"], p["v"], ctypes.byref(aff or _aff()), p["cache_k"],
+                                 p["cache_v"], p["cache_len"], p["o_base"], p["o_out"], p["ws"],
+                                 wsb, None)
+
+
+@pytest.mark.parametrize("name", ["q_base", "q_out", "pos", "k", "v", "o_base", "o_out"])
+def test_sft_rejects_null_pointers(name):
+    assert _sft(_shape(), **{name: None}) == ox.E_INVALID
+
+
+def test_sft_rejects_bad_arguments():
+    assert _sft(_shape(), pos=FAKE + 2) == ox.E_INVALID        # positions must be int32-aligned
+    assert _sft(_shape(), R=0) == ox.E_INVALID
+    assert _sft(_shape(), T=0) == ox.E_INVALID
+    assert _sft(_shape(), R=8, ws_bytes=ox.lib().orthros_workspace_bytes(ctypes.byref(_shape()))) \
+        == ox.E_WORKSPACE                                        # 8 rows need the larger workspace
+    assert _sft(_shape(), cache_k=FAKE) == ox.E_INVALID          # cache is all-or-nothing
+    assert _sft(_shape(capacity=32), cache_k=FAKE, cache_v=FAKE, cache_len=FAKE) == ox.E_CAPACITY
+    assert _sft(_shape(head_dim=48)) == ox.E_UNSUPPORTED
+    assert _sft(_shape(), aff=_aff(alpha_out=None)) == ox.E_INVALID
+
+
+def _chunk(shape, past=100, C=64, ws_bytes=None, **ptrs):
+    p = dict(q_base=FAKE, q_out=FAKE, k=FAKE, v=FAKE, cache_k=FAKE, cache_v=FAKE, cache_len=FAKE,
+             o_base=FAKE, o_out=FAKE, ws=FAKE)
+    p.update(ptrs)
+    L = ox.lib()
+    wsb = L.orthros_workspace_bytes(ctypes.byref(shape)) if ws_bytes is None else ws_bytes
+    return L.orthros_prefill_chunk(ctypes.byref(shape), past, C, p["q_base"], p["q_out"], p["k"],
+                                   p["v"], ctypes.byref(_aff()), p["cache_k"], p["cache_v"],
+                                   p["cache_len"], p["o_base"], p["o_out"], p["ws"], wsb, None)
+
+
+@pytest.mark.parametrize("name", ["q_base", "q_out", "k", "v", "cache_k", "cache_v",
+                                  "cache_len", "o_base", "o_out"])
+def test_prefill_chunk_rejects_null_and_misaligned(name):
+    assert _chunk(_shape(), **{name: None}) == ox.E_INVALID
+    assert _chunk(_shape(), **{name: FAKE + 4}) == ox.E_INVALID
+
+
+def test_prefill_chunk_rejects_bad_lengths_and_workspace():
+    assert _chunk(_shape(), past=-1) == ox.E_INVALID
+    assert _chunk(_shape(), C=0) == ox.E_INVALID
+    assert _chunk(_shape(capacity=163), past=100, C=64) == ox.E_CAPACITY
+    assert _chunk(_shape(capacity=164), past=100, C=64, ws=None) == ox.E_WORKSPACE
+    assert _chunk(_shape(), ws_bytes=64) == ox.E_WORKSPACE

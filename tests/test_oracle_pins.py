@@ -285,3 +285,56 @@ def test_sampled_rows_match_full_evaluation():
     for t in [0, 6, 7, 29]:
         np.testing.assert_array_equal(part[0][:, t], full[0][:, t])
     assert np.isnan(part[0][:, 1]).all()
+
+
+@pytest.mark.parametrize("chunks,w", [([9, 7, 12], 5), ([1, 1, 30], 4), ([16, 16], 40), ([5], 3)])
+def test_chunked_prefill_equals_one_shot_prefill(chunks, w):
+    """§3.2 prefilling in pieces: each chunk's rows equal the one-shot prefill rows at the same
+    positions, and the last chunk's output row equals the one-shot output row."""
+    B, hq, hkv, d = 2, 4, 2, 8
+    P = sum(chunks)
+    qb, qo = _rand(B, P, hq, d), _rand(B, 1, hq, d)
+    k, v = _rand(B, P, hkv, d), _rand(B, P, hkv, d)
+    aff = _affine(hq, d)
+    ob, oo, ck, cv, ln = oracle.prefill(qb, qo, k, v, *aff, window=w)
+    hk, hv, past = np.zeros((B, 0, hkv, d)), np.zeros((B, 0, hkv, d)), 0
+    for i, c in enumerate(chunks):
+        sl = slice(past, past + c)
+        q_o = qo if i == len(chunks) - 1 else _rand(B, 1, hq, d)
+        cb, co, hk, hv, cl = oracle.prefill_chunk(hk, hv, past, qb[:, sl], q_o, k[:, sl], v[:, sl],
+                                                  *aff, window=w)
+        np.testing.assert_allclose(cb, ob[:, sl], atol=1e-13)
+        past += c
+        assert cl.tolist() == [past] * B
+    np.testing.assert_allclose(co, oo, atol=1e-13)
+    np.testing.assert_array_equal(hk, ck)
+    np.testing.assert_array_equal(hv, cv)
+
+
+def test_chunk_rows_match_sdpa_band_over_joined_sequence():
+    """Library routine: a chunk after cached history is a band-masked SDPA over the joined keys,
+    restricted to the chunk's query rows; its output row is the causal SDPA row at the end."""
+    past, C, hq, hkv, d, w = 13, 10, 4, 1, 16, 6
+    hk, hv = _rand(1, past, hkv, d), _rand(1, past, hkv, d)
+    qb, qo = _rand(1, C, hq, d), _rand(1, 1, hq, d)
+    k, v = _rand(1, C, hkv, d), _rand(1, C, hkv, d)
+    aff = _affine(hq, d)
+    cb, co, Kj, Vj, _ = oracle.prefill_chunk(hk, hv, past, qb, qo, k, v, *aff, window=w)
+    n = past + C
+    q_eff = aff[0].reshape(hq, d) * qb[0] + aff[1].reshape(hq, d)
+    t = np.arange(past, n)[:, None]
+    j = np.arange(n)[None, :]
+    band = (j <= t) & (j > t - w)
+    # SDPA with C query rows against n keys: pad the queries to n rows, take the chunk's rows
+    qpad = np.zeros((n, hq, d))
+    qpad[past:] = q_eff
+    mpad = np.ones((n, n), dtype=bool)
+    mpad[past:] = band
+    ref = _sdpa(qpad, np.concatenate([hk[0], k[0]]), np.concatenate([hv[0], v[0]]), mask=mpad,
+                gqa=True)[past:]
+    np.testing.assert_allclose(cb[0], ref, rtol=0, atol=1e-12)
+    qo_eff = aff[2].reshape(hq, d) * qo[0, 0] + aff[3].reshape(hq, d)
+    ref_o = _sdpa(qo_eff[None], np.concatenate([hk[0], k[0]]), np.concatenate([hv[0], v[0]]),
+                  gqa=True)[0]  # one query row sees every key 0 .. n-1
+    np.testing.assert_allclose(co[0, 0], ref_o, rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(Kj[0], np.concatenate([hk[0], k[0]]))
