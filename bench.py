@@ -13,11 +13,15 @@ The same JSON line carries:
   * decode: the 16 x 131072-token decode workload, 128 consecutive decode steps, as
     microseconds per step and the split-key kernel's algorithmic HBM bytes / launch time
     against 8 TB/s;
+  * prefill_chunked: the same prompt fed as 16 chunks of 8192 tokens (orthros_prefill_chunk);
+  * sft: the supervised fine-tuning regime at the 1.3B-like shape (batch 4, T 2048, 16 heads,
+    window 512) with output rows at the last 512 positions, and its banded kernels' share of
+    the bf16 peak;
   * cpu_baseline: the float64 oracle (test infrastructure) timed on this host on a bounded
     sample of the same prefill (base rows at seeded positions, all heads).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--skip-decode] [--skip-cpu]
-       [--copy-calibration]
+       [--skip-regimes] [--copy-calibration]
 """
 from __future__ import annotations
 
@@ -178,6 +182,71 @@ def bench_decode(wl, warmup, dev):
                 split_s=split_s)
 
 
+def bench_sft(wl, R, steps, warmup, dev):
+    """SFT regime: base rows at every position, output rows at the last R positions."""
+    inp = syn.make_sft(wl, list(range(wl.length - R, wl.length)), device=dev)
+    B, T, Hq, d = inp["q_base"].shape
+    Hkv = inp["k"].shape[2]
+    shape = ox.Shape(B, Hq, Hkv, d, wl.window, torch.bfloat16, T)
+    aff = ox.Affine(*inp["affine"])
+    pos = torch.arange(T - R, T, dtype=torch.int32, device=dev)
+    ob = torch.empty(B, T, Hq, d, dtype=torch.bfloat16, device=dev)
+    oo = torch.empty(B, R, Hq, d, dtype=torch.bfloat16, device=dev)
+    ws = ox.make_workspace(shape, dev, sft_rows=R)
+
+    def step():
+        ox.forward_sft(shape, inp["q_base"], inp["q_out"], pos, inp["k"], inp["v"], aff, ob, oo, ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ox.timing_begin()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    stages = ox.timing_end()
+    flops = 4.0 * d * Hq * B * (swa_pairs(T, wl.window) + sum(t + 1 for t in range(T - R, T)))
+    band_ms, band_n = stages["band"]
+    log(f"sft {wl.name} R={R}: {ms:.3f} ms/step; stages {stages}")
+    return dict(ms=ms, flops=flops, band_ms=band_ms / max(steps, 1))
+
+
+def bench_prefill_chunked(wl, chunk, steps, warmup, dev, inp):
+    """The same prompt prefilled in chunks of `chunk` tokens (cache grows chunk by chunk)."""
+    B, P, Hq, d = inp["q_base"].shape
+    Hkv = inp["k"].shape[2]
+    shape = ox.Shape(B, Hq, Hkv, d, wl.window, torch.bfloat16, P)
+    aff = ox.Affine(*inp["affine"])
+    ck = torch.empty(B, Hkv, P, d, dtype=torch.bfloat16, device=dev)
+    cv = torch.empty_like(ck)
+    cl = torch.zeros(B, dtype=torch.int32, device=dev)
+    ws = ox.make_workspace(shape, dev)
+    starts = list(range(0, P, chunk))
+    views = [(s0, inp["q_base"][:, s0:s0 + chunk].contiguous(), inp["k"][:, s0:s0 + chunk].contiguous(),
+              inp["v"][:, s0:s0 + chunk].contiguous()) for s0 in starts]
+    obs = [torch.empty(B, q.shape[1], Hq, d, dtype=torch.bfloat16, device=dev) for _, q, _, _ in views]
+    oo = torch.empty(B, 1, Hq, d, dtype=torch.bfloat16, device=dev)
+
+    def step():
+        for (s0, q, k, v), ob in zip(views, obs):
+            ox.prefill_chunk(shape, s0, q, inp["q_out"], k, v, aff, ck, cv, cl, ob, oo, ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ox.timing_begin()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    stages = ox.timing_end()
+    log(f"prefill in {len(starts)} chunks of {chunk}: {ms:.3f} ms/step; stages {stages}")
+    return dict(ms=ms, chunks=len(starts), band_ms=stages["band"][0] / max(steps, 1))
+
+
 def cpu_baseline(inp, wl, budget_s=12.0):
     """The float64 oracle on host cores: base rows at seeded positions (all heads)."""
     import oracle
@@ -219,6 +288,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--skip-cpu", action="store_true")
+    ap.add_argument("--skip-regimes", action="store_true",
+                    help="skip the SFT and chunked-prefill measurements")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a 1 GiB device copy (reference for HBM byte counters)")
     ap.add_argument("--workload", default="prefill_8b_128k",
@@ -287,6 +358,24 @@ def main():
                          "bytes_per_launch": dc["split_bytes"]},
             "stage_us_per_step": {k: round(v[0] * 1e3 / dw.steps, 2)
                                   for k, v in dc["stages"].items() if v[1]},
+        }
+    if not args.skip_regimes:
+        ch = bench_prefill_chunked(wl, 8192, max(2, args.steps // 3), 1, dev, pf["inp"])
+        rec["prefill_chunked"] = {
+            "workload": f"{wl.name} in chunks of 8192", "chunks": ch["chunks"],
+            "ms_per_step": round(ch["ms"], 4), "tokens_per_s": round(tokens / (ch["ms"] / 1e3), 1),
+            "band_frac": round(base_flops / (ch["band_ms"] / 1e3) / PEAK_BF16_FLOPS, 4),
+        }
+        sw = syn.WORKLOADS["pt_1p3b_2k"]
+        sf = bench_sft(sw, 512, args.steps, args.warmup, dev)
+        rec["sft"] = {
+            "workload": f"{sw.name}, response rows at the last 512 positions",
+            "ms_per_step": round(sf["ms"], 4),
+            "tokens_per_s": round(sw.batch * sw.length / (sf["ms"] / 1e3), 1),
+            "roofline": {"bound": "mfma", "achieved": round(sf["flops"] / (sf["band_ms"] / 1e3) / 1e12, 2),
+                         "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
+                         "frac": round(sf["flops"] / (sf["band_ms"] / 1e3) / PEAK_BF16_FLOPS, 4),
+                         "kernel": "band_kernel (both launches)"},
         }
     if not args.skip_cpu:
         rec["cpu_baseline"] = cpu_baseline(pf["inp"], wl)
