@@ -22,6 +22,12 @@ namespace orthros {
 namespace {
 constexpr int kTK = 64;      // keys per tile
 constexpr int kRows = 16;    // query rows per work-group (MFMA N)
+// Probabilities are exp2(score - m) with a per-row reference m that moves only when it must
+// (fp32 and bf16 share their exponent range, so values up to 2^64 lose nothing): when a lane's
+// probabilities could exceed 2^64, or at the row's first keys if their maximum lies outside
+// +-kSafeScore (otherwise m stays 0).
+constexpr float kLazyBound = 18446744073709551616.f;  // 2^64
+constexpr float kSafeScore = 64.f;
 
 template <int D>
 struct SplitSmem {
@@ -108,7 +114,11 @@ __global__ __launch_bounds__(256) void split_rows_kernel(SplitParams p) {
   }
 
   // Query fragment (B operand of mfma 16x16x32): lane (j, kg) holds channels 32*st + 8*kg + e.
-  bf16x8 qf[NST];
+  // The fp32 query is carried as a bf16 pair hi + lo (lo = the rounding residue of hi), and so
+  // are the probabilities below: two MFMAs per product keep both near fp32 accuracy, which long
+  // rows need (a bf16 query and bf16 probabilities alone leave a relative error of order 3e-3
+  // on a 128K-key row). The kernel is bound by memory traffic, so the extra MFMAs are free.
+  bf16x8 qf[NST], qf_lo[NST];
   {
     const uint16_t* qsrc = nullptr;
     const float *al = nullptr, *be = nullptr;
@@ -127,15 +137,17 @@ __global__ __launch_bounds__(256) void split_rows_kernel(SplitParams p) {
       const int c0 = 32 * st + 8 * kg;
       u32x4 raw = {0u, 0u, 0u, 0u};
       if (qsrc) raw = *reinterpret_cast<const u32x4*>(qsrc + c0);
-      bf16x8 f;
+      bf16x8 f, flo;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const uint32_t w = raw[e >> 1];
         const float x = (e & 1) ? bf16_hi(w) : bf16_lo(w);
         const float y = qsrc ? (al[c0 + e] * x + be[c0 + e]) * p.scale_log2 : 0.f;
         f[e] = (__bf16)y;
+        flo[e] = (__bf16)(y - (float)f[e]);
       }
       qf[st] = f;
+      qf_lo[st] = flo;
     }
   }
 
@@ -156,7 +168,8 @@ __global__ __launch_bounds__(256) void split_rows_kernel(SplitParams p) {
   f32x4 O[NMT];
 #pragma unroll
   for (int mt = 0; mt < NMT; ++mt) O[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = kNegInf, l = 0.f;
+  float mref = 0.f, l = 0.f;
+  bool seen = false;  // the row met a key of its range in this wavefront's share
 
   if (kb < ke) {
     u32x4 kreg[KCH], vreg[VIT][2];
@@ -212,36 +225,56 @@ __global__ __launch_bounds__(256) void split_rows_kernel(SplitParams p) {
         for (int st = 0; st < NST; ++st) {
           const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + (16 * wv + j) * KSTR + 32 * st + 8 * kg);
           acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[st], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf_lo[st], acc, 0, 0, 0);
         }
         float sc[4];
-        float mx = kNegInf;
+        bool anykey = false;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int64_t key = wk0 + 4 * kg + r;
           const bool ok = key < ke && key >= lo && key <= hi;
           sc[r] = ok ? acc[r] : kNegInf;
-          mx = fmaxf(mx, sc[r]);
+          anykey = anykey || ok;
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float mn = fmaxf(m, mx);
-        const float alpha = mn == kNegInf ? 1.f : fast_exp2(m - mn);
-        const float ms = mn == kNegInf ? 0.f : mn;
-        float ps = 0.f;
-        s16x4 pb;
+        float ps;
+        s16x4 pb, pb_lo;
+        auto probs = [&]() {
+          ps = 0.f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float pr = fast_exp2(sc[r] - ms);
-          ps += pr;
-          pb[r] = (short)f32_to_bf16(pr);
+          for (int r = 0; r < 4; ++r) {
+            const float pr = fast_exp2(sc[r] - mref);
+            ps += pr;
+            const uint16_t hb = f32_to_bf16(pr);
+            pb[r] = (short)hb;
+            pb_lo[r] = (short)f32_to_bf16(pr - bf16_to_f32(hb));
+          }
+        };
+        probs();
+        const bool need = !(ps <= kLazyBound) || (!seen && anykey);
+        if (__builtin_amdgcn_ballot_w64(need)) {  // rare: move the reference of some rows
+          int nrow = need ? 1 : 0;  // the 4 lanes of a row decide together
+          nrow |= __shfl_xor(nrow, 16, 64);
+          nrow |= __shfl_xor(nrow, 32, 64);
+          float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+          mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+          mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+          const bool move = nrow && mx != kNegInf;
+          const bool keep0 = !seen && mx > -kSafeScore && mx < kSafeScore;
+          const float nref = move ? (keep0 ? 0.f : mx) : mref;
+          const float alpha = seen ? fast_exp2(mref - nref) : 0.f;  // unseen rows hold zeros
+          seen = seen || move;
+          mref = nref;
+          l *= alpha;
+#pragma unroll
+          for (int mt = 0; mt < NMT; ++mt) O[mt] *= alpha;
+          probs();
         }
-        l = l * alpha + ps;
-        m = mn;
+        l += ps;
 #pragma unroll
         for (int mt = 0; mt < NMT; ++mt) {
-          O[mt] *= alpha;
           const s16x4 a = *reinterpret_cast<const s16x4*>(vt + (16 * mt + j) * VSTR + 16 * wv + 4 * kg);
           O[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb, O[mt], 0, 0, 0);
+          O[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb_lo, O[mt], 0, 0, 0);
         }
       }
       buf ^= 1;
@@ -258,7 +291,7 @@ __global__ __launch_bounds__(256) void split_rows_kernel(SplitParams p) {
   constexpr int RW = kRows * (D + 2);
   float* rw = red + wv * RW;
   if (kg == 0) {
-    rw[j] = m;
+    rw[j] = seen ? mref : kNegInf;  // reference of this wavefront's share (-inf: no key)
     rw[kRows + j] = l;
   }
 #pragma unroll

@@ -32,10 +32,13 @@
  *     always fp32 [num_q_heads * head_dim] (one entry per query head and channel).
  *   - Grouped queries: query head h reads kv head h / (num_q_heads / num_kv_heads).
  *   - Every pointer must be 16-byte aligned. Outputs must not alias inputs.
- *   - bf16 arithmetic: scale-offset in fp32, the query rounded once to bf16 for the matrix
- *     cores, scores and softmax in fp32, probabilities rounded once to bf16 for the value
- *     product, fp32 accumulation, output rounded once to bf16 (round to nearest even).
- *     fp32 calls compute every step in fp32.
+ *   - bf16 arithmetic: scale-offset in fp32, scores and softmax in fp32, fp32 accumulation,
+ *     output rounded once to bf16 (round to nearest even). The query enters the matrix cores
+ *     and the probabilities enter the value product as bf16: rounded once for the windowed
+ *     and pre-training rows (a few thousand keys), carried as a bf16 pair (value + rounding
+ *     residue, two products) for the split-key rows (decode, the output rows of prefill and of
+ *     short SFT responses), whose 100K-key rows would otherwise accumulate a relative error of
+ *     order 3e-3. fp32 calls compute every step in fp32.
  *   - Return value: ORTHROS_OK (0) or a negative ORTHROS_E_* code. Arguments are validated
  *     before anything is enqueued, so a call that returns an argument error has no effect.
  */
