@@ -51,7 +51,7 @@ CSRC = os.path.join(ROOT, "efficient_attention_amd", "csrc")
 # figure no longer describes the kernel and `traffic` is reported as null.
 TRAFFIC = {
     "band_kernel": {"sha": "06973e7d56491b46", "bytes_per_launch": 2.7852e+09},
-    "split_rows_kernel": {"sha": "7ae92e118e6335d5", "bytes_per_launch": 8.5975e+09},
+    "split_rows_kernel": {"sha": "e085bb09a032e91f", "bytes_per_launch": 8.5975e+09},
 }
 
 
