@@ -21,6 +21,9 @@ Efficient Transformers":
   * §3.2 Prefilling with the prompt arriving in chunks: the chunk's base tokens append their
     keys/values after the cached ones and run their windows over history plus chunk; one
     output row at the chunk's last token sees every key.
+  * §3.2 Decoding over a paged cache (the batched serving setting §5 names as future work):
+    the same decode step, with each sequence's history stored in fixed-size pages of a shared
+    pool and found through a per-sequence table of page indices.
 
 Readings where the pages are silent or garbled (all listed in the repository's design notes):
   * scale: the extracted equations lost the square root and the division; the scale is the
@@ -51,6 +54,9 @@ __all__ = [
     "forward_pt",
     "forward_sft",
     "prefill_chunk",
+    "gather_pages",
+    "paged_write",
+    "decode_step_paged",
 ]
 
 
@@ -263,3 +269,70 @@ def prefill_chunk(hist_k, hist_v, past_len, q_base, q_out, k, v, alpha_b, beta_b
         o_out[b, 0] = output_row(scale_offset(q_out[b, 0], alpha_o, beta_o), Kj[b], Vj[b],
                                  past_len + C - 1, s)
     return o_base, o_out, Kj, Vj, np.full(B, past_len + C, dtype=np.int64)
+
+
+def gather_pages(pages, table_row, length) -> np.ndarray:
+    """History of one sequence read out of a paged cache, as [length, H_kv, d] float64.
+
+    pages: [num_pages, H_kv, page_size, d] pool; table_row: page index of each logical block
+    of the sequence. Token t sits in page table_row[t // page_size] at slot t % page_size.
+    """
+    pages = np.asarray(pages)
+    ps = pages.shape[2]
+    rows = []
+    for t in range(int(length)):
+        rows.append(_f64(pages[int(table_row[t // ps]), :, t % ps, :]))
+    if not rows:
+        return np.zeros((0, pages.shape[1], pages.shape[3]))
+    return np.stack(rows)
+
+
+def paged_write(k_pages, v_pages, table, cache_len, k, v):
+    """Append T tokens per sequence to a paged cache (prefilling or decoding into pages).
+
+    k_pages, v_pages [num_pages, H_kv, page_size, d]; table [B, max_pages]; cache_len [B];
+    k, v [B, T, H_kv, d]. Tokens go to positions cache_len[b] .. cache_len[b] + T - 1. A
+    sequence without room for all T tokens (capacity max_pages * page_size) is left unchanged
+    and reported as full. Returns (new k_pages, new v_pages, new lengths, full flags) as
+    float64 copies; the inputs are not modified.
+    """
+    kp = _f64(k_pages).copy()
+    vp = _f64(v_pages).copy()
+    k = _f64(k)
+    v = _f64(v)
+    B, T = k.shape[0], k.shape[1]
+    ps = kp.shape[2]
+    cap = np.shape(table)[1] * ps
+    lens = np.asarray(cache_len, dtype=np.int64).copy()
+    full = np.zeros(B, dtype=bool)
+    for b in range(B):
+        L = int(lens[b])
+        if L < 0 or L + T > cap:
+            full[b] = True
+            continue
+        for i in range(T):
+            t = L + i
+            page = int(table[b][t // ps])
+            kp[page, :, t % ps, :] = k[b, i]
+            vp[page, :, t % ps, :] = v[b, i]
+        lens[b] = L + T
+    return kp, vp, lens, full
+
+
+def decode_step_paged(k_pages, v_pages, table, cache_len, q_base, q_out, k_new, v_new,
+                      alpha_b, beta_b, alpha_o, beta_o, window, scale=None):
+    """§3.2 Decoding with the history in a paged cache.
+
+    The attention outputs are those of ``decode_step`` over each sequence's gathered history
+    (the new key L is this step's k_new, v_new); the new token is then written to position L
+    through the table (nothing is written for a full sequence).
+    Returns (o_base, o_out, new k_pages, new v_pages, new lengths, full flags).
+    """
+    B = len(cache_len)
+    hk = [gather_pages(k_pages, table[b], cache_len[b]) for b in range(B)]
+    hv = [gather_pages(v_pages, table[b], cache_len[b]) for b in range(B)]
+    o_base, o_out, _, _, _ = decode_step(hk, hv, cache_len, q_base, q_out, k_new, v_new,
+                                         alpha_b, beta_b, alpha_o, beta_o, window, scale)
+    kp, vp, lens, full = paged_write(k_pages, v_pages, table, cache_len,
+                                     _f64(k_new)[:, None], _f64(v_new)[:, None])
+    return o_base, o_out, kp, vp, lens, full

@@ -338,3 +338,77 @@ def test_chunk_rows_match_sdpa_band_over_joined_sequence():
                   gqa=True)[0]  # one query row sees every key 0 .. n-1
     np.testing.assert_allclose(co[0, 0], ref_o, rtol=0, atol=1e-12)
     np.testing.assert_array_equal(Kj[0], np.concatenate([hk[0], k[0]]))
+
+
+def _scatter_blocks(hist, table, pool_pages, ps):
+    """Test-side construction of a paged pool: block i of the history (tokens i ps .. i ps +
+    ps - 1, as a [H_kv, ps, d] slab) is copied whole into page table[i]. Written per block with
+    slicing, independently of the oracle's per-token gather."""
+    pool = np.asarray(pool_pages).copy()
+    L = hist.shape[0]
+    for i in range((L + ps - 1) // ps):
+        blk = hist[i * ps:(i + 1) * ps]            # [n, H_kv, d]
+        pool[table[i], :, :blk.shape[0], :] = np.transpose(blk, (1, 0, 2))
+    return pool
+
+
+@pytest.mark.parametrize("ps,lengths", [(1, [5, 9]), (4, [13, 8, 1]), (16, [40, 0]),
+                                        (64, [30, 64])])
+def test_gather_pages_inverts_a_block_scatter(ps, lengths):
+    Hkv, d = 2, 8
+    max_pages = max((L + ps - 1) // ps for L in lengths) + 1
+    num_pages = len(lengths) * max_pages + 3
+    perm = RNG.permutation(num_pages)
+    table = perm[:len(lengths) * max_pages].reshape(len(lengths), max_pages)
+    pool = RNG.standard_normal((num_pages, Hkv, ps, d))
+    for b, L in enumerate(lengths):
+        hist = RNG.standard_normal((L, Hkv, d))
+        pooled = _scatter_blocks(hist, table[b], pool, ps)
+        np.testing.assert_array_equal(oracle.gather_pages(pooled, table[b], L), hist)
+        # pages outside this sequence's blocks are untouched by the scatter
+        used = set(table[b][:(L + ps - 1) // ps].tolist())
+        for pg in range(num_pages):
+            if pg not in used:
+                np.testing.assert_array_equal(pooled[pg], pool[pg])
+
+
+@pytest.mark.parametrize("ps", [1, 8, 32])
+def test_paged_decode_equals_contiguous_decode(ps):
+    """Same outputs as decode_step over the gathered histories; the new token lands in exactly
+    one slot per sequence (read back through the table); a full sequence writes nothing."""
+    B, Hq, Hkv, d, w = 3, 4, 2, 8, 5
+    max_pages = 40 // ps + 2
+    cap = max_pages * ps
+    lengths = [7, 33, cap]  # the last sequence is full
+    num_pages = B * max_pages + 2
+    table = RNG.permutation(num_pages)[:B * max_pages].reshape(B, max_pages)
+    kp = RNG.standard_normal((num_pages, Hkv, ps, d))
+    vp = RNG.standard_normal((num_pages, Hkv, ps, d))
+    hk = [RNG.standard_normal((L, Hkv, d)) for L in lengths]
+    hv = [RNG.standard_normal((L, Hkv, d)) for L in lengths]
+    for b in range(B):
+        kp = _scatter_blocks(hk[b], table[b], kp, ps)
+        vp = _scatter_blocks(hv[b], table[b], vp, ps)
+    qb = RNG.standard_normal((B, Hq, d))
+    qo = RNG.standard_normal((B, Hq, d))
+    kn = RNG.standard_normal((B, Hkv, d))
+    vn = RNG.standard_normal((B, Hkv, d))
+    aff = [1 + 0.1 * RNG.standard_normal(Hq * d), 0.1 * RNG.standard_normal(Hq * d),
+           1 + 0.1 * RNG.standard_normal(Hq * d), 0.1 * RNG.standard_normal(Hq * d)]
+    ob, oo, kp2, vp2, lens, full = oracle.decode_step_paged(kp, vp, table, np.array(lengths),
+                                                            qb, qo, kn, vn, *aff, window=w)
+    rb, ro, _, _, _ = oracle.decode_step(hk, hv, np.array(lengths), qb, qo, kn, vn, *aff,
+                                         window=w)
+    np.testing.assert_array_equal(ob, rb)
+    np.testing.assert_array_equal(oo, ro)
+    assert lens.tolist() == [lengths[0] + 1, lengths[1] + 1, lengths[2]]
+    assert full.tolist() == [False, False, True]
+    for b in range(2):
+        L = lengths[b]
+        np.testing.assert_array_equal(oracle.gather_pages(kp2, table[b], L + 1),
+                                      np.concatenate([hk[b], kn[b][None]]))
+        np.testing.assert_array_equal(oracle.gather_pages(vp2, table[b], L + 1),
+                                      np.concatenate([hv[b], vn[b][None]]))
+    changed = np.argwhere(kp2 != kp)
+    assert len({(int(c[0]), int(c[2])) for c in changed}) == 2  # one (page, slot) per written seq
+    np.testing.assert_array_equal(kp2[table[2]], kp[table[2]])
