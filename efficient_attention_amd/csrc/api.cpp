@@ -130,6 +130,103 @@ int heads_per_chunk(int G, bool with_base) {
   return G < cap ? G : cap;
 }
 
+// Paged cache arguments -> kernel view. Page indices are int32, the page size a power of two,
+// and the per-sequence capacity (max_pages pages) must be the shape's capacity.
+int check_paged(const orthros_shape* s, const orthros_paged_kv* c, void* ws, PagedKV* out) {
+  if (!c) return ORTHROS_E_INVALID;
+  if (check_ptrs({c->k_pages, c->v_pages, c->block_table})) return ORTHROS_E_INVALID;
+  if (c->num_pages < 1 || c->num_pages > INT32_MAX || c->max_pages < 1) return ORTHROS_E_INVALID;
+  if (c->page_size < 1 || c->page_size > (1 << 24) || (c->page_size & (c->page_size - 1)))
+    return ORTHROS_E_INVALID;
+  if ((int64_t)c->max_pages * c->page_size != s->capacity) return ORTHROS_E_INVALID;
+  int lg = 0;
+  while ((1 << lg) < c->page_size) ++lg;
+  out->table = c->block_table;
+  out->tbl_sb = c->max_pages;
+  out->num_pages = c->num_pages;
+  out->k_sh = (idx_t)c->page_size * s->head_dim;
+  out->k_sp = out->k_sh * s->num_kv_heads;
+  out->ps_log2 = lg;
+  out->status = reinterpret_cast<int32_t*>(ws);
+  return ORTHROS_OK;
+}
+
+// One decode step over a contiguous cache (pg.table == nullptr) or a paged pool.
+int decode_common(const orthros_shape* s, const void* q_base, const void* q_out,
+                  const void* k_new, const void* v_new, const orthros_affine* aff,
+                  void* cache_k, void* cache_v, const PagedKV& pg, int32_t* cache_len,
+                  int64_t max_len_hint, void* o_base, void* o_out, void* ws, size_t ws_bytes,
+                  hipStream_t st) {
+  int rc;
+  if (max_len_hint < 0) return ORTHROS_E_INVALID;
+  if ((rc = check_affine(aff))) return rc;
+  if ((rc = check_ptrs({q_base, q_out, k_new, v_new, cache_len, o_base, o_out}))) return rc;
+  if ((rc = check_ws(s, ws, ws_bytes))) return rc;
+
+  const int B = s->batch, Hq = s->num_q_heads, Hkv = s->num_kv_heads, d = s->head_dim;
+  const int G = Hq / Hkv;
+  const float scale = scale_of(s);
+  const WsLayout L = ws_layout(s);
+  char* wsc = static_cast<char*>(ws);
+  int64_t hint = max_len_hint < s->capacity ? max_len_hint : s->capacity;
+
+  if (s->dtype == ORTHROS_F32) {
+    RowsF32Params r{};
+    r.q = static_cast<const float*>(q_base);
+    r.q_sb = (idx_t)Hq * d; r.q_st = 0; r.q_sh = d;
+    r.alpha = aff->alpha_base; r.beta = aff->beta_base;
+    r.k = static_cast<const float*>(cache_k); r.v = static_cast<const float*>(cache_v);
+    r.k_sb = (idx_t)Hkv * s->capacity * d; r.k_st = d; r.k_sh = s->capacity * d;
+    r.pg = pg;
+    r.knew = static_cast<const float*>(k_new); r.vnew = static_cast<const float*>(v_new);
+    r.kn_sb = (idx_t)Hkv * d; r.kn_sh = d;
+    r.len = cache_len; r.cap = s->capacity;
+    r.o = static_cast<float*>(o_base); r.o_sb = (idx_t)Hq * d; r.o_st = 0; r.o_sh = d;
+    r.B = B; r.Hq = Hq; r.Hkv = Hkv; r.G = G; r.d = d; r.nrows = 1; r.t0 = 0;
+    r.window = s->window; r.scale = scale;
+    rc = launch_rc(run_stage(ORTHROS_STAGE_ROWS_F32, st, [&] { return launch_rows_f32(r, st); }));
+    if (rc) return rc;
+    RowsF32Params o = r;
+    o.q = static_cast<const float*>(q_out);
+    o.alpha = aff->alpha_out; o.beta = aff->beta_out;
+    o.o = static_cast<float*>(o_out);
+    o.window = INT_MAX;
+    rc = launch_rc(run_stage(ORTHROS_STAGE_ROWS_F32, st, [&] { return launch_rows_f32(o, st); }));
+    if (rc) return rc;
+  } else {
+    SplitParams sp{};
+    sp.q_out = q_out; sp.q_base = q_base; sp.q_sb = (idx_t)Hq * d; sp.q_sh = d;
+    sp.a_out = aff->alpha_out; sp.b_out = aff->beta_out;
+    sp.a_base = aff->alpha_base; sp.b_base = aff->beta_base;
+    sp.k = cache_k; sp.v = cache_v;
+    sp.k_sb = (idx_t)Hkv * s->capacity * d; sp.k_sh = s->capacity * d; sp.k_st = d;
+    sp.pg = pg;
+    sp.knew = k_new; sp.vnew = v_new; sp.kn_sb = (idx_t)Hkv * d; sp.kn_sh = d;
+    sp.len = cache_len; sp.cap = s->capacity;
+    sp.B = B; sp.Hq = Hq; sp.Hkv = Hkv; sp.G = G;
+    sp.HC = heads_per_chunk(G, true);
+    sp.nchunks = (G + sp.HC - 1) / sp.HC;
+    sp.window = s->window; sp.with_base = 1;
+    sp.nsplit = nsplit_for(hint + 1, (int64_t)B * Hkv * sp.nchunks);
+    sp.scale_log2 = scale * kLog2e;
+    sp.pm = reinterpret_cast<float*>(wsc + L.pm);
+    sp.pl = reinterpret_cast<float*>(wsc + L.pl);
+    sp.po = reinterpret_cast<float*>(wsc + L.po);
+    rc = launch_rc(run_stage(ORTHROS_STAGE_SPLIT_ROWS, st, [&] { return launch_split_rows(sp, d, st); }));
+    if (rc) return rc;
+    MergeParams mp{};
+    mp.pm = sp.pm; mp.pl = sp.pl; mp.po = sp.po;
+    mp.out0 = o_out; mp.o_sb0 = (idx_t)Hq * d; mp.o_sh0 = d;
+    mp.out1 = o_base; mp.o_sb1 = (idx_t)Hq * d; mp.o_sh1 = d;
+    mp.rows = B * Hq * 2; mp.nsplit = sp.nsplit; mp.d = d; mp.Hq = Hq; mp.nstreams = 2; mp.bf16 = 1;
+    rc = launch_rc(run_stage(ORTHROS_STAGE_MERGE, st, [&] { return launch_merge(mp, st); }));
+    if (rc) return rc;
+  }
+  AppendParams ap{k_new, v_new, cache_k, cache_v, cache_len,
+                  reinterpret_cast<int32_t*>(wsc), B, Hkv, d, esize(s), s->capacity, pg};
+  return launch_rc(run_stage(ORTHROS_STAGE_APPEND, st, [&] { return launch_append(ap, st); }));
+}
+
 }  // namespace
 
 extern "C" {
@@ -246,71 +343,38 @@ int orthros_decode_step(const orthros_shape* s, const void* q_base, const void* 
                         void* o_base, void* o_out, void* ws, size_t ws_bytes, hipStream_t st) {
   int rc = check_shape(s);
   if (rc) return rc;
-  if (max_len_hint < 0) return ORTHROS_E_INVALID;
-  if ((rc = check_affine(aff))) return rc;
-  if ((rc = check_ptrs({q_base, q_out, k_new, v_new, cache_k, cache_v, cache_len, o_base, o_out}))) return rc;
+  if ((rc = check_ptrs({cache_k, cache_v}))) return rc;
+  return decode_common(s, q_base, q_out, k_new, v_new, aff, cache_k, cache_v, PagedKV{},
+                       cache_len, max_len_hint, o_base, o_out, ws, ws_bytes, st);
+}
+
+int orthros_decode_step_paged(const orthros_shape* s, const void* q_base, const void* q_out,
+                              const void* k_new, const void* v_new, const orthros_affine* aff,
+                              const orthros_paged_kv* cache, int32_t* cache_len,
+                              int64_t max_len_hint, void* o_base, void* o_out, void* ws,
+                              size_t ws_bytes, hipStream_t st) {
+  int rc = check_shape(s);
+  if (rc) return rc;
   if ((rc = check_ws(s, ws, ws_bytes))) return rc;
+  PagedKV pg{};
+  if ((rc = check_paged(s, cache, ws, &pg))) return rc;
+  return decode_common(s, q_base, q_out, k_new, v_new, aff, cache->k_pages, cache->v_pages, pg,
+                       cache_len, max_len_hint, o_base, o_out, ws, ws_bytes, st);
+}
 
-  const int B = s->batch, Hq = s->num_q_heads, Hkv = s->num_kv_heads, d = s->head_dim;
-  const int G = Hq / Hkv;
-  const float scale = scale_of(s);
-  const WsLayout L = ws_layout(s);
-  char* wsc = static_cast<char*>(ws);
-  int64_t hint = max_len_hint < s->capacity ? max_len_hint : s->capacity;
-
-  if (s->dtype == ORTHROS_F32) {
-    RowsF32Params r{};
-    r.q = static_cast<const float*>(q_base);
-    r.q_sb = (idx_t)Hq * d; r.q_st = 0; r.q_sh = d;
-    r.alpha = aff->alpha_base; r.beta = aff->beta_base;
-    r.k = static_cast<const float*>(cache_k); r.v = static_cast<const float*>(cache_v);
-    r.k_sb = (idx_t)Hkv * s->capacity * d; r.k_st = d; r.k_sh = s->capacity * d;
-    r.knew = static_cast<const float*>(k_new); r.vnew = static_cast<const float*>(v_new);
-    r.kn_sb = (idx_t)Hkv * d; r.kn_sh = d;
-    r.len = cache_len; r.cap = s->capacity;
-    r.o = static_cast<float*>(o_base); r.o_sb = (idx_t)Hq * d; r.o_st = 0; r.o_sh = d;
-    r.B = B; r.Hq = Hq; r.Hkv = Hkv; r.G = G; r.d = d; r.nrows = 1; r.t0 = 0;
-    r.window = s->window; r.scale = scale;
-    rc = launch_rc(run_stage(ORTHROS_STAGE_ROWS_F32, st, [&] { return launch_rows_f32(r, st); }));
-    if (rc) return rc;
-    RowsF32Params o = r;
-    o.q = static_cast<const float*>(q_out);
-    o.alpha = aff->alpha_out; o.beta = aff->beta_out;
-    o.o = static_cast<float*>(o_out);
-    o.window = INT_MAX;
-    rc = launch_rc(run_stage(ORTHROS_STAGE_ROWS_F32, st, [&] { return launch_rows_f32(o, st); }));
-    if (rc) return rc;
-  } else {
-    SplitParams sp{};
-    sp.q_out = q_out; sp.q_base = q_base; sp.q_sb = (idx_t)Hq * d; sp.q_sh = d;
-    sp.a_out = aff->alpha_out; sp.b_out = aff->beta_out;
-    sp.a_base = aff->alpha_base; sp.b_base = aff->beta_base;
-    sp.k = cache_k; sp.v = cache_v;
-    sp.k_sb = (idx_t)Hkv * s->capacity * d; sp.k_sh = s->capacity * d; sp.k_st = d;
-    sp.knew = k_new; sp.vnew = v_new; sp.kn_sb = (idx_t)Hkv * d; sp.kn_sh = d;
-    sp.len = cache_len; sp.cap = s->capacity;
-    sp.B = B; sp.Hq = Hq; sp.Hkv = Hkv; sp.G = G;
-    sp.HC = heads_per_chunk(G, true);
-    sp.nchunks = (G + sp.HC - 1) / sp.HC;
-    sp.window = s->window; sp.with_base = 1;
-    sp.nsplit = nsplit_for(hint + 1, (int64_t)B * Hkv * sp.nchunks);
-    sp.scale_log2 = scale * kLog2e;
-    sp.pm = reinterpret_cast<float*>(wsc + L.pm);
-    sp.pl = reinterpret_cast<float*>(wsc + L.pl);
-    sp.po = reinterpret_cast<float*>(wsc + L.po);
-    rc = launch_rc(run_stage(ORTHROS_STAGE_SPLIT_ROWS, st, [&] { return launch_split_rows(sp, d, st); }));
-    if (rc) return rc;
-    MergeParams mp{};
-    mp.pm = sp.pm; mp.pl = sp.pl; mp.po = sp.po;
-    mp.out0 = o_out; mp.o_sb0 = (idx_t)Hq * d; mp.o_sh0 = d;
-    mp.out1 = o_base; mp.o_sb1 = (idx_t)Hq * d; mp.o_sh1 = d;
-    mp.rows = B * Hq * 2; mp.nsplit = sp.nsplit; mp.d = d; mp.Hq = Hq; mp.nstreams = 2; mp.bf16 = 1;
-    rc = launch_rc(run_stage(ORTHROS_STAGE_MERGE, st, [&] { return launch_merge(mp, st); }));
-    if (rc) return rc;
-  }
-  AppendParams ap{k_new, v_new, cache_k, cache_v, cache_len,
-                  reinterpret_cast<int32_t*>(wsc), B, Hkv, d, esize(s), s->capacity};
-  return launch_rc(run_stage(ORTHROS_STAGE_APPEND, st, [&] { return launch_append(ap, st); }));
+int orthros_paged_write(const orthros_shape* s, int64_t T, const void* k, const void* v,
+                        const orthros_paged_kv* cache, int32_t* cache_len, void* ws,
+                        size_t ws_bytes, hipStream_t st) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if (T < 1 || T > INT_MAX / 2) return ORTHROS_E_INVALID;
+  if ((rc = check_ptrs({k, v, cache_len}))) return rc;
+  if ((rc = check_ws(s, ws, ws_bytes))) return rc;
+  PagedKV pg{};
+  if ((rc = check_paged(s, cache, ws, &pg))) return rc;
+  PagedWriteParams wp{k, v, cache->k_pages, cache->v_pages, cache_len, s->batch, (int)T,
+                      s->num_kv_heads, s->head_dim, esize(s), s->capacity, pg};
+  return launch_rc(run_stage(ORTHROS_STAGE_CACHE_WRITE, st, [&] { return launch_paged_write(wp, st); }));
 }
 
 int orthros_forward_pt(const orthros_shape* s, int64_t T, const void* q_base, const void* q_out,

@@ -42,8 +42,11 @@ __global__ __launch_bounds__(64) void rows_f32_kernel(RowsF32Params p) {
   }
   const int64_t lo = t - (int64_t)p.window + 1 > 0 ? t - (int64_t)p.window + 1 : 0;
   float m = kNegInf, l = 0.f;
-  const float* kb = p.k + (idx_t)b * p.k_sb + (idx_t)g * p.k_sh;
-  const float* vb = p.v + (idx_t)b * p.k_sb + (idx_t)g * p.k_sh;
+  // Cached rows: contiguous [B, Hkv, cap, d], or kv head g of the sequence's pages.
+  const int32_t* tbl = p.pg.table ? p.pg.table + (idx_t)b * p.pg.tbl_sb : nullptr;
+  const idx_t head_off = tbl ? (idx_t)g * p.pg.k_sh : (idx_t)b * p.k_sb + (idx_t)g * p.k_sh;
+  const float* kb = p.k + head_off;
+  const float* vb = p.v + head_off;
   for (int64_t j = lo; j <= t; ++j) {
     const float* kr;
     const float* vr;
@@ -51,8 +54,9 @@ __global__ __launch_bounds__(64) void rows_f32_kernel(RowsF32Params p) {
       kr = p.knew + (idx_t)b * p.kn_sb + (idx_t)g * p.kn_sh;
       vr = p.vnew + (idx_t)b * p.kn_sb + (idx_t)g * p.kn_sh;
     } else {
-      kr = kb + j * p.k_st;
-      vr = vb + j * p.k_st;
+      const idx_t off = tbl ? paged_offset(p.pg, tbl, j, p.cap, p.k_st) : j * p.k_st;
+      kr = kb + off;
+      vr = vb + off;
     }
     float s = 0.f;
 #pragma unroll

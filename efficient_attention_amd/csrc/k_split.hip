@@ -41,7 +41,7 @@ struct SplitSmem {
 };
 }  // namespace
 
-template <int D>
+template <int D, bool PAGED>
 __global__ __launch_bounds__(256) void split_rows_kernel(SplitParams p) {
   using SM = SplitSmem<D>;
   constexpr int KSTR = SM::KSTR, VSTR = SM::VSTR;
@@ -151,19 +151,17 @@ __global__ __launch_bounds__(256) void split_rows_kernel(SplitParams p) {
     }
   }
 
-  const uint16_t* kbase = reinterpret_cast<const uint16_t*>(p.k) + (idx_t)b * p.k_sb + (idx_t)g * p.k_sh;
-  const uint16_t* vbase = reinterpret_cast<const uint16_t*>(p.v) + (idx_t)b * p.k_sb + (idx_t)g * p.k_sh;
+  // Cached rows: contiguous [B, Hkv, cap, d], or (PAGED) kv head g of the pages the
+  // sequence's table row names.
+  const idx_t head_off = PAGED ? (idx_t)g * p.pg.k_sh : (idx_t)b * p.k_sb + (idx_t)g * p.k_sh;
+  const uint16_t* kbase = reinterpret_cast<const uint16_t*>(p.k) + head_off;
+  const uint16_t* vbase = reinterpret_cast<const uint16_t*>(p.v) + head_off;
   const uint16_t* knew = p.knew ? reinterpret_cast<const uint16_t*>(p.knew) + (idx_t)b * p.kn_sb + (idx_t)g * p.kn_sh : nullptr;
   const uint16_t* vnew = p.vnew ? reinterpret_cast<const uint16_t*>(p.vnew) + (idx_t)b * p.kn_sb + (idx_t)g * p.kn_sh : nullptr;
-
-  auto krow = [&](int64_t key) -> const uint16_t* {
-    if (key >= ke) key = ke - 1;
-    return key == Lnew ? knew : kbase + key * p.k_st;
-  };
-  auto vrow = [&](int64_t key) -> const uint16_t* {
-    if (key >= ke) key = ke - 1;
-    return key == Lnew ? vnew : vbase + key * p.k_st;
-  };
+  const int32_t* tbl = PAGED ? p.pg.table + (idx_t)b * p.pg.tbl_sb : nullptr;
+  // Pages of 64 keys or more hold whole tiles (tiles start at multiples of 64): one table
+  // read per tile. Smaller pages: one per row.
+  const bool page_per_tile = PAGED && p.pg.ps_log2 >= 6;
 
   f32x4 O[NMT];
 #pragma unroll
@@ -174,6 +172,26 @@ __global__ __launch_bounds__(256) void split_rows_kernel(SplitParams p) {
   if (kb < ke) {
     u32x4 kreg[KCH], vreg[VIT][2];
     auto load_tile = [&](int64_t t0) {
+      // Offset of row `key` of this tile (keys past the range re-read its last key; key Lnew
+      // comes from this step's input instead).
+      idx_t tile_off = 0;
+      if (page_per_tile) tile_off = paged_offset(p.pg, tbl, t0, p.cap, p.k_st) - t0 * p.k_st;
+      auto row_off = [&](int64_t key) -> idx_t {
+        if constexpr (PAGED) {
+          if (page_per_tile) return tile_off + key * p.k_st;
+          return paged_offset(p.pg, tbl, key, p.cap, p.k_st);
+        } else {
+          return key * p.k_st;
+        }
+      };
+      auto krow = [&](int64_t key) -> const uint16_t* {
+        if (key >= ke) key = ke - 1;
+        return key == Lnew ? knew : kbase + row_off(key);
+      };
+      auto vrow = [&](int64_t key) -> const uint16_t* {
+        if (key >= ke) key = ke - 1;
+        return key == Lnew ? vnew : vbase + row_off(key);
+      };
 #pragma unroll
       for (int i = 0; i < KCH; ++i) {
         const int ci = tid + 256 * i;
@@ -382,10 +400,17 @@ __global__ __launch_bounds__(64) void merge_kernel(MergeParams p) {
 
 hipError_t launch_split_rows(const SplitParams& p, int d, hipStream_t s) {
   dim3 grid(p.nsplit, p.Hkv * p.nchunks, p.B);
-  if (d == 128)
-    hipLaunchKernelGGL(split_rows_kernel<128>, grid, dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL(split_rows_kernel<64>, grid, dim3(256), 0, s, p);
+  if (p.pg.table) {
+    if (d == 128)
+      hipLaunchKernelGGL((split_rows_kernel<128, true>), grid, dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL((split_rows_kernel<64, true>), grid, dim3(256), 0, s, p);
+  } else {
+    if (d == 128)
+      hipLaunchKernelGGL((split_rows_kernel<128, false>), grid, dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL((split_rows_kernel<64, false>), grid, dim3(256), 0, s, p);
+  }
   return hipGetLastError();
 }
 

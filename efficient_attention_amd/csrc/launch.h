@@ -8,6 +8,39 @@ namespace orthros {
 
 typedef int64_t idx_t;
 
+constexpr int32_t kStatusCacheFull = 1;  // ORTHROS_STATUS_CACHE_FULL
+constexpr int32_t kStatusBadPage = 2;    // ORTHROS_STATUS_BAD_PAGE
+
+// Paged key/value cache: a pool [num_pages, Hkv, 2^ps_log2, d] shared by the batch. Token t of
+// sequence b is slot t mod 2^ps_log2 of page table[b * tbl_sb + (t >> ps_log2)]; k_sp and k_sh
+// are the element strides between pages and between the kv heads of a page. table == nullptr
+// means the cache is the contiguous [B, Hkv, cap, d] one.
+struct PagedKV {
+  const int32_t* table;
+  idx_t tbl_sb;
+  int64_t num_pages;
+  idx_t k_sp, k_sh;
+  int ps_log2;
+  int32_t* status;  // sticky status word (bit kStatusBadPage)
+};
+
+// Element offset of token `key` within kv head 0 of the pool, for the sequence whose table row
+// is `tbl` (rows are k_st elements apart inside a page). The key is clamped into [0, cap) so
+// the table read stays inside the row. A page index outside [0, num_pages) sets kStatusBadPage
+// and *bad, and page 0 stands in for it (readers then stay in bounds; writers must skip).
+__device__ __forceinline__ idx_t paged_offset(const PagedKV& pk, const int32_t* tbl, int64_t key,
+                                              int64_t cap, idx_t k_st, bool* bad = nullptr) {
+  if (key > cap - 1) key = cap - 1;
+  if (key < 0) key = 0;
+  int32_t page = tbl[key >> pk.ps_log2];
+  if (page < 0 || (int64_t)page >= pk.num_pages) {
+    __hip_atomic_fetch_or(pk.status, kStatusBadPage, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (bad) *bad = true;
+    page = 0;
+  }
+  return (idx_t)page * pk.k_sp + (key & (((int64_t)1 << pk.ps_log2) - 1)) * k_st;
+}
+
 // Bulk cache write (prefill / pre-training): k, v [B, T, Hkv, d] -> cache [B, Hkv, cap, d],
 // len[b] = T for every sequence.
 // Rows t of k, v go to cache rows t_first + t; len[b] = t_first + T afterwards.
@@ -32,6 +65,20 @@ struct AppendParams {
   int32_t* status;
   int B, Hkv, d, esize;
   int64_t cap;
+  PagedKV pg;  // paged pool (ck / cv point at it) when pg.table is set
+};
+
+// Paged bulk write: token t of k, v [B, T, Hkv, d] goes to position len[b] + t of the paged
+// cache (a sequence without room for all T tokens is skipped); paged_advance then moves len.
+struct PagedWriteParams {
+  const void* k;
+  const void* v;
+  void* ck;
+  void* cv;
+  int32_t* len;
+  int B, T, Hkv, d, esize;
+  int64_t cap;
+  PagedKV pg;
 };
 
 // Split-key few-row attention (bf16). One work-group per (split, kv head x head chunk, b).
@@ -62,6 +109,7 @@ struct SplitParams {
   idx_t q_st;
   int B, Hq, Hkv, G, HC, nchunks, window, nsplit, with_base;
   float scale_log2;
+  PagedKV pg;  // decode over a paged pool (k / v point at it; k_sh, k_sb unused) when set
   float* pm;  // [rows][nsplit]
   float* pl;  // [rows][nsplit]
   float* po;  // [rows][nsplit][d]
@@ -114,6 +162,7 @@ struct RowsF32Params {
   int64_t cap;         // decode: cache capacity (device lengths are clamped to it)
   const int32_t* pos;  // optional row positions (row r at pos[r], clamped to [0, nkeys))
   int64_t nkeys;       // with pos: keys available
+  PagedKV pg;          // decode over a paged pool (k / v point at it) when pg.table is set
   float* o;
   idx_t o_sb, o_st, o_sh;
   int B, Hq, Hkv, G, d, nrows, t0, window;
@@ -122,6 +171,7 @@ struct RowsF32Params {
 
 hipError_t launch_cache_write(const CacheWriteParams& p, hipStream_t s);
 hipError_t launch_append(const AppendParams& p, hipStream_t s);
+hipError_t launch_paged_write(const PagedWriteParams& p, hipStream_t s);
 hipError_t launch_split_rows(const SplitParams& p, int d, hipStream_t s);
 hipError_t launch_merge(const MergeParams& p, hipStream_t s);
 hipError_t launch_band(const BandParams& p, int d, hipStream_t s);

@@ -15,19 +15,22 @@ import torch
 
 __all__ = [
     "OK", "E_INVALID", "E_UNSUPPORTED", "E_WORKSPACE", "E_CAPACITY", "E_LAUNCH",
-    "STATUS_CACHE_FULL", "STAGES", "OrthrosError", "Shape", "Affine", "lib", "library_path",
-    "workspace_bytes", "sft_workspace_bytes", "make_workspace", "prefill", "prefill_chunk",
-    "decode_step", "forward_pt", "forward_sft", "read_device_status", "status_string",
+    "STATUS_CACHE_FULL", "STATUS_BAD_PAGE", "STAGES", "OrthrosError", "Shape", "Affine",
+    "PagedKV", "lib", "library_path", "workspace_bytes", "sft_workspace_bytes",
+    "make_workspace", "prefill", "prefill_chunk", "decode_step", "decode_step_paged",
+    "paged_write", "forward_pt", "forward_sft", "read_device_status", "status_string",
     "timing_begin", "timing_end", "EXPORTED_SYMBOLS",
 ]
 
 OK, E_INVALID, E_UNSUPPORTED, E_WORKSPACE, E_CAPACITY, E_LAUNCH = 0, -1, -2, -3, -4, -5
 STATUS_CACHE_FULL = 1
+STATUS_BAD_PAGE = 2
 F32, BF16 = 0, 1
 STAGES = ("cache_write", "band", "split_rows", "merge", "append", "rows_f32")
 EXPORTED_SYMBOLS = (
     "orthros_workspace_bytes", "orthros_sft_workspace_bytes", "orthros_prefill",
-    "orthros_prefill_chunk", "orthros_decode_step", "orthros_forward_pt", "orthros_forward_sft",
+    "orthros_prefill_chunk", "orthros_decode_step", "orthros_decode_step_paged",
+    "orthros_paged_write", "orthros_forward_pt", "orthros_forward_sft",
     "orthros_read_device_status", "orthros_status_string", "orthros_timing_begin",
     "orthros_timing_end",
 )
@@ -53,6 +56,12 @@ class _CShape(ctypes.Structure):
 class _CAffine(ctypes.Structure):
     _fields_ = [("alpha_base", ctypes.c_void_p), ("beta_base", ctypes.c_void_p),
                 ("alpha_out", ctypes.c_void_p), ("beta_out", ctypes.c_void_p)]
+
+
+class _CPagedKV(ctypes.Structure):
+    _fields_ = [("k_pages", ctypes.c_void_p), ("v_pages", ctypes.c_void_p),
+                ("block_table", ctypes.c_void_p), ("num_pages", ctypes.c_int64),
+                ("page_size", ctypes.c_int32), ("max_pages", ctypes.c_int32)]
 
 
 def library_path() -> str:
@@ -86,6 +95,12 @@ def lib() -> ctypes.CDLL:
         L.orthros_prefill_chunk.argtypes = [sp, i64, i64, vp, vp, vp, vp, ap, vp, vp, vp, vp, vp,
                                             vp, sz, vp]
         L.orthros_prefill_chunk.restype = ctypes.c_int
+        pp = ctypes.POINTER(_CPagedKV)
+        L.orthros_decode_step_paged.argtypes = [sp, vp, vp, vp, vp, ap, pp, vp, i64, vp, vp, vp,
+                                                sz, vp]
+        L.orthros_decode_step_paged.restype = ctypes.c_int
+        L.orthros_paged_write.argtypes = [sp, i64, vp, vp, pp, vp, vp, sz, vp]
+        L.orthros_paged_write.restype = ctypes.c_int
         L.orthros_read_device_status.argtypes = [vp, sz, ctypes.POINTER(i32), ctypes.c_int, vp]
         L.orthros_read_device_status.restype = ctypes.c_int
         L.orthros_status_string.argtypes = [ctypes.c_int]
@@ -133,6 +148,33 @@ class Affine:
             _check(t, (n,), torch.float32, device, "scale-offset vector")
         return _CAffine(self.alpha_base.data_ptr(), self.beta_base.data_ptr(),
                         self.alpha_out.data_ptr(), self.beta_out.data_ptr())
+
+
+@dataclass(frozen=True)
+class PagedKV:
+    """Paged cache (the C struct orthros_paged_kv): k_pages, v_pages [num_pages, H_kv,
+    page_size, d] and block_table int32 [batch, max_pages], all on the device."""
+    k_pages: torch.Tensor
+    v_pages: torch.Tensor
+    block_table: torch.Tensor
+
+    @property
+    def page_size(self) -> int:
+        return int(self.k_pages.shape[2])
+
+    @property
+    def max_pages(self) -> int:
+        return int(self.block_table.shape[1])
+
+    def c(self, shape: "Shape", device) -> _CPagedKV:
+        n, _, ps, _ = self.k_pages.shape
+        dims = (n, shape.num_kv_heads, ps, shape.head_dim)
+        _check(self.k_pages, dims, shape.dtype, device, "k_pages")
+        _check(self.v_pages, dims, shape.dtype, device, "v_pages")
+        _check(self.block_table, (shape.batch, self.max_pages), torch.int32, device,
+               "block_table")
+        return _CPagedKV(self.k_pages.data_ptr(), self.v_pages.data_ptr(),
+                         self.block_table.data_ptr(), n, ps, self.max_pages)
 
 
 def _check(t, shape, dtype, device, what):
@@ -245,6 +287,44 @@ def decode_step(shape: Shape, q_base, q_out, k_new, v_new, affine: Affine, cache
         cache_len.data_ptr(), int(max_len_hint), o_base.data_ptr(), o_out.data_ptr(),
         workspace.data_ptr(), workspace.numel(), _stream(stream))
     _rc(rc, "orthros_decode_step")
+
+
+def decode_step_paged(shape: Shape, q_base, q_out, k_new, v_new, affine: Affine,
+                      cache: PagedKV, cache_len, max_len_hint: int, o_base, o_out, workspace,
+                      stream=None):
+    """orthros_decode_step_paged: the decode pair over a paged cache."""
+    B, Hq, Hkv, d = shape.batch, shape.num_q_heads, shape.num_kv_heads, shape.head_dim
+    dev, dt = q_base.device, shape.dtype
+    _check(q_base, (B, Hq, d), dt, dev, "q_base")
+    _check(q_out, (B, Hq, d), dt, dev, "q_out")
+    _check(k_new, (B, Hkv, d), dt, dev, "k_new")
+    _check(v_new, (B, Hkv, d), dt, dev, "v_new")
+    _check(cache_len, (B,), torch.int32, dev, "cache_len")
+    _check(o_base, (B, Hq, d), dt, dev, "o_base")
+    _check(o_out, (B, Hq, d), dt, dev, "o_out")
+    aff = affine.c(Hq * d, dev)
+    pc = cache.c(shape, dev)
+    rc = lib().orthros_decode_step_paged(
+        ctypes.byref(shape.c()), q_base.data_ptr(), q_out.data_ptr(), k_new.data_ptr(),
+        v_new.data_ptr(), ctypes.byref(aff), ctypes.byref(pc), cache_len.data_ptr(),
+        int(max_len_hint), o_base.data_ptr(), o_out.data_ptr(), workspace.data_ptr(),
+        workspace.numel(), _stream(stream))
+    _rc(rc, "orthros_decode_step_paged")
+
+
+def paged_write(shape: Shape, k, v, cache: PagedKV, cache_len, workspace, stream=None):
+    """orthros_paged_write: append k, v [B, T, H_kv, d] to a paged cache."""
+    B, Hkv, d = shape.batch, shape.num_kv_heads, shape.head_dim
+    T = k.shape[1]
+    dev, dt = k.device, shape.dtype
+    _check(k, (B, T, Hkv, d), dt, dev, "k")
+    _check(v, (B, T, Hkv, d), dt, dev, "v")
+    _check(cache_len, (B,), torch.int32, dev, "cache_len")
+    pc = cache.c(shape, dev)
+    rc = lib().orthros_paged_write(ctypes.byref(shape.c()), T, k.data_ptr(), v.data_ptr(),
+                                   ctypes.byref(pc), cache_len.data_ptr(), workspace.data_ptr(),
+                                   workspace.numel(), _stream(stream))
+    _rc(rc, "orthros_paged_write")
 
 
 def forward_pt(shape: Shape, q_base, q_out, k, v, affine: Affine, o_base, o_out, workspace,

@@ -13,7 +13,8 @@
  *     prefilling runs the base stream over the prompt and one output row at the last prompt
  *     token (orthros_prefill, or orthros_prefill_chunk for a prompt arriving in chunks);
  *     decoding processes one new token per sequence as a base copy (cache append + window)
- *     and an output copy (full history) (orthros_decode_step).
+ *     and an output copy (full history) (orthros_decode_step, or orthros_decode_step_paged
+ *     over a paged cache filled by orthros_paged_write).
  * The key/value and query projections (x W_K, x W_V, x W_Q) and the output projection are the
  * caller's: the library starts from head-split projections (Algorithm 1, the split-heads step)
  * and returns the per-head outputs of the two attention calls, before the heads are merged.
@@ -70,8 +71,12 @@ enum {
 
 /* Sticky device status bits, read with orthros_read_device_status. */
 enum {
-  ORTHROS_STATUS_CACHE_FULL = 1  /* a decode step found cache_len == capacity: its token was
-                                    not appended (its attention outputs are still exact) */
+  ORTHROS_STATUS_CACHE_FULL = 1, /* a decode step found cache_len == capacity: its token was
+                                    not appended (its attention outputs are still exact); or a
+                                    paged write found no room for a sequence's tokens */
+  ORTHROS_STATUS_BAD_PAGE = 2    /* a block-table entry outside [0, num_pages) was met: page 0
+                                    was read in its place (those outputs are meaningless) and
+                                    nothing was written through it */
 };
 
 /* Problem shape, passed by host pointer. */
@@ -191,6 +196,49 @@ int orthros_prefill_chunk(const orthros_shape* shape, int64_t past_len, int64_t 
                           void* o_base, void* o_out,
                           void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Paged key/value cache: a pool of fixed-size pages shared by the batch, as a serving engine
+ * keeps it (the batched decoding that "Orthros: Phase-Aware Heterogeneous Attention for
+ * Efficient Transformers" names as future work in §5). Token t of sequence b lives in page
+ * block_table[b * max_pages + t / page_size], slot t % page_size. Within a page the layout is
+ * head-major like the contiguous cache, so each (page, kv head) is one run of page_size rows:
+ *   k_pages, v_pages  [num_pages, H_kv, page_size, d] (shape.dtype)
+ *   block_table       int32 [batch, max_pages], device; entries are page indices
+ *   page_size         a power of two (1 .. 2^24); pages of 64 or more rows are fastest
+ * A sequence's capacity is max_pages * page_size and must equal shape.capacity. The caller
+ * owns the pool and the table and assigns pages; a sequence's table entries must name pages
+ * for every position it holds or is about to receive. */
+typedef struct {
+  void* k_pages;
+  void* v_pages;
+  const int32_t* block_table;
+  int64_t num_pages;
+  int32_t page_size;
+  int32_t max_pages;
+} orthros_paged_kv;
+
+/* orthros_decode_step over a paged cache (§3.2 decoding; same outputs, same rounding):
+ * sequence b's keys 0 .. L-1 (L = cache_len[b]) are read through its table row, key L is this
+ * step's (k_new, v_new), which is then written to position L through the table, and
+ * cache_len[b] becomes L+1. A full sequence (L == capacity) sets ORTHROS_STATUS_CACHE_FULL
+ * and is not appended; a bad table entry sets ORTHROS_STATUS_BAD_PAGE. Arguments as for
+ * orthros_decode_step, with the cache given by `cache` (host pointer). */
+int orthros_decode_step_paged(const orthros_shape* shape,
+                              const void* q_base, const void* q_out,
+                              const void* k_new, const void* v_new,
+                              const orthros_affine* affine,
+                              const orthros_paged_kv* cache, int32_t* cache_len,
+                              int64_t max_len_hint,
+                              void* o_base, void* o_out,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Appends T tokens per sequence to a paged cache: k, v [B, T, H_kv, d] go to positions
+ * cache_len[b] .. cache_len[b] + T - 1 through the table, then cache_len[b] += T (prefilling a
+ * prompt into pages, §3.2: the base tokens write the cache). A sequence without room for all T
+ * tokens is left unchanged and ORTHROS_STATUS_CACHE_FULL is set. Requires T >= 1. */
+int orthros_paged_write(const orthros_shape* shape, int64_t T, const void* k, const void* v,
+                        const orthros_paged_kv* cache, int32_t* cache_len,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Copies the workspace's sticky status word to *host_status (host pointer) after draining
  * `stream`; clears it on the device afterwards when `clear` is non-zero. Synchronous. */
 int orthros_read_device_status(void* workspace, size_t workspace_bytes, int32_t* host_status,
@@ -204,7 +252,7 @@ const char* orthros_status_string(int code);
  * them and writes, per stage, the summed milliseconds and the launch count (host arrays of
  * ORTHROS_NUM_STAGES entries), then stops recording. Host-side state; not thread-safe. */
 enum {
-  ORTHROS_STAGE_CACHE_WRITE = 0,  /* bulk cache write (prefill / pt) */
+  ORTHROS_STAGE_CACHE_WRITE = 0,  /* bulk cache write (prefill / pt / paged write) */
   ORTHROS_STAGE_BAND = 1,         /* banded flash kernel (Eq. 4 windows, Eq. 5 causal rows) */
   ORTHROS_STAGE_SPLIT_ROWS = 2,   /* split-key few-row kernel (output rows, decode pair) */
   ORTHROS_STAGE_MERGE = 3,        /* split merge */

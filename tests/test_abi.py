@@ -214,3 +214,66 @@ def test_prefill_chunk_rejects_bad_lengths_and_workspace():
     assert _chunk(_shape(capacity=163), past=100, C=64) == ox.E_CAPACITY
     assert _chunk(_shape(capacity=164), past=100, C=64, ws=None) == ox.E_WORKSPACE
     assert _chunk(_shape(), ws_bytes=64) == ox.E_WORKSPACE
+
+
+def _paged(**kw):
+    c = dict(k_pages=FAKE, v_pages=FAKE, block_table=FAKE, num_pages=100, page_size=64,
+             max_pages=16)
+    c.update(kw)
+    return ox._CPagedKV(**c)
+
+
+def _decode_paged(shape, cache=None, hint=100, ws_bytes=None, **ptrs):
+    p = dict(q_base=FAKE, q_out=FAKE, k_new=FAKE, v_new=FAKE, cache_len=FAKE, o_base=FAKE,
+             o_out=FAKE, ws=FAKE)
+    p.update(ptrs)
+    L = ox.lib()
+    wsb = L.orthros_workspace_bytes(ctypes.byref(shape)) if ws_bytes is None else ws_bytes
+    c = cache if cache is not None else _paged()
+    return L.orthros_decode_step_paged(ctypes.byref(shape), p["q_base"], p["q_out"], p["k_new"],
+                                       p["v_new"], ctypes.byref(_aff()), ctypes.byref(c),
+                                       p["cache_len"], hint, p["o_base"], p["o_out"], p["ws"],
+                                       wsb, None)
+
+
+def _paged_write(shape, T=8, cache=None, ws_bytes=None, **ptrs):
+    p = dict(k=FAKE, v=FAKE, cache_len=FAKE, ws=FAKE)
+    p.update(ptrs)
+    L = ox.lib()
+    wsb = L.orthros_workspace_bytes(ctypes.byref(shape)) if ws_bytes is None else ws_bytes
+    c = cache if cache is not None else _paged()
+    return L.orthros_paged_write(ctypes.byref(shape), T, p["k"], p["v"], ctypes.byref(c),
+                                 p["cache_len"], p["ws"], wsb, None)
+
+
+@pytest.mark.parametrize("name", ["q_base", "q_out", "k_new", "v_new", "cache_len", "o_base",
+                                  "o_out"])
+def test_decode_paged_rejects_null_and_misaligned(name):
+    assert _decode_paged(_shape(), **{name: None}) == ox.E_INVALID
+    assert _decode_paged(_shape(), **{name: FAKE + 4}) == ox.E_INVALID
+
+
+@pytest.mark.parametrize("bad", [dict(k_pages=None), dict(v_pages=FAKE + 8),
+                                 dict(block_table=None), dict(num_pages=0),
+                                 dict(num_pages=1 << 31), dict(max_pages=0),
+                                 dict(page_size=0), dict(page_size=48),  # not a power of two
+                                 dict(page_size=32),                      # capacity 512 != 1024
+                                 dict(max_pages=17)])                     # capacity 1088
+def test_paged_cache_descriptor_is_validated(bad):
+    shape = _shape()  # capacity 1024 = 16 pages x 64
+    assert _decode_paged(shape, cache=_paged(**bad)) == ox.E_INVALID
+    assert _paged_write(shape, cache=_paged(**bad)) == ox.E_INVALID
+
+
+def test_paged_calls_reject_bad_shape_lengths_and_workspace():
+    L = ox.lib()
+    assert L.orthros_decode_step_paged(ctypes.byref(_shape()), FAKE, FAKE, FAKE, FAKE,
+                                       ctypes.byref(_aff()), None, FAKE, 1, FAKE, FAKE, FAKE,
+                                       1 << 30, None) == ox.E_INVALID
+    assert _decode_paged(_shape(head_dim=96)) == ox.E_UNSUPPORTED
+    assert _decode_paged(_shape(), hint=-1) == ox.E_INVALID
+    assert _decode_paged(_shape(), ws_bytes=100) == ox.E_WORKSPACE
+    assert _decode_paged(_shape(), ws=None) == ox.E_WORKSPACE
+    assert _paged_write(_shape(), T=0) == ox.E_INVALID
+    assert _paged_write(_shape(), k=None) == ox.E_INVALID
+    assert _paged_write(_shape(), ws_bytes=16) == ox.E_WORKSPACE

@@ -173,3 +173,50 @@ def test_decode_8b_128k_fullsize():
     for s in range(steps):  # appended rows, bit for bit
         assert torch.equal(ck[:, :, L0 + s], inp["k_new"][s])
         assert torch.equal(cv[:, :, L0 + s], inp["v_new"][s])
+
+
+def test_decode_8b_128k_paged_equals_contiguous():
+    """The full-size decode workload with its history dealt into a shuffled pool of 64-token
+    pages: two steps, outputs bit for bit equal to the contiguous cache's (same kernels and
+    arithmetic; test_decode_8b_128k_fullsize checks those against the oracle)."""
+    wl = syn.WORKLOADS["decode_8b_128k"]
+    _say("full-size paged decode", wl)
+    B, L0, Hq, Hkv, d = wl.batch, wl.length, wl.q_heads, wl.kv_heads, wl.head_dim
+    ps = 64
+    max_pages = -(-(L0 + wl.steps + 4) // ps)
+    cap = max_pages * ps
+    inp = syn.make_decode_resident(wl, DEV, cap)
+    ck, cv = inp["cache_k"], inp["cache_v"]
+    g = torch.Generator(device=DEV)
+    g.manual_seed(wl.seed + 11)
+    num_pages = B * max_pages
+    table = torch.randperm(num_pages, generator=g, device=DEV).view(B, max_pages)
+    kp = torch.empty(num_pages, Hkv, ps, d, dtype=torch.bfloat16, device=DEV)
+    vp = torch.empty_like(kp)
+    nb = L0 // ps
+    for b in range(B):
+        idx = table[b, :nb]
+        kp[idx] = ck[b, :, :L0].reshape(Hkv, nb, ps, d).permute(1, 0, 2, 3)
+        vp[idx] = cv[b, :, :L0].reshape(Hkv, nb, ps, d).permute(1, 0, 2, 3)
+    cache = ox.PagedKV(kp, vp, table.to(torch.int32).contiguous())
+    shape = ox.Shape(B, Hq, Hkv, d, wl.window, torch.bfloat16, cap)
+    cl_c = torch.full((B,), L0, dtype=torch.int32, device=DEV)
+    cl_p = cl_c.clone()
+    ws_c, ws_p = ox.make_workspace(shape, DEV), ox.make_workspace(shape, DEV)
+    aff = ox.Affine(*inp["affine"])
+    for s in range(2):
+        args = [inp[n][s] for n in ("q_base", "q_out", "k_new", "v_new")]
+        outs = [torch.empty(B, Hq, d, dtype=torch.bfloat16, device=DEV) for _ in range(4)]
+        ox.decode_step(shape, *args, aff, ck, cv, cl_c, L0 + s, outs[0], outs[1], ws_c)
+        ox.decode_step_paged(shape, *args, aff, cache, cl_p, L0 + s, outs[2], outs[3], ws_p)
+        torch.cuda.synchronize()
+        assert not torch.isnan(outs[0]).any().item()
+        assert torch.equal(outs[0], outs[2]), f"o_base differs at step {s}"
+        assert torch.equal(outs[1], outs[3]), f"o_out differs at step {s}"
+    assert torch.equal(cl_c, cl_p)
+    assert ox.read_device_status(ws_p) == 0
+    for s in range(2):
+        t = L0 + s
+        page = table[:, t // ps]
+        assert torch.equal(kp[page, :, t % ps], inp["k_new"][s])
+        assert torch.equal(vp[page, :, t % ps], inp["v_new"][s])
