@@ -136,13 +136,39 @@ def bench_prefill(wl, steps, warmup, dev):
     return dict(ms=ms, stages=stages, inp=inp, planted=inp["planted_pos"])
 
 
-def bench_decode(wl, warmup, dev):
+def paged_pool(ck, cv, L0, ps, seed):
+    """The resident contiguous caches [B, H_kv, cap, d] dealt into a pool of ps-token pages in
+    a seeded random order: (k_pages, v_pages, block_table [B, cap / ps] int32)."""
+    B, Hkv, cap, d = ck.shape
+    assert cap % ps == 0 and L0 % ps == 0
+    max_pages, nb = cap // ps, L0 // ps
+    g = torch.Generator(device=ck.device)
+    g.manual_seed(seed)
+    table = torch.randperm(B * max_pages, generator=g, device=ck.device).view(B, max_pages)
+    kp = torch.empty(B * max_pages, Hkv, ps, d, dtype=ck.dtype, device=ck.device)
+    vp = torch.empty_like(kp)
+    for b in range(B):
+        kp[table[b, :nb]] = ck[b, :, :L0].reshape(Hkv, nb, ps, d).permute(1, 0, 2, 3)
+        vp[table[b, :nb]] = cv[b, :, :L0].reshape(Hkv, nb, ps, d).permute(1, 0, 2, 3)
+    return kp, vp, table.to(torch.int32).contiguous()
+
+
+def bench_decode(wl, warmup, dev, page_size=0):
+    """Decode steps over the resident caches; with page_size > 0 over a shuffled page pool."""
     S = wl.steps
-    log(f"decode {wl.name}: filling {wl.batch} caches of {wl.length} tokens on {dev}")
+    log(f"decode {wl.name}: filling {wl.batch} caches of {wl.length} tokens on {dev}"
+        + (f", {page_size}-token pages" if page_size else ""))
     B, L0, Hq, Hkv, d = wl.batch, wl.length, wl.q_heads, wl.kv_heads, wl.head_dim
     cap = L0 + S + warmup
+    if page_size:
+        cap = -(-cap // page_size) * page_size
     inp = syn.make_decode_resident(wl, dev, cap)
     ck, cv = inp["cache_k"], inp["cache_v"]
+    cache = None
+    if page_size:
+        cache = ox.PagedKV(*paged_pool(ck, cv, L0, page_size, wl.seed + 11))
+        inp["cache_k"] = inp["cache_v"] = ck = cv = None
+        torch.cuda.empty_cache()
     qb, qo, kn, vn = inp["q_base"], inp["q_out"], inp["k_new"], inp["v_new"]
     aff = ox.Affine(*inp["affine"])
     shape = ox.Shape(B, Hq, Hkv, d, wl.window, torch.bfloat16, cap)
@@ -151,16 +177,22 @@ def bench_decode(wl, warmup, dev):
     oo = torch.empty_like(ob)
     ws = ox.make_workspace(shape, dev)
 
+    def step(s, hint):
+        if cache is None:
+            ox.decode_step(shape, qb[s], qo[s], kn[s], vn[s], aff, ck, cv, cl, hint, ob, oo, ws)
+        else:
+            ox.decode_step_paged(shape, qb[s], qo[s], kn[s], vn[s], aff, cache, cl, hint, ob, oo,
+                                 ws)
+
     for i in range(warmup):
-        ox.decode_step(shape, qb[i % S], qo[i % S], kn[i % S], vn[i % S], aff, ck, cv, cl,
-                       L0 + i, ob, oo, ws)
+        step(i % S, L0 + i)
     cl.fill_(L0)
     torch.cuda.synchronize()
     log(f"decode warmup {warmup} done; timing {S} steps")
     ox.timing_begin()
     t0 = time.perf_counter()
     for s in range(S):
-        ox.decode_step(shape, qb[s], qo[s], kn[s], vn[s], aff, ck, cv, cl, L0 + s, ob, oo, ws)
+        step(s, L0 + s)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     stages = ox.timing_end()
@@ -358,6 +390,24 @@ def main():
                          "bytes_per_launch": dc["split_bytes"]},
             "stage_us_per_step": {k: round(v[0] * 1e3 / dw.steps, 2)
                                   for k, v in dc["stages"].items() if v[1]},
+        }
+        del dc
+        torch.cuda.empty_cache()
+        ps = 64
+        dp = bench_decode(dw, 4, dev, page_size=ps)
+        ach = dp["split_bytes"] / dp["split_s"]
+        rec["decode_paged"] = {
+            "metric": "decode-step us @128K", "workload": f"{dw.name}, paged",
+            "page_size": ps, "pages": "shuffled pool, one block table row per sequence",
+            "us_per_step": round(dp["us"], 2),
+            "roofline": {"bound": "hbm", "achieved": round(ach / 1e9, 1),
+                         "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
+                         "frac": round(ach / PEAK_HBM_BYTES, 4),
+                         "kernel": "split_rows_kernel (paged)",
+                         "launch_us": round(dp["split_s"] * 1e6, 2),
+                         "bytes_per_launch": dp["split_bytes"]},
+            "stage_us_per_step": {k: round(v[0] * 1e3 / dw.steps, 2)
+                                  for k, v in dp["stages"].items() if v[1]},
         }
     if not args.skip_regimes:
         ch = bench_prefill_chunked(wl, 8192, max(2, args.steps // 3), 1, dev, pf["inp"])
