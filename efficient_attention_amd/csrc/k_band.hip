@@ -49,21 +49,22 @@ __device__ __forceinline__ float lane_pair_sum(float x) {
   return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 }
 
-// One wave-wide 16-byte-per-lane copy from global memory straight into LDS (lane i fills
-// bytes 16 i .. 16 i + 15 from the address `lds`). Issued as inline assembly so the compiler does
-// not make every later LDS read wait for it (it cannot tell the copy's destination slot from the
-// slots being read); the kernel waits for these copies itself before the barrier that publishes
-// them. M0, which carries the LDS address, is restored afterwards.
-__device__ __forceinline__ void copy_to_lds(const void* g, uint32_t lds) {
+// One wave-wide 16-byte-per-lane copy from global memory straight into LDS: lane i reads
+// `base` + off_i (a scalar base and a 32-bit per-lane offset, so no vector address arithmetic)
+// and fills bytes 16 i .. 16 i + 15 from the LDS address `lds`. Issued as inline assembly so
+// the compiler does not make every later LDS read wait for it (it cannot tell the copy's
+// destination slot from the slots being read); the kernel waits for these copies itself before
+// the barrier that publishes them. M0, which carries the LDS address, is restored afterwards.
+__device__ __forceinline__ void copy_to_lds(const void* base, uint32_t off, uint32_t lds) {
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %1\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %2, off\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "s"(lds), "v"(g)
+      : "s"(lds), "v"(off), "s"(base)
       : "memory");
 }
 __device__ __forceinline__ void wait_lds_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -109,10 +110,12 @@ __global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
     pb = (int)(lid % npb);
     rest = (int)(lid / npb);
   }
-  const int hc = rest % nhc;
+  // (integer division runs on the vector ALUs: read the results back as scalars)
+  pb = __builtin_amdgcn_readfirstlane(pb);
+  const int hc = __builtin_amdgcn_readfirstlane(rest % nhc);
   rest /= nhc;
-  const int g = rest % p.Hkv;
-  const int b = rest / p.Hkv;
+  const int g = __builtin_amdgcn_readfirstlane(rest % p.Hkv);
+  const int b = __builtin_amdgcn_readfirstlane(rest / p.Hkv);
   const int r0 = pb * BMP;                     // first row of the work-group
   const int h = g * p.G + hc * HPW + (wv % HPW);
   const int r0w = r0 + kQW * (wv / HPW);       // first row of this wavefront
@@ -200,6 +203,10 @@ __global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
   const int tile_lo = glo / kTK * kTK;
   const int tile_hi = ghi / kTK * kTK;
   const int ntiles = (tile_hi - tile_lo) / kTK + 1;
+  // Scalar copies for the loop and the tile copies (the per-wavefront conditions below keep
+  // their vector form: as scalar branches they cost the register allocator more than they save).
+  const int tile_hi_s = __builtin_amdgcn_readfirstlane(tile_hi);
+  const int ntiles_s = __builtin_amdgcn_readfirstlane(ntiles);
   const int wlo = qmin_w - w + 1;  // lowest key any row of this wavefront needs (may be < 0)
   auto tile_key = [&](int e) { return tile_hi - kTK * e; };
   // This wavefront's tiles: ea (holds its highest row) .. eb (holds its lowest key), contiguous.
@@ -238,26 +245,27 @@ __global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
     svoff[i] = (uint32_t)r * rowb + 16u * (uint32_t)(c ^ (4 * ((r >> 1) % (NCH / 4))));
   }
   const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) unsigned char*)smem);
+  const int wv_s = __builtin_amdgcn_readfirstlane(wv);
   auto load_tile = [&](int e) {
-    const int tb = tile_key(e);
+    const int tb = tile_hi_s - kTK * e;
     const unsigned char* kt = reinterpret_cast<const unsigned char*>(kbase) + (idx_t)tb * rowb;
     const unsigned char* vt = reinterpret_cast<const unsigned char*>(vbase) + (idx_t)tb * rowb;
     unsigned char* st = smem + (e % kStages) * STAGEB;
     if (tb + kTK <= nk) {
 #pragma unroll
       for (int i = 0; i < NINST; ++i) {
-        const uint32_t kd = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(st - smem) + (wv * NINST + i) * 1024);
-        copy_to_lds(kt + skoff[i], kd);
-        copy_to_lds(vt + svoff[i], kd + TILEB);
+        const uint32_t kd = lds0 + (uint32_t)(st - smem) + (wv_s * NINST + i) * 1024;
+        copy_to_lds(kt, skoff[i], kd);
+        copy_to_lds(vt, svoff[i], kd + TILEB);
       }
     } else {
 #pragma unroll
       for (int i = 0; i < NINST; ++i) {
         const int over = srow[i] - (nk - 1 - tb);
         const uint32_t back = over > 0 ? (uint32_t)over * rowb : 0u;
-        const uint32_t kd = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(st - smem) + (wv * NINST + i) * 1024);
-        copy_to_lds(kt + (skoff[i] - back), kd);
-        copy_to_lds(vt + (svoff[i] - back), kd + TILEB);
+        const uint32_t kd = lds0 + (uint32_t)(st - smem) + (wv_s * NINST + i) * 1024;
+        copy_to_lds(kt, skoff[i] - back, kd);
+        copy_to_lds(vt, svoff[i] - back, kd + TILEB);
       }
     }
   };
@@ -384,14 +392,14 @@ __global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
   // slot tile e - 2 left (free since the previous barrier) and has landed by the barrier that
   // ends iteration e (the barrier waits for outstanding loads).
   load_tile(0);
-  if (ntiles > 1) load_tile(1);
+  if (ntiles_s > 1) load_tile(1);
   wait_lds_copies();
   __syncthreads();
 
   f32x16 S0 = zero16, S1 = zero16;
   bf16x8 P0[2], P1[2];
-  for (int e = 0; e < ntiles; ++e) {
-    if (e + 2 < ntiles) load_tile(e + 2);
+  for (int e = 0; e < ntiles_s; ++e) {
+    if (e + 2 < ntiles_s) load_tile(e + 2);
     if (wactive && e >= ea && e <= eb) {
       const bool prev = e > ea, next = e < eb, fl = full(e);
       if (!prev) qk(S0, e, 0);
