@@ -21,6 +21,10 @@ Efficient Transformers":
   * §3.2 Prefilling with the prompt arriving in chunks: the chunk's base tokens append their
     keys/values after the cached ones and run their windows over history plus chunk; one
     output row at the chunk's last token sees every key.
+  * §3.2 Pre-Training is a training regime (the loss is taken at every position) and §3.1
+    makes alpha, beta, alpha', beta' learnable: the backward pass gives the gradients of both
+    streams with respect to the raw queries, the shared keys and values and the four
+    scale-offset vectors, and the training forward the per-row log-sum-exp it reuses.
   * §3.2 Decoding over a paged cache (the batched serving setting §5 names as future work):
     the same decode step, with each sequence's history stored in fixed-size pages of a shared
     pool and found through a per-sequence table of page indices.
@@ -57,6 +61,8 @@ __all__ = [
     "gather_pages",
     "paged_write",
     "decode_step_paged",
+    "lse_pt",
+    "backward_pt",
 ]
 
 
@@ -336,3 +342,95 @@ def decode_step_paged(k_pages, v_pages, table, cache_len, q_base, q_out, k_new, 
     kp, vp, lens, full = paged_write(k_pages, v_pages, table, cache_len,
                                      _f64(k_new)[:, None], _f64(v_new)[:, None])
     return o_base, o_out, kp, vp, lens, full
+
+
+def _stream_rows(T: int, window):
+    """Key range [lo, t] of every row t: Eq. 4 with a window, Eq. 5 (window None) without."""
+    return [(0 if window is None else max(0, t - window + 1), t) for t in range(T)]
+
+
+def lse_pt(q_base, q_out, k, alpha_b, beta_b, alpha_o, beta_o, window, scale=None):
+    """Per-row log-sum-exp (natural log) of the scaled scores s q_t . k_j over each row's keys,
+    for the base rows (Eq. 4 ranges) and the output rows (Eq. 5 ranges) of the Pre-Training
+    regime. Returns (lse_base, lse_out), each [B, H_q, T]."""
+    k = _f64(k)
+    B, T, hq, d = np.shape(q_base)
+    hkv = k.shape[2]
+    s = default_scale(d) if scale is None else scale
+    out = []
+    for q_raw, a, bt, w in ((q_base, alpha_b, beta_b, window), (q_out, alpha_o, beta_o, None)):
+        q = scale_offset(q_raw, a, bt)
+        lse = np.empty((B, hq, T))
+        for b in range(B):
+            for h in range(hq):
+                g = _kv_head(h, hq, hkv)
+                for t, (lo, hi) in enumerate(_stream_rows(T, w)):
+                    z = s * (k[b, lo:hi + 1, g] @ q[b, t, h])
+                    m = z.max()
+                    lse[b, h, t] = m + np.log(np.exp(z - m).sum())
+        out.append(lse)
+    return out[0], out[1]
+
+
+def _stream_backward(q_raw, a, bt, K, V, dO, window, s):
+    """Backward of one stream for one (sequence, query head).
+
+    q_raw [T, d] raw queries with their scale-offset a, bt [d]; K, V [T, d] of the kv head;
+    dO [T, d] the gradient of the loss with respect to the stream's outputs. With
+    q = a (.) q_raw + bt, P the row-softmax weights of s q K^T over each row's keys and
+    O = P V: dV = P^T dO; dP = dO V^T; the softmax Jacobian gives
+    dZ_tj = P_tj (dP_tj - sum_m P_tm dP_tm); dq = s dZ K; dK = s dZ^T q; and through the
+    scale-offset dq_raw = a (.) dq, da = sum_t dq (.) q_raw, db = sum_t dq.
+    """
+    q = a * q_raw + bt
+    T = q.shape[0]
+    P = np.zeros((T, T))
+    for t, (lo, hi) in enumerate(_stream_rows(T, window)):
+        P[t, lo:hi + 1] = attention_weights(q[t], K[lo:hi + 1], s)
+    dV = P.T @ dO
+    dP = dO @ V.T
+    dZ = P * (dP - np.sum(P * dP, axis=1, keepdims=True))
+    dq = s * (dZ @ K)
+    dK = s * (dZ.T @ q)
+    return a * dq, np.sum(dq * q_raw, axis=0), np.sum(dq, axis=0), dK, dV
+
+
+def backward_pt(q_base, q_out, k, v, alpha_b, beta_b, alpha_o, beta_o, do_base, do_out,
+                window, scale=None):
+    """Gradients of the Pre-Training regime's two streams (§3.2) for the output gradients
+    do_base, do_out [B, T, H_q, d].
+
+    Returns a dict with dq_base, dq_out [B, T, H_q, d] (with respect to the raw queries, before
+    the scale-offset), dk, dv [B, T, H_kv, d] (both streams' contributions, summed over the
+    query heads that share each kv head) and dalpha_b, dbeta_b, dalpha_o, dbeta_o [H_q * d]
+    (summed over sequences and positions).
+    """
+    k = _f64(k)
+    v = _f64(v)
+    B, T, hq, d = np.shape(q_base)
+    hkv = k.shape[2]
+    s = default_scale(d) if scale is None else scale
+    res = dict(dq_base=np.zeros((B, T, hq, d)), dq_out=np.zeros((B, T, hq, d)),
+               dk=np.zeros((B, T, hkv, d)), dv=np.zeros((B, T, hkv, d)))
+    for name, q_raw, a, bt, dO, w in (("b", q_base, alpha_b, beta_b, do_base, window),
+                                      ("o", q_out, alpha_o, beta_o, do_out, None)):
+        q_raw = _f64(q_raw)
+        dO = _f64(dO)
+        A = _f64(a).reshape(hq, d)
+        Bt = _f64(bt).reshape(hq, d)
+        da = np.zeros((hq, d))
+        db = np.zeros((hq, d))
+        dq_all = res["dq_base" if name == "b" else "dq_out"]
+        for b in range(B):
+            for h in range(hq):
+                g = _kv_head(h, hq, hkv)
+                dqr, dah, dbh, dK, dV = _stream_backward(q_raw[b, :, h], A[h], Bt[h], k[b, :, g],
+                                                         v[b, :, g], dO[b, :, h], w, s)
+                dq_all[b, :, h] = dqr
+                da[h] += dah
+                db[h] += dbh
+                res["dk"][b, :, g] += dK
+                res["dv"][b, :, g] += dV
+        res["dalpha_" + name] = da.reshape(-1)
+        res["dbeta_" + name] = db.reshape(-1)
+    return res

@@ -412,3 +412,97 @@ def test_paged_decode_equals_contiguous_decode(ps):
     changed = np.argwhere(kp2 != kp)
     assert len({(int(c[0]), int(c[2])) for c in changed}) == 2  # one (page, slot) per written seq
     np.testing.assert_array_equal(kp2[table[2]], kp[table[2]])
+
+
+# ---- training: backward pass and per-row log-sum-exp ----------------------------------------
+def _train_case(B=1, T=8, Hq=2, Hkv=1, d=4, seed=5):
+    r = np.random.default_rng(seed)
+    x = dict(q_base=r.standard_normal((B, T, Hq, d)), q_out=r.standard_normal((B, T, Hq, d)),
+             k=r.standard_normal((B, T, Hkv, d)), v=r.standard_normal((B, T, Hkv, d)),
+             alpha_b=1 + 0.3 * r.standard_normal(Hq * d), beta_b=0.3 * r.standard_normal(Hq * d),
+             alpha_o=1 + 0.3 * r.standard_normal(Hq * d), beta_o=0.3 * r.standard_normal(Hq * d))
+    g = dict(do_base=r.standard_normal((B, T, Hq, d)), do_out=r.standard_normal((B, T, Hq, d)))
+    return x, g
+
+
+def _loss(x, g, w):
+    ob, oo = oracle.forward_pt(x["q_base"], x["q_out"], x["k"], x["v"], x["alpha_b"],
+                               x["beta_b"], x["alpha_o"], x["beta_o"], window=w)
+    return float(np.sum(ob * g["do_base"]) + np.sum(oo * g["do_out"]))
+
+
+_GRAD_OF = dict(q_base="dq_base", q_out="dq_out", k="dk", v="dv", alpha_b="dalpha_b",
+                beta_b="dbeta_b", alpha_o="dalpha_o", beta_o="dbeta_o")
+
+
+@pytest.mark.parametrize("w,Hq,Hkv,B", [(3, 2, 1, 1), (1, 2, 2, 1), (20, 4, 2, 2)])
+def test_backward_matches_central_differences_of_the_forward(w, Hq, Hkv, B):
+    """Every gradient entry equals the central difference of L = <do_base, o_base> +
+    <do_out, o_out> computed with the (separately pinned) forward oracle."""
+    x, g = _train_case(B=B, Hq=Hq, Hkv=Hkv, seed=10 + w)
+    grads = oracle.backward_pt(x["q_base"], x["q_out"], x["k"], x["v"], x["alpha_b"],
+                               x["beta_b"], x["alpha_o"], x["beta_o"], g["do_base"], g["do_out"],
+                               window=w)
+    h = 1e-5
+    for name, gname in _GRAD_OF.items():
+        arr = x[name]
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            keep = arr[idx]
+            arr[idx] = keep + h
+            lp = _loss(x, g, w)
+            arr[idx] = keep - h
+            lm = _loss(x, g, w)
+            arr[idx] = keep
+            num[idx] = (lp - lm) / (2 * h)
+        np.testing.assert_allclose(grads[gname], num, rtol=1e-6, atol=1e-7, err_msg=gname)
+
+
+def test_backward_matches_torch_autograd_through_sdpa():
+    """Gradients equal torch autograd (float64) through scaled_dot_product_attention with an
+    explicit band mask (base stream) and its causal flag (output stream), GQA by repeating
+    the kv heads."""
+    B, T, Hq, Hkv, d, w = 2, 37, 4, 2, 8, 9
+    x, g = _train_case(B=B, T=T, Hq=Hq, Hkv=Hkv, d=d, seed=3)
+    t = {n: torch.tensor(a, dtype=torch.float64, requires_grad=True) for n, a in x.items()}
+    G = Hq // Hkv
+    K = t["k"].transpose(1, 2).repeat_interleave(G, dim=1)
+    V = t["v"].transpose(1, 2).repeat_interleave(G, dim=1)
+    qb = (t["alpha_b"].view(Hq, d) * t["q_base"] + t["beta_b"].view(Hq, d)).transpose(1, 2)
+    qo = (t["alpha_o"].view(Hq, d) * t["q_out"] + t["beta_o"].view(Hq, d)).transpose(1, 2)
+    i = torch.arange(T)
+    band = (i[None, :] <= i[:, None]) & (i[None, :] > i[:, None] - w)
+    F = torch.nn.functional
+    ob = F.scaled_dot_product_attention(qb, K, V, attn_mask=band)
+    oo = F.scaled_dot_product_attention(qo, K, V, is_causal=True)
+    loss = (ob * torch.tensor(g["do_base"]).transpose(1, 2)).sum() + \
+           (oo * torch.tensor(g["do_out"]).transpose(1, 2)).sum()
+    loss.backward()
+    grads = oracle.backward_pt(x["q_base"], x["q_out"], x["k"], x["v"], x["alpha_b"],
+                               x["beta_b"], x["alpha_o"], x["beta_o"], g["do_base"], g["do_out"],
+                               window=w)
+    for name, gname in _GRAD_OF.items():
+        np.testing.assert_allclose(grads[gname], t[name].grad.numpy(), rtol=1e-9, atol=1e-11,
+                                   err_msg=gname)
+
+
+def test_lse_matches_library_logsumexp():
+    B, T, Hq, Hkv, d, w = 1, 30, 4, 2, 8, 7
+    x, _ = _train_case(B=B, T=T, Hq=Hq, Hkv=Hkv, d=d, seed=4)
+    lb, lo = oracle.lse_pt(x["q_base"], x["q_out"], x["k"], x["alpha_b"], x["beta_b"],
+                           x["alpha_o"], x["beta_o"], window=w)
+    s = 1 / math.sqrt(d)
+    i = torch.arange(T)
+    band = (i[None, :] <= i[:, None]) & (i[None, :] > i[:, None] - w)
+    causal = i[None, :] <= i[:, None]
+    for q_raw, a, bt, mask, got in ((x["q_base"], x["alpha_b"], x["beta_b"], band, lb),
+                                    (x["q_out"], x["alpha_o"], x["beta_o"], causal, lo)):
+        q = torch.tensor(a.reshape(Hq, d) * q_raw + bt.reshape(Hq, d))[0]  # [T, Hq, d]
+        for h in range(Hq):
+            kk = torch.tensor(x["k"][0, :, h // (Hq // Hkv)])
+            z = s * q[:, h] @ kk.T
+            z = z.masked_fill(~mask, float("-inf"))
+            np.testing.assert_allclose(got[0, h], torch.logsumexp(z, dim=1).numpy(), rtol=1e-12)
+    # a row with one key (t = 0) has lse equal to its only score
+    q0 = x["alpha_b"].reshape(Hq, d) * x["q_base"][0, 0] + x["beta_b"].reshape(Hq, d)
+    np.testing.assert_allclose(lb[0, 0, 0], s * q0[0] @ x["k"][0, 0, 0], rtol=1e-12)
