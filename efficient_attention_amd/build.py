@@ -15,7 +15,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "liborthros.so")
-SOURCES = ["k_cache.hip", "k_rows_f32.hip", "k_split.hip", "k_band.hip", "api.cpp"]
+SOURCES = ["k_cache.hip", "k_rows_f32.hip", "k_split.hip", "k_band.hip", "k_bwd.hip",
+           "k_bwd_f32.hip", "api.cpp"]
 ARCH = "gfx950"
 
 

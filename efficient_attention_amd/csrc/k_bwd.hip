@@ -1,0 +1,557 @@
+// Training backward on the matrix cores (bf16 in, fp32 accumulation).
+//
+// Gradients of "Orthros: Phase-Aware Heterogeneous Attention for Efficient Transformers",
+// §3.2 Pre-Training regime: base rows (Eq. 4, keys t-w+1 .. t) and output rows (Eq. 5, keys
+// 0 .. t) at every position, with respect to the queries, the shared keys and values and the
+// scale-offset vectors of §3.1. For a row t with weights P_j = exp(z_j - lse_t) (z_j the scaled
+// score, lse_t saved by the forward), output gradient dO and D_t = dO . O_t:
+//   dP_j = dO . v_j;  dZ_j = P_j (dP_j - D_t);  dq = s sum_j dZ_j k_j;
+//   dk_j += s dZ_j q;  dv_j += P_j dO.
+// Kernels:
+//   qprep_kernel   q' = bf16((alpha (.) q_raw + beta) s log2 e) for both streams: the score
+//                  operand, rounded once as in the forward
+//   bwd_q_kernel   per 32 query rows of one stream: D_t and dq (fp32, before the scale-offset)
+//                    S^T = K Q'^T, dP^T = V dO^T   (A operand: key / value rows from LDS)
+//                    dQ^T += K^T dZ^T              (A operand: transposed key reads)
+//   bwd_kv_kernel  per 32 keys: dk and dv over both streams' rows of every query head of the
+//                  kv head's group
+//                    S = Q' K^T, dP = dO V^T       (A operand: query / gradient rows from LDS)
+//                    dV^T += dO^T P, dK^T += Q'^T dZ   (A operand: transposed reads)
+// Tiles are copied from global memory straight into LDS, 16-byte slots XOR-swizzled by row; a
+// product's output registers serve directly as the B operand of the next product, as in the
+// forward.
+#include "common.h"
+#include "launch.h"
+#include "lds_mfma.h"
+
+namespace orthros {
+
+namespace {
+constexpr int kTK = 64;     // keys per tile, query side
+constexpr int kQW = 32;     // rows per wavefront (query side) / rows per tile (key side)
+constexpr int kQNW = 8;     // wavefronts per work-group, query side
+constexpr int kKNW = 4;     // wavefronts per work-group, key side, 32 keys each
+constexpr float kLn2 = 0.69314718055994531f;
+
+// Byte offset of 16-byte slot `chunk` of row `row` of a row-major LDS tile with NCH slots per
+// row, the slot index XOR-swizzled by the row (row reads of 16 consecutive rows hit distinct
+// banks; so do the transposed 8-byte reads).
+template <int NCH>
+__device__ __forceinline__ uint32_t slot_off(int row, int chunk) {
+  return (uint32_t)(row * NCH * 16 + 16 * (chunk ^ (row % NCH)));
+}
+
+// Transposed-read offsets (bytes, within a tile) for the A operand V^T-style product: lane
+// group G = lane / 16 supplies, from its lane L, row 16 ks + 8 h2 + 4 (G / 2) + L / 4 at
+// channels 32 dt + 16 (G % 2) + 4 (L % 4) .. + 3; off[h2][dt] covers ks = 0 (ks adds
+// 16 ks rows, which leaves the swizzle unchanged).
+template <int D>
+__device__ __forceinline__ void tr_offsets(int lane, uint32_t (&off)[2][D / 32]) {
+  constexpr int NCH = D / 8;
+  const int G = lane >> 4, L = lane & 15;
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) {
+    const int row = 8 * h2 + 4 * (G >> 1) + (L >> 2);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      const int chunk = 4 * dt + 2 * (G & 1) + ((L & 3) >> 1);
+      off[h2][dt] = slot_off<NCH>(row, chunk) + 8 * (L & 1);
+    }
+  }
+}
+}  // namespace
+
+// ---- q' for both streams -----------------------------------------------------------------------
+struct QPrepParams {
+  const void* q[2];
+  const float* alpha[2];
+  const float* beta[2];
+  void* qp[2];
+  idx_t n;   // elements per stream (B T Hq d)
+  int hd;    // Hq d (the scale-offset period)
+  float c;   // s log2 e
+};
+
+__global__ __launch_bounds__(256) void qprep_kernel(QPrepParams p) {
+  const int st = blockIdx.y;
+  const uint16_t* q = static_cast<const uint16_t*>(p.q[st]);
+  uint16_t* o = static_cast<uint16_t*>(p.qp[st]);
+  const float* al = p.alpha[st];
+  const float* be = p.beta[st];
+  for (idx_t i = (idx_t)blockIdx.x * 256 + threadIdx.x; i < p.n / 8; i += (idx_t)gridDim.x * 256) {
+    const idx_t e0 = i * 8;
+    const int c0 = (int)(e0 % p.hd);
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(q + e0);
+    const f32x4 a0 = *reinterpret_cast<const f32x4*>(al + c0);
+    const f32x4 a1 = *reinterpret_cast<const f32x4*>(al + c0 + 4);
+    const f32x4 b0 = *reinterpret_cast<const f32x4*>(be + c0);
+    const f32x4 b1 = *reinterpret_cast<const f32x4*>(be + c0 + 4);
+    u32x4 out;
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const uint32_t w = raw[e >> 1];
+      const float x0 = bf16_lo(w), x1 = bf16_hi(w);
+      const float y0 = ((e < 4 ? a0[e] : a1[e - 4]) * x0 + (e < 4 ? b0[e] : b1[e - 4])) * p.c;
+      const float y1 = ((e < 4 ? a0[e + 1] : a1[e - 3]) * x1 + (e < 4 ? b0[e + 1] : b1[e - 3])) * p.c;
+      out[e >> 1] = pack_bf16x2(y0, y1);
+    }
+    *reinterpret_cast<u32x4*>(o + e0) = out;
+  }
+}
+
+// ---- query side ------------------------------------------------------------------------------
+// Work-group: 8 wavefronts, HPW query heads of one kv head x (8 / HPW) blocks of 32 rows. p.q
+// is q' (prepared); K and V tiles of 64 keys go through a two-slot LDS ring.
+template <int D, int HPW>
+__global__ __launch_bounds__(64 * kQNW) void bwd_q_kernel(BwdQParams p) {
+  constexpr int NCH = D / 8, ROWB = D * 2, TILEB = kTK * ROWB, STAGEB = 2 * TILEB;
+  constexpr int PB = kQNW / HPW, BMP = kQW * PB, NKS = D / 16, NDT = D / 32;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGEB];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int T = p.T;
+  const int nhc = p.G / HPW;
+  const int npb = (T + BMP - 1) / BMP;
+  const uint32_t total = (uint32_t)p.B * p.Hkv * nhc * npb;
+  const uint32_t lid = xcd_swizzle(blockIdx.x, total);
+  const int inner = p.B * p.Hkv * nhc;
+  const int pb = __builtin_amdgcn_readfirstlane(npb - 1 - (int)(lid / inner));  // longest first
+  int rest = (int)(lid % inner);
+  const int hc = __builtin_amdgcn_readfirstlane(rest % nhc);
+  rest /= nhc;
+  const int g = __builtin_amdgcn_readfirstlane(rest % p.Hkv);
+  const int b = __builtin_amdgcn_readfirstlane(rest / p.Hkv);
+  const int h = g * p.G + hc * HPW + (wv % HPW);
+  const int r0 = pb * BMP;
+  const int r0w = r0 + kQW * (wv / HPW);
+  const int j = lane & 31, hh = lane >> 5;
+  const int row = r0w + j;
+  const bool rvalid = row < T;
+  const bool wactive = r0w < T;
+  const int qrow = rvalid ? row : T - 1;
+  const int w = p.window < T ? p.window : T;
+
+  // Row data: q' and dO fragments (B operands), D_t = dO . O, lse in log2 units.
+  const idx_t rbase = ((idx_t)b * T + qrow) * p.Hq * D + (idx_t)h * D;
+  bf16x8 qf[NKS], dof[NKS];
+  float dsum = 0.f;
+#pragma unroll
+  for (int s = 0; s < NKS; ++s) {
+    const int c0 = 16 * s + 8 * hh;
+    qf[s] = *reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(p.q) + rbase + c0);
+    const u32x4 dr = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.dout) + rbase + c0);
+    const u32x4 orr = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.o) + rbase + c0);
+    dof[s] = __builtin_bit_cast(bf16x8, dr);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      dsum += bf16_lo(dr[e]) * bf16_lo(orr[e]) + bf16_hi(dr[e]) * bf16_hi(orr[e]);
+  }
+  const float Dt = lane_pair_sum(dsum);
+  const idx_t lrow = ((idx_t)b * p.Hq + h) * T + qrow;
+  const float lse2 = p.lse[lrow] * kLog2e;
+  if (rvalid && hh == 0) p.D[lrow] = Dt;
+
+  // Key range of the work-group and of this wavefront (tiles ascending from tile_lo).
+  const int last_w = r0w + kQW - 1 < T - 1 ? r0w + kQW - 1 : T - 1;
+  const int last_b = r0 + BMP - 1 < T - 1 ? r0 + BMP - 1 : T - 1;
+  const int tq = rvalid ? row : last_w;
+  const int glo = r0 - w + 1 > 0 ? r0 - w + 1 : 0;
+  const int tile_lo = __builtin_amdgcn_readfirstlane(glo / kTK * kTK);
+  const int ntiles = __builtin_amdgcn_readfirstlane((last_b / kTK * kTK - glo / kTK * kTK) / kTK + 1);
+  const int wlo = r0w - w + 1 > 0 ? r0w - w + 1 : 0;
+  const int ea = (wlo / kTK * kTK - tile_lo) / kTK;
+  const int eb = (last_w / kTK * kTK - tile_lo) / kTK;
+  auto full = [&](int tb) { return tb + kTK - 1 <= r0w && tb >= last_w - w + 1 && tb + kTK - 1 <= T - 1; };
+
+  // Tile copies (global side swizzled; wave wv fills rows (wv NINST + i) LROWS .. of a tile).
+  constexpr int LROWS = 1024 / ROWB;
+  constexpr int NINST = kTK / LROWS / kQNW;
+  static_assert(NINST >= 1 && NINST * LROWS * kQNW == kTK, "copies cover a tile");
+  const uint32_t rowb = (uint32_t)p.Hkv * D * 2u;
+  const unsigned char* kb = reinterpret_cast<const unsigned char*>(p.k) + ((idx_t)b * T * p.Hkv + g) * D * 2;
+  const unsigned char* vb = reinterpret_cast<const unsigned char*>(p.v) + ((idx_t)b * T * p.Hkv + g) * D * 2;
+  uint32_t coff[NINST];
+  int crow[NINST];
+#pragma unroll
+  for (int i = 0; i < NINST; ++i) {
+    const int r = (wv * NINST + i) * LROWS + lane / NCH;
+    const int c = lane % NCH;
+    crow[i] = r;
+    coff[i] = (uint32_t)r * rowb + 16u * (uint32_t)(c ^ (r % NCH));
+  }
+  const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) unsigned char*)smem);
+  const int wv_s = __builtin_amdgcn_readfirstlane(wv);
+  auto load_tile = [&](int e) {
+    const int tb = tile_lo + kTK * e;
+    const unsigned char* kt = kb + (idx_t)tb * rowb;
+    const unsigned char* vt = vb + (idx_t)tb * rowb;
+    const uint32_t st = lds0 + (uint32_t)((e & 1) * STAGEB);
+#pragma unroll
+    for (int i = 0; i < NINST; ++i) {
+      const int over = crow[i] - (T - 1 - tb);  // rows past the end re-read the last row
+      const uint32_t back = over > 0 ? (uint32_t)over * rowb : 0u;
+      const uint32_t kd = st + (uint32_t)(wv_s * NINST + i) * 1024u;
+      copy_to_lds(kt, coff[i] - back, kd);
+      copy_to_lds(vt, coff[i] - back, kd + TILEB);
+    }
+  };
+
+  uint32_t rd_off[NKS];
+#pragma unroll
+  for (int s = 0; s < NKS; ++s) rd_off[s] = slot_off<NCH>(j, 2 * s + hh);
+  uint32_t tr_off[2][NDT];
+  tr_offsets<D>(lane, tr_off);
+
+  f32x16 dQ[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dQ[dt][r] = 0.f;
+  f32x16 zero16;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) zero16[r] = 0.f;
+
+  load_tile(0);
+  wait_lds_copies();
+  __syncthreads();
+  for (int e = 0; e < ntiles; ++e) {
+    if (e + 1 < ntiles) load_tile(e + 1);
+    if (wactive && e >= ea && e <= eb) {
+      const int tb = tile_lo + kTK * e;
+      const bool fl = full(tb);
+      const unsigned char* st = smem + (e & 1) * STAGEB;
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        f32x16 S = zero16, dP = zero16;
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) {
+          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(st + 32 * m * ROWB + rd_off[s]);
+          S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[s], S, 0, 0, 0);
+        }
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) {
+          const bf16x8 va = *reinterpret_cast<const bf16x8*>(st + TILEB + 32 * m * ROWB + rd_off[s]);
+          dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, dof[s], dP, 0, 0, 0);
+        }
+        if (!fl) {
+          const int kk = tb + 32 * m + 4 * hh;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kk + 8 * (r >> 2) + (r & 3);
+            const bool ok = key <= tq && key > tq - w && key < T;
+            S[r] = ok ? S[r] : kNegInf;
+          }
+        }
+        bf16x8 Z[2];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float pr = fast_exp2(S[r] - lse2);
+          Z[r >> 3][r & 7] = (__bf16)(pr * (dP[r] - Dt));
+        }
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) {
+            const unsigned char* base = st + 16 * (2 * m + k2) * ROWB;
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + tr_off[0][dt]));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + tr_off[1][dt]));
+            dQ[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cat_tr(lo, hi), Z[k2], dQ[dt], 0, 0, 0);
+          }
+        }
+      }
+    }
+    wait_lds_copies();
+    __syncthreads();
+  }
+
+  if (rvalid) {
+    float* out = p.dq + ((idx_t)b * T + row) * p.Hq * D + (idx_t)h * D;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        f32x4 v4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v4[i] = dQ[dt][4 * rg + i] * p.scale;
+        *reinterpret_cast<f32x4*>(out + 32 * dt + 8 * rg + 4 * hh) = v4;
+      }
+  }
+}
+
+// ---- key side --------------------------------------------------------------------------------
+// Work-group: 4 wavefronts, 128 keys of one kv head (wavefront wv owns keys k0 + 32 wv ..).
+// The keys' fragments stay in registers, their values in LDS; 32-row query tiles (q', dO,
+// lse, D) of both streams and every head of the group go through a two-slot LDS ring.
+template <int D>
+__global__ __launch_bounds__(64 * kKNW) void bwd_kv_kernel(BwdKVParams p) {
+  constexpr int NCH = D / 8, ROWB = D * 2, NKS = D / 16, NDT = D / 32;
+  constexpr int KB = kKNW * 32;                  // keys per work-group
+  constexpr int VBYTES = KB * ROWB;              // value block
+  constexpr int QTB = kQW * ROWB;                // one 32-row tile
+  constexpr int STG = 2 * QTB + 2 * kQW * 4;     // q', dO, lse, D
+  __shared__ __attribute__((aligned(16))) unsigned char smem[VBYTES + 2 * STG];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int T = p.T;
+  const int nkb = (T + KB - 1) / KB;
+  const uint32_t total = (uint32_t)p.B * p.Hkv * nkb;
+  const uint32_t lid = xcd_swizzle(blockIdx.x, total);
+  const int bg = p.B * p.Hkv;
+  const int kbi = __builtin_amdgcn_readfirstlane((int)(lid / bg));  // block 0 (most rows) first
+  const int g = __builtin_amdgcn_readfirstlane((int)(lid % bg) % p.Hkv);
+  const int b = __builtin_amdgcn_readfirstlane((int)(lid % bg) / p.Hkv);
+  const int k0 = kbi * KB;
+  const int k0w = k0 + 32 * wv;
+  const int j = lane & 31, hh = lane >> 5;
+  const int key = k0w + j;
+  const bool kvalid = key < T;
+  const int wk_s = __builtin_amdgcn_readfirstlane(wv);
+
+  const idx_t kst = (idx_t)p.Hkv * D;  // elements between consecutive keys
+  const uint16_t* kg = static_cast<const uint16_t*>(p.k) + (idx_t)b * T * kst + (idx_t)g * D;
+  // K^T fragments (B operand of S = Q' K^T): lane (key j, half hh) holds channels 16 s + 8 hh ..
+  bf16x8 kf[NKS];
+  {
+    const uint16_t* kr = kg + (idx_t)(kvalid ? key : T - 1) * kst;
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) kf[s] = *reinterpret_cast<const bf16x8*>(kr + 16 * s + 8 * hh);
+  }
+  const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) unsigned char*)smem);
+  // Value block -> LDS (rows past the end re-read the last row).
+  {
+    constexpr int LROWS = 1024 / ROWB;
+    constexpr int NV = KB / LROWS / kKNW;
+    const unsigned char* vg = reinterpret_cast<const unsigned char*>(static_cast<const uint16_t*>(p.v) + (idx_t)b * T * kst + (idx_t)g * D);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int r = (wv * NV + i) * LROWS + lane / NCH;
+      const int c = lane % NCH;
+      const int kr = k0 + r < T ? k0 + r : T - 1;
+      copy_to_lds(vg, (uint32_t)kr * (uint32_t)(kst * 2) + 16u * (uint32_t)(c ^ (r % NCH)),
+                  lds0 + (uint32_t)(wk_s * NV + i) * 1024u);
+    }
+  }
+
+  // Row tiles: stream st covers rows k0 .. min(T-1, k0 + KB - 1 + w_st - 1).
+  int wst[2], qt0[2], nqt[2];
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    wst[st] = p.window[st] < T ? p.window[st] : T;
+    const int hi = k0 + KB - 1 + wst[st] - 1 < T - 1 ? k0 + KB - 1 + wst[st] - 1 : T - 1;
+    qt0[st] = k0 / kQW;
+    nqt[st] = hi / kQW - qt0[st] + 1;
+  }
+  const int n0 = p.G * nqt[0];
+  const int nitems = n0 + p.G * nqt[1];
+  auto item = [&](int i, int& st, int& hd, int& qt) {
+    st = i < n0 ? 0 : 1;
+    const int k = i < n0 ? i : i - n0;
+    hd = g * p.G + k / nqt[st];
+    qt = qt0[st] + k % nqt[st];
+  };
+
+  // Per-item copies: q' and dO tiles of 32 rows (rows past the end re-read the last row).
+  constexpr int LROWS = 1024 / ROWB;
+  constexpr int NQI = kQW / LROWS / kKNW;
+  static_assert(NQI >= 1 && NQI * LROWS * kKNW == kQW, "copies cover a row tile");
+  uint32_t coff[NQI];
+  int crow[NQI];
+#pragma unroll
+  for (int i = 0; i < NQI; ++i) {
+    const int r = (wv * NQI + i) * LROWS + lane / NCH;
+    const int c = lane % NCH;
+    crow[i] = r;
+    coff[i] = (uint32_t)r * (uint32_t)(p.Hq * D * 2) + 16u * (uint32_t)(c ^ (r % NCH));
+  }
+  const uint32_t rowq = (uint32_t)p.Hq * D * 2;
+  float ld_lse = 0.f, ld_D = 0.f;  // thread tid < 32: row tid of the next tile
+  auto load_item = [&](int i, int slot) {
+    int st, hd, qt;
+    item(i, st, hd, qt);
+    const int t0 = qt * kQW;
+    const idx_t off0 = ((idx_t)b * T + t0) * p.Hq * D + (idx_t)hd * D;
+    const unsigned char* qg = reinterpret_cast<const unsigned char*>(static_cast<const uint16_t*>(p.q[st]) + off0);
+    const unsigned char* dg = reinterpret_cast<const unsigned char*>(static_cast<const uint16_t*>(p.dout[st]) + off0);
+    const uint32_t sb = lds0 + VBYTES + (uint32_t)(slot * STG);
+#pragma unroll
+    for (int k = 0; k < NQI; ++k) {
+      const int over = crow[k] - (T - 1 - t0);
+      const uint32_t back = over > 0 ? (uint32_t)over * rowq : 0u;
+      const uint32_t dst = sb + (uint32_t)(wk_s * NQI + k) * 1024u;
+      copy_to_lds(qg, coff[k] - back, dst);
+      copy_to_lds(dg, coff[k] - back, dst + QTB);
+    }
+    if (tid < kQW) {
+      const int t = t0 + tid < T ? t0 + tid : T - 1;
+      const idx_t lr = ((idx_t)b * p.Hq + hd) * T + t;
+      ld_lse = p.lse[st][lr] * kLog2e;
+      ld_D = p.D[st][lr];
+    }
+  };
+  auto store_rowdata = [&](int slot) {
+    if (tid < kQW) {
+      float* f = reinterpret_cast<float*>(smem + VBYTES + slot * STG + 2 * QTB);
+      f[tid] = ld_lse;
+      f[kQW + tid] = ld_D;
+    }
+  };
+
+  uint32_t rd_off[NKS];
+#pragma unroll
+  for (int s = 0; s < NKS; ++s) rd_off[s] = slot_off<NCH>(j, 2 * s + hh);
+  uint32_t tr_off[2][NDT];
+  tr_offsets<D>(lane, tr_off);
+  uint32_t vb_off[NKS];  // V^T B operand: key 32 wv + j, channels 16 s + 8 hh ..
+#pragma unroll
+  for (int s = 0; s < NKS; ++s) vb_off[s] = slot_off<NCH>(32 * wv + j, 2 * s + hh);
+
+  f32x16 dK[NDT], dV[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dK[dt][r] = 0.f;
+      dV[dt][r] = 0.f;
+    }
+  f32x16 zero16;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) zero16[r] = 0.f;
+
+  if (nitems > 0) {
+    load_item(0, 0);
+    store_rowdata(0);
+  }
+  wait_lds_copies();
+  __syncthreads();
+  for (int i = 0; i < nitems; ++i) {
+    const int slot = i & 1;
+    if (i + 1 < nitems) load_item(i + 1, slot ^ 1);
+    int st, hd, qt;
+    item(i, st, hd, qt);
+    (void)hd;
+    const int t0 = qt * kQW;
+    const int w = wst[st];
+    // rows t0 .. t0+31 against keys k0w .. k0w+31: any pair with key <= t < key + w?
+    const bool need = t0 + kQW - 1 >= k0w && t0 <= k0w + 31 + w - 1 && k0w < T;
+    if (need) {
+      const bool fl = t0 >= k0w + 31 && t0 + kQW - 1 <= k0w + w - 1 && t0 + kQW - 1 < T && k0w + 31 < T;
+      const unsigned char* sq = smem + VBYTES + slot * STG;
+      const unsigned char* sd = sq + QTB;
+      const float* rowf = reinterpret_cast<const float*>(sq + 2 * QTB);
+      f32x16 S = zero16, dP = zero16;
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) {
+        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(sq + rd_off[s]);
+        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[s], S, 0, 0, 0);
+      }
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) {
+        const bf16x8 da = *reinterpret_cast<const bf16x8*>(sd + rd_off[s]);
+        const bf16x8 vbv = *reinterpret_cast<const bf16x8*>(smem + vb_off[s]);
+        dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vbv, dP, 0, 0, 0);
+      }
+      // Register r holds row i(r) = 8 (r / 4) + 4 hh + r % 4 of the tile, column key j.
+      bf16x8 Pb[2], Zb[2];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(rowf + 8 * q4 + 4 * hh);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(rowf + kQW + 8 * q4 + 4 * hh);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int r = 4 * q4 + k;
+          float s = S[r];
+          if (!fl) {
+            const int t = t0 + 8 * q4 + 4 * hh + k;
+            const bool ok = key <= t && key > t - w && t < T && kvalid;
+            s = ok ? s : kNegInf;
+          }
+          const float pr = fast_exp2(s - l4[k]);
+          Pb[r >> 3][r & 7] = (__bf16)pr;
+          Zb[r >> 3][r & 7] = (__bf16)(pr * (dP[r] - d4[k]));
+        }
+      }
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const s16x4 dlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sd + 16 * k2 * ROWB + tr_off[0][dt]));
+          const s16x4 dhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sd + 16 * k2 * ROWB + tr_off[1][dt]));
+          dV[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cat_tr(dlo, dhi), Pb[k2], dV[dt], 0, 0, 0);
+          const s16x4 qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sq + 16 * k2 * ROWB + tr_off[0][dt]));
+          const s16x4 qhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sq + 16 * k2 * ROWB + tr_off[1][dt]));
+          dK[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cat_tr(qlo, qhi), Zb[k2], dK[dt], 0, 0, 0);
+        }
+      }
+    }
+    if (i + 1 < nitems) store_rowdata(slot ^ 1);
+    wait_lds_copies();
+    __syncthreads();
+  }
+
+  if (kvalid) {
+    const idx_t o = ((idx_t)b * T + key) * kst + (idx_t)g * D;
+    uint16_t* dkr = static_cast<uint16_t*>(p.dk) + o;
+    uint16_t* dvr = static_cast<uint16_t*>(p.dv) + o;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int c = 32 * dt + 8 * rg + 4 * hh;
+        u32x2 a, v;
+        a[0] = pack_bf16x2(dK[dt][4 * rg + 0] * kLn2, dK[dt][4 * rg + 1] * kLn2);
+        a[1] = pack_bf16x2(dK[dt][4 * rg + 2] * kLn2, dK[dt][4 * rg + 3] * kLn2);
+        v[0] = pack_bf16x2(dV[dt][4 * rg + 0], dV[dt][4 * rg + 1]);
+        v[1] = pack_bf16x2(dV[dt][4 * rg + 2], dV[dt][4 * rg + 3]);
+        *reinterpret_cast<u32x2*>(dkr + c) = a;
+        *reinterpret_cast<u32x2*>(dvr + c) = v;
+      }
+  }
+}
+
+// ---- launchers -------------------------------------------------------------------------------
+hipError_t launch_qprep(const void* q0, const void* q1, const float* a0, const float* b0,
+                        const float* a1, const float* b1, void* o0, void* o1, idx_t n, int hd,
+                        float c, hipStream_t s) {
+  QPrepParams p{{q0, q1}, {a0, a1}, {b0, b1}, {o0, o1}, n, hd, c};
+  idx_t blocks = (n / 8 + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(qprep_kernel, dim3((unsigned)blocks, 2), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_q_bf16(const BwdQParams& p, int d, hipStream_t s) {
+  int hpw = 1;
+  if (p.G % 8 == 0) hpw = 8;
+  else if (p.G % 4 == 0) hpw = 4;
+  else if (p.G % 2 == 0) hpw = 2;
+  const int bmp = kQW * (kQNW / hpw);
+  const int npb = (p.T + bmp - 1) / bmp;
+  dim3 grid((unsigned)(p.B * p.Hkv * (p.G / hpw) * npb)), block(64 * kQNW);
+#define ORTHROS_BWDQ(DD, HH) hipLaunchKernelGGL((bwd_q_kernel<DD, HH>), grid, block, 0, s, p)
+  if (d == 128) {
+    if (hpw == 8) ORTHROS_BWDQ(128, 8);
+    else if (hpw == 4) ORTHROS_BWDQ(128, 4);
+    else if (hpw == 2) ORTHROS_BWDQ(128, 2);
+    else ORTHROS_BWDQ(128, 1);
+  } else {
+    if (hpw == 8) ORTHROS_BWDQ(64, 8);
+    else if (hpw == 4) ORTHROS_BWDQ(64, 4);
+    else if (hpw == 2) ORTHROS_BWDQ(64, 2);
+    else ORTHROS_BWDQ(64, 1);
+  }
+#undef ORTHROS_BWDQ
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_kv_bf16(const BwdKVParams& p, int d, hipStream_t s) {
+  const int nkb = (p.T + kKNW * 32 - 1) / (kKNW * 32);
+  dim3 grid((unsigned)(p.B * p.Hkv * nkb)), block(64 * kKNW);
+  if (d == 128)
+    hipLaunchKernelGGL(bwd_kv_kernel<128>, grid, block, 0, s, p);
+  else
+    hipLaunchKernelGGL(bwd_kv_kernel<64>, grid, block, 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace orthros

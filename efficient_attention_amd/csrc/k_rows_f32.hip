@@ -72,6 +72,7 @@ __global__ __launch_bounds__(64) void rows_f32_kernel(RowsF32Params p) {
   }
   float* orow = p.o + (idx_t)b * p.o_sb + (idx_t)row * p.o_st + (idx_t)h * p.o_sh;
   const float inv = 1.f / l;
+  if (p.lse && lane == 0) p.lse[(idx_t)b * p.lse_sb + (idx_t)h * p.lse_sh + row] = m + logf(l);
 #pragma unroll
   for (int e = 0; e < E; ++e) orow[lane + 64 * e] = o[e] * inv;
 }

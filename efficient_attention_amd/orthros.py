@@ -18,7 +18,8 @@ __all__ = [
     "STATUS_CACHE_FULL", "STATUS_BAD_PAGE", "STAGES", "OrthrosError", "Shape", "Affine",
     "PagedKV", "lib", "library_path", "workspace_bytes", "sft_workspace_bytes",
     "make_workspace", "prefill", "prefill_chunk", "decode_step", "decode_step_paged",
-    "paged_write", "forward_pt", "forward_sft", "read_device_status", "status_string",
+    "paged_write", "forward_pt", "forward_sft", "forward_pt_lse", "backward_workspace_bytes",
+    "backward_pt", "read_device_status", "status_string",
     "timing_begin", "timing_end", "EXPORTED_SYMBOLS",
 ]
 
@@ -26,11 +27,13 @@ OK, E_INVALID, E_UNSUPPORTED, E_WORKSPACE, E_CAPACITY, E_LAUNCH = 0, -1, -2, -3,
 STATUS_CACHE_FULL = 1
 STATUS_BAD_PAGE = 2
 F32, BF16 = 0, 1
-STAGES = ("cache_write", "band", "split_rows", "merge", "append", "rows_f32")
+STAGES = ("cache_write", "band", "split_rows", "merge", "append", "rows_f32", "bwd_q", "bwd_kv",
+          "bwd_affine")
 EXPORTED_SYMBOLS = (
     "orthros_workspace_bytes", "orthros_sft_workspace_bytes", "orthros_prefill",
     "orthros_prefill_chunk", "orthros_decode_step", "orthros_decode_step_paged",
     "orthros_paged_write", "orthros_forward_pt", "orthros_forward_sft",
+    "orthros_forward_pt_lse", "orthros_backward_workspace_bytes", "orthros_backward_pt",
     "orthros_read_device_status", "orthros_status_string", "orthros_timing_begin",
     "orthros_timing_end",
 )
@@ -56,6 +59,11 @@ class _CShape(ctypes.Structure):
 class _CAffine(ctypes.Structure):
     _fields_ = [("alpha_base", ctypes.c_void_p), ("beta_base", ctypes.c_void_p),
                 ("alpha_out", ctypes.c_void_p), ("beta_out", ctypes.c_void_p)]
+
+
+class _CAffineGrad(ctypes.Structure):
+    _fields_ = [("dalpha_base", ctypes.c_void_p), ("dbeta_base", ctypes.c_void_p),
+                ("dalpha_out", ctypes.c_void_p), ("dbeta_out", ctypes.c_void_p)]
 
 
 class _CPagedKV(ctypes.Structure):
@@ -101,6 +109,15 @@ def lib() -> ctypes.CDLL:
         L.orthros_decode_step_paged.restype = ctypes.c_int
         L.orthros_paged_write.argtypes = [sp, i64, vp, vp, pp, vp, vp, sz, vp]
         L.orthros_paged_write.restype = ctypes.c_int
+        L.orthros_forward_pt_lse.argtypes = [sp, i64, vp, vp, vp, vp, ap, vp, vp, vp, vp, vp, sz,
+                                             vp]
+        L.orthros_forward_pt_lse.restype = ctypes.c_int
+        L.orthros_backward_workspace_bytes.argtypes = [sp, i64]
+        L.orthros_backward_workspace_bytes.restype = sz
+        L.orthros_backward_pt.argtypes = [sp, i64, vp, vp, vp, vp, ap, vp, vp, vp, vp, vp, vp,
+                                          vp, vp, vp, vp, ctypes.POINTER(_CAffineGrad), vp, sz,
+                                          vp]
+        L.orthros_backward_pt.restype = ctypes.c_int
         L.orthros_read_device_status.argtypes = [vp, sz, ctypes.POINTER(i32), ctypes.c_int, vp]
         L.orthros_read_device_status.restype = ctypes.c_int
         L.orthros_status_string.argtypes = [ctypes.c_int]
@@ -379,6 +396,62 @@ def forward_sft(shape: Shape, q_base, q_out, out_pos, k, v, affine: Affine, o_ba
         o_base.data_ptr(), o_out.data_ptr(), workspace.data_ptr(), workspace.numel(),
         _stream(stream))
     _rc(rc, "orthros_forward_sft")
+
+
+def forward_pt_lse(shape: Shape, q_base, q_out, k, v, affine: Affine, o_base, o_out, lse_base,
+                   lse_out, workspace, stream=None):
+    """orthros_forward_pt_lse: the pre-training forward plus per-row log-sum-exp."""
+    B, Hq, Hkv, d = shape.batch, shape.num_q_heads, shape.num_kv_heads, shape.head_dim
+    T = q_base.shape[1]
+    dev, dt = q_base.device, shape.dtype
+    _check(q_base, (B, T, Hq, d), dt, dev, "q_base")
+    _check(q_out, (B, T, Hq, d), dt, dev, "q_out")
+    _check(k, (B, T, Hkv, d), dt, dev, "k")
+    _check(v, (B, T, Hkv, d), dt, dev, "v")
+    _check(o_base, (B, T, Hq, d), dt, dev, "o_base")
+    _check(o_out, (B, T, Hq, d), dt, dev, "o_out")
+    _check(lse_base, (B, Hq, T), torch.float32, dev, "lse_base")
+    _check(lse_out, (B, Hq, T), torch.float32, dev, "lse_out")
+    aff = affine.c(Hq * d, dev)
+    rc = lib().orthros_forward_pt_lse(
+        ctypes.byref(shape.c()), T, q_base.data_ptr(), q_out.data_ptr(), k.data_ptr(),
+        v.data_ptr(), ctypes.byref(aff), o_base.data_ptr(), o_out.data_ptr(),
+        lse_base.data_ptr(), lse_out.data_ptr(), workspace.data_ptr(), workspace.numel(),
+        _stream(stream))
+    _rc(rc, "orthros_forward_pt_lse")
+
+
+def backward_workspace_bytes(shape: Shape, T: int) -> int:
+    return int(lib().orthros_backward_workspace_bytes(ctypes.byref(shape.c()), int(T)))
+
+
+def backward_pt(shape: Shape, q_base, q_out, k, v, affine: Affine, o_base, o_out, lse_base,
+                lse_out, do_base, do_out, dq_base, dq_out, dk, dv, dgrad, workspace,
+                stream=None):
+    """orthros_backward_pt. dgrad: (dalpha_base, dbeta_base, dalpha_out, dbeta_out), fp32
+    [num_q_heads * head_dim] device tensors (outputs)."""
+    B, Hq, Hkv, d = shape.batch, shape.num_q_heads, shape.num_kv_heads, shape.head_dim
+    T = q_base.shape[1]
+    dev, dt = q_base.device, shape.dtype
+    for t, n in ((q_base, "q_base"), (q_out, "q_out"), (o_base, "o_base"), (o_out, "o_out"),
+                 (do_base, "do_base"), (do_out, "do_out"), (dq_base, "dq_base"),
+                 (dq_out, "dq_out")):
+        _check(t, (B, T, Hq, d), dt, dev, n)
+    for t, n in ((k, "k"), (v, "v"), (dk, "dk"), (dv, "dv")):
+        _check(t, (B, T, Hkv, d), dt, dev, n)
+    _check(lse_base, (B, Hq, T), torch.float32, dev, "lse_base")
+    _check(lse_out, (B, Hq, T), torch.float32, dev, "lse_out")
+    for t in dgrad:
+        _check(t, (Hq * d,), torch.float32, dev, "scale-offset gradient")
+    aff = affine.c(Hq * d, dev)
+    g = _CAffineGrad(*(t.data_ptr() for t in dgrad))
+    rc = lib().orthros_backward_pt(
+        ctypes.byref(shape.c()), T, q_base.data_ptr(), q_out.data_ptr(), k.data_ptr(),
+        v.data_ptr(), ctypes.byref(aff), o_base.data_ptr(), o_out.data_ptr(),
+        lse_base.data_ptr(), lse_out.data_ptr(), do_base.data_ptr(), do_out.data_ptr(),
+        dq_base.data_ptr(), dq_out.data_ptr(), dk.data_ptr(), dv.data_ptr(), ctypes.byref(g),
+        workspace.data_ptr(), workspace.numel(), _stream(stream))
+    _rc(rc, "orthros_backward_pt")
 
 
 def read_device_status(workspace, clear: bool = False, stream=None) -> int:

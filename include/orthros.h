@@ -196,6 +196,53 @@ int orthros_prefill_chunk(const orthros_shape* shape, int64_t past_len, int64_t 
                           void* o_base, void* o_out,
                           void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Training (§3.2 Pre-Training: the loss is taken at every position, and the scale-offset
+ * vectors of §3.1 are learnable). orthros_forward_pt_lse is orthros_forward_pt (without the
+ * cache) that also returns, per row of each stream, the natural-log log-sum-exp of the row's
+ * scaled scores, lse_t = log sum_j exp(s q_t . k_j) over the row's keys:
+ *   lse_base, lse_out  fp32 [B, H_q, T] (head-major, positions contiguous). */
+int orthros_forward_pt_lse(const orthros_shape* shape, int64_t T,
+                           const void* q_base, const void* q_out, const void* k, const void* v,
+                           const orthros_affine* affine,
+                           void* o_base, void* o_out, float* lse_base, float* lse_out,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Gradients of the scale-offset vectors (device pointers, fp32 [num_q_heads * head_dim]). */
+typedef struct {
+  float* dalpha_base;
+  float* dbeta_base;
+  float* dalpha_out;
+  float* dbeta_out;
+} orthros_affine_grad;
+
+/* Bytes of workspace orthros_backward_pt needs for sequences of T tokens (0 if invalid). Its
+ * contents need no initialisation. */
+size_t orthros_backward_workspace_bytes(const orthros_shape* shape, int64_t T);
+
+/* Backward of the Pre-Training regime (both streams). Inputs are those of the forward
+ * (q_base, q_out, k, v [.., d], affine), its outputs o_base, o_out and lse_base, lse_out (from
+ * orthros_forward_pt_lse) and the loss gradients do_base, do_out [B, T, H_q, d]. Outputs:
+ *   dq_base, dq_out [B, T, H_q, d]  gradients with respect to the raw queries (before the
+ *                                   scale-offset)
+ *   dk, dv [B, T, H_kv, d]          both streams' contributions, summed over the query heads of
+ *                                   each kv head's group
+ *   dgrad                           d alpha, d beta of each stream, summed over sequences and
+ *                                   positions (host pointer to a struct of device pointers)
+ * With P the softmax weights of a row, dP = dO V^T and D = rowsum(dO (.) O), the score
+ * gradient is P (.) (dP - D); the kernels recompute P from the saved lse. bf16 calls take
+ * bf16 operands on the matrix cores with fp32 accumulation and return dq, dk, dv in bf16 (the
+ * scale-offset gradients are fp32); fp32 calls compute in fp32. Sums over rows run in a fixed
+ * order, so results are deterministic. */
+int orthros_backward_pt(const orthros_shape* shape, int64_t T,
+                        const void* q_base, const void* q_out, const void* k, const void* v,
+                        const orthros_affine* affine,
+                        const void* o_base, const void* o_out,
+                        const float* lse_base, const float* lse_out,
+                        const void* do_base, const void* do_out,
+                        void* dq_base, void* dq_out, void* dk, void* dv,
+                        const orthros_affine_grad* dgrad,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Paged key/value cache: a pool of fixed-size pages shared by the batch, as a serving engine
  * keeps it (the batched decoding that "Orthros: Phase-Aware Heterogeneous Attention for
  * Efficient Transformers" names as future work in §5). Token t of sequence b lives in page
@@ -258,7 +305,10 @@ enum {
   ORTHROS_STAGE_MERGE = 3,        /* split merge */
   ORTHROS_STAGE_APPEND = 4,       /* decode append + length update */
   ORTHROS_STAGE_ROWS_F32 = 5,     /* fp32 row kernel */
-  ORTHROS_NUM_STAGES = 6
+  ORTHROS_STAGE_BWD_Q = 6,        /* backward: query side (and the query preparation) */
+  ORTHROS_STAGE_BWD_KV = 7,       /* backward: key / value side */
+  ORTHROS_STAGE_BWD_AFFINE = 8,   /* backward: scale-offset gradients */
+  ORTHROS_NUM_STAGES = 9
 };
 int orthros_timing_begin(void);
 int orthros_timing_end(double* stage_ms, int64_t* stage_launches);

@@ -220,3 +220,17 @@ def test_decode_8b_128k_paged_equals_contiguous():
         page = table[:, t // ps]
         assert torch.equal(kp[page, :, t % ps], inp["k_new"][s])
         assert torch.equal(vp[page, :, t % ps], inp["v_new"][s])
+
+
+def test_pt_1p3b_2k_training_fullsize():
+    """Pre-training forward (with lse) and backward at the 1.3B shape (4 x 2048 tokens, 16 heads,
+    d 128, window 512) in the launch configuration the benchmark times; every element of every
+    gradient against the float64 oracle on the same inputs (drawn on the device)."""
+    from tests.test_gpu_training import check_against_oracle, run_training
+    wl = syn.WORKLOADS["pt_1p3b_2k"]
+    _say("full-size training", wl)
+    inp, do_b, do_o, got = run_training(wl, device=DEV)
+    inp = {n: (t.cpu() if isinstance(t, torch.Tensor) else
+               tuple(a.cpu() for a in t) if isinstance(t, tuple) else t) for n, t in inp.items()}
+    worst = check_against_oracle(wl, inp, do_b.cpu(), do_o.cpu(), got)
+    _say("pt_1p3b_2k training: " + " ".join(f"{n} {m[1]:.2e}" for n, m in worst.items()))
