@@ -246,6 +246,53 @@ def bench_sft(wl, R, steps, warmup, dev):
     return dict(ms=ms, flops=flops, band_ms=band_ms / max(steps, 1))
 
 
+def bench_training(wl, steps, warmup, dev):
+    """Pre-training regime, one training step of the attention: forward with lse + backward."""
+    inp = syn.make_pt(wl, device=dev)
+    B, T, Hq, d = inp["q_base"].shape
+    Hkv = inp["k"].shape[2]
+    shape = ox.Shape(B, Hq, Hkv, d, wl.window, torch.bfloat16, T)
+    aff = ox.Affine(*inp["affine"])
+    g = torch.Generator(device=dev)
+    g.manual_seed(wl.seed + 101)
+    do_b = torch.randn(B, T, Hq, d, generator=g, device=dev).to(torch.bfloat16)
+    do_o = torch.randn(B, T, Hq, d, generator=g, device=dev).to(torch.bfloat16)
+    ob = torch.empty(B, T, Hq, d, dtype=torch.bfloat16, device=dev)
+    oo = torch.empty_like(ob)
+    lb = torch.empty(B, Hq, T, dtype=torch.float32, device=dev)
+    lo = torch.empty_like(lb)
+    ws = ox.make_workspace(shape, dev)
+    bws = torch.empty(ox.backward_workspace_bytes(shape, T), dtype=torch.uint8, device=dev)
+    dqb, dqo = torch.empty_like(ob), torch.empty_like(ob)
+    dk, dv = torch.empty_like(inp["k"]), torch.empty_like(inp["v"])
+    dg = [torch.empty(Hq * d, dtype=torch.float32, device=dev) for _ in range(4)]
+
+    def step():
+        ox.forward_pt_lse(shape, inp["q_base"], inp["q_out"], inp["k"], inp["v"], aff, ob, oo,
+                          lb, lo, ws)
+        ox.backward_pt(shape, inp["q_base"], inp["q_out"], inp["k"], inp["v"], aff, ob, oo, lb,
+                       lo, do_b, do_o, dqb, dqo, dk, dv, dg, bws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ox.timing_begin()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    stages = ox.timing_end()
+    pairs = B * Hq * (swa_pairs(T, wl.window) + T * (T + 1) // 2)
+    fwd_flops = 4.0 * d * pairs
+    bwd_flops = 10.0 * d * pairs  # five products per (query, key) pair
+    per = {k: v[0] / max(steps, 1) for k, v in stages.items() if v[1]}
+    bwd_ms = per.get("bwd_q", 0) + per.get("bwd_kv", 0) + per.get("bwd_affine", 0)
+    log(f"training {wl.name}: {ms:.3f} ms/step; stages {per}")
+    return dict(ms=ms, per=per, fwd_flops=fwd_flops, bwd_flops=bwd_flops, bwd_ms=bwd_ms,
+                pairs=pairs, d=d)
+
+
 def bench_prefill_chunked(wl, chunk, steps, warmup, dev, inp):
     """The same prompt prefilled in chunks of `chunk` tokens (cache grows chunk by chunk)."""
     B, P, Hq, d = inp["q_base"].shape
@@ -427,6 +474,26 @@ def main():
                          "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
                          "frac": round(sf["flops"] / (sf["band_ms"] / 1e3) / PEAK_BF16_FLOPS, 4),
                          "kernel": "band_kernel (both launches)"},
+        }
+    if not args.skip_regimes:
+        tw = syn.WORKLOADS["pt_1p3b_2k"]
+        tr = bench_training(tw, args.steps, args.warmup, dev)
+        per = tr["per"]
+        ach = tr["bwd_flops"] / (tr["bwd_ms"] / 1e3)
+        rec["training"] = {
+            "workload": f"{tw.name}: forward with log-sum-exp + backward, both streams",
+            "ms_per_step": round(tr["ms"], 4),
+            "tokens_per_s": round(tw.batch * tw.length / (tr["ms"] / 1e3), 1),
+            "forward_ms": round(per.get("band", 0), 4), "backward_ms": round(tr["bwd_ms"], 4),
+            "stage_ms_per_step": {k: round(v, 4) for k, v in per.items()},
+            "roofline": {"bound": "mfma", "achieved": round(ach / 1e12, 2),
+                         "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
+                         "frac": round(ach / PEAK_BF16_FLOPS, 4),
+                         "kernel": "backward (bwd_q + bwd_kv + scale-offset), 10 d FLOP per pair",
+                         "flops_per_step": tr["bwd_flops"]},
+            "kernel_tflops": {
+                "bwd_q": round(6.0 * tr["d"] * tr["pairs"] / (per.get("bwd_q", 1) / 1e3) / 1e12, 1),
+                "bwd_kv": round(8.0 * tr["d"] * tr["pairs"] / (per.get("bwd_kv", 1) / 1e3) / 1e12, 1)},
         }
     if not args.skip_cpu:
         rec["cpu_baseline"] = cpu_baseline(pf["inp"], wl)

@@ -238,7 +238,7 @@ BwdLayout bwd_layout(const orthros_shape* s, int64_t T) {
   const size_t rows = (size_t)s->batch * (size_t)T;
   const size_t n = (size_t)s->num_q_heads * s->head_dim;
   BwdLayout L;
-  L.chunk_rows = 64;
+  L.chunk_rows = 32;
   L.nchunk = (int)((rows + L.chunk_rows - 1) / L.chunk_rows);
   size_t off = kStatusBytes;
   const size_t qpb = s->dtype == ORTHROS_BF16 ? up(rows * n * 2) : 0;

@@ -283,7 +283,7 @@ __global__ __launch_bounds__(64 * kQNW) void bwd_q_kernel(BwdQParams p) {
 // The keys' fragments stay in registers, their values in LDS; 32-row query tiles (q', dO,
 // lse, D) of both streams and every head of the group go through a two-slot LDS ring.
 template <int D>
-__global__ __launch_bounds__(64 * kKNW) void bwd_kv_kernel(BwdKVParams p) {
+__global__ __launch_bounds__(64 * kKNW, 2) void bwd_kv_kernel(BwdKVParams p) {
   constexpr int NCH = D / 8, ROWB = D * 2, NKS = D / 16, NDT = D / 32;
   constexpr int KB = kKNW * 32;                  // keys per work-group
   constexpr int VBYTES = KB * ROWB;              // value block

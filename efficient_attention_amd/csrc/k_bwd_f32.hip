@@ -139,42 +139,60 @@ __global__ __launch_bounds__(64) void bwd_kv_f32_kernel(BwdKVParams p) {
 }
 
 // dq_raw = alpha (.) dq for every row, and per chunk of rows the partial sums of dq (.) q_raw
-// and dq per column; then the partials are added in chunk order.
+// and dq per column; then the partials are added in chunk order. Each thread owns 4 adjacent
+// columns (16-byte loads) and keeps several rows' loads in flight.
 __global__ __launch_bounds__(256) void affine_grad_partial_kernel(AffineGradParams p) {
-  const int c = blockIdx.y * 256 + threadIdx.x;
+  const int c = (blockIdx.y * 256 + threadIdx.x) * 4;
   if (c >= p.n) return;
   const int r0 = blockIdx.x * p.chunk_rows;
   const int r1 = r0 + p.chunk_rows < p.rows ? r0 + p.chunk_rows : p.rows;
-  const float a = p.alpha[c];
-  float sa = 0.f, sb = 0.f;
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p.alpha + c);
+  const float* __restrict__ dq = p.dq;
+  f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
   for (int r = r0; r < r1; ++r) {
     const idx_t i = (idx_t)r * p.n + c;
-    const float x = p.dq[i];
-    float qr;
+    const f32x4 x = *reinterpret_cast<const f32x4*>(dq + i);
+    f32x4 qr;
     if (p.bf16) {
-      qr = bf16_to_f32(static_cast<const uint16_t*>(p.q)[i]);
-      static_cast<uint16_t*>(p.dq_raw)[i] = f32_to_bf16(a * x);
+      const u32x2 w = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.q) + i);
+      qr = f32x4{bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1])};
+      u32x2 o;
+      o[0] = pack_bf16x2(a[0] * x[0], a[1] * x[1]);
+      o[1] = pack_bf16x2(a[2] * x[2], a[3] * x[3]);
+      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.dq_raw) + i) = o;
     } else {
-      qr = static_cast<const float*>(p.q)[i];
-      static_cast<float*>(p.dq_raw)[i] = a * x;
+      qr = *reinterpret_cast<const f32x4*>(static_cast<const float*>(p.q) + i);
+      *reinterpret_cast<f32x4*>(static_cast<float*>(p.dq_raw) + i) = a * x;
     }
     sa += x * qr;
     sb += x;
   }
-  p.part[((idx_t)blockIdx.x * 2 + 0) * p.n + c] = sa;
-  p.part[((idx_t)blockIdx.x * 2 + 1) * p.n + c] = sb;
+  *reinterpret_cast<f32x4*>(p.part + ((idx_t)blockIdx.x * 2 + 0) * p.n + c) = sa;
+  *reinterpret_cast<f32x4*>(p.part + ((idx_t)blockIdx.x * 2 + 1) * p.n + c) = sb;
 }
 
+// Sum of the chunk partials, per column: 4 slices of 64 threads each add every fourth chunk
+// (loads unrolled so several are in flight), then the slices combine in a fixed order.
 __global__ __launch_bounds__(256) void affine_grad_final_kernel(AffineGradParams p) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  if (c >= p.n) return;
+  __shared__ float red[2][4][64];
+  const int cl = threadIdx.x & 63, sl = threadIdx.x >> 6;
+  const int c = blockIdx.x * 64 + cl;
   float sa = 0.f, sb = 0.f;
-  for (int k = 0; k < p.nchunk; ++k) {
-    sa += p.part[((idx_t)k * 2 + 0) * p.n + c];
-    sb += p.part[((idx_t)k * 2 + 1) * p.n + c];
+  if (c < p.n) {
+#pragma unroll 8
+    for (int k = sl; k < p.nchunk; k += 4) {
+      sa += p.part[((idx_t)k * 2 + 0) * p.n + c];
+      sb += p.part[((idx_t)k * 2 + 1) * p.n + c];
+    }
   }
-  p.dalpha[c] = sa;
-  p.dbeta[c] = sb;
+  red[0][sl][cl] = sa;
+  red[1][sl][cl] = sb;
+  __syncthreads();
+  if (sl == 0 && c < p.n) {
+    p.dalpha[c] = (red[0][0][cl] + red[0][1][cl]) + (red[0][2][cl] + red[0][3][cl]);
+    p.dbeta[c] = (red[1][0][cl] + red[1][1][cl]) + (red[1][2][cl] + red[1][3][cl]);
+  }
 }
 
 hipError_t launch_bwd_q_f32(const BwdQParams& p, int d, hipStream_t s) {
@@ -196,11 +214,11 @@ hipError_t launch_bwd_kv_f32(const BwdKVParams& p, int d, hipStream_t s) {
 }
 
 hipError_t launch_affine_grad(const AffineGradParams& p, hipStream_t s) {
-  const unsigned cb = (unsigned)((p.n + 255) / 256);
-  hipLaunchKernelGGL(affine_grad_partial_kernel, dim3((unsigned)p.nchunk, cb), dim3(256), 0, s, p);
+  const unsigned cb4 = (unsigned)((p.n / 4 + 255) / 256);
+  hipLaunchKernelGGL(affine_grad_partial_kernel, dim3((unsigned)p.nchunk, cb4), dim3(256), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(affine_grad_final_kernel, dim3(cb), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(affine_grad_final_kernel, dim3((unsigned)((p.n + 63) / 64)), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
