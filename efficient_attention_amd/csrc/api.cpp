@@ -9,6 +9,7 @@
 #include <vector>
 
 #include "launch.h"
+#include "launch_bwd.h"
 
 using namespace orthros;
 

@@ -22,6 +22,7 @@
 // forward.
 #include "common.h"
 #include "launch.h"
+#include "launch_bwd.h"
 #include "lds_mfma.h"
 
 namespace orthros {

@@ -12,6 +12,7 @@
 // dv); the bf16 path has matrix-core kernels and shares the reduction.
 #include "common.h"
 #include "launch.h"
+#include "launch_bwd.h"
 
 namespace orthros {
 

@@ -173,53 +173,6 @@ struct RowsF32Params {
   float scale;
 };
 
-// Training backward of one stream's rows (pre-training regime): row t of [B, T, Hq, d] attends
-// keys lo(t) .. t with lo(t) = max(0, t - window + 1) of k, v [B, T, Hkv, d].
-struct BwdQParams {
-  const void* q;           // raw queries of the stream
-  const float* alpha;      // the stream's scale-offset [Hq d]
-  const float* beta;
-  const void* k;
-  const void* v;
-  const void* o;           // forward output of the stream
-  const void* dout;        // its gradient
-  const float* lse;        // [B, Hq, T] natural-log log-sum-exp of the forward rows
-  float* D;                // out: [B, Hq, T] rowsum(dout * o)
-  float* dq;               // out: [B, T, Hq, d] fp32 gradient of the post-affine query
-  int B, T, Hq, Hkv, G, window;
-  float scale;
-};
-
-// Key-side backward: dk, dv [B, T, Hkv, d] from both streams' rows (index 0 base, 1 output).
-struct BwdKVParams {
-  const void* q[2];
-  const float* alpha[2];
-  const float* beta[2];
-  const void* dout[2];
-  const float* lse[2];
-  const float* D[2];
-  int window[2];
-  const void* k;
-  const void* v;
-  void* dk;
-  void* dv;
-  int B, T, Hq, Hkv, G;
-  float scale;
-};
-
-// Query-side scale-offset gradient of one stream: dq_raw = alpha (.) dq, and the sums over
-// all rows of dq (.) q_raw (d alpha) and dq (d beta), in a fixed order (two passes).
-struct AffineGradParams {
-  const float* dq;         // [rows, n] fp32 post-affine gradient
-  const void* q;           // [rows, n] raw queries
-  const float* alpha;      // [n]
-  void* dq_raw;            // out: [rows, n] in the call's dtype
-  float* part;             // [nchunk][2][n] partial sums
-  float* dalpha;           // out: [n]
-  float* dbeta;            // out: [n]
-  int rows, n, chunk_rows, nchunk, bf16;
-};
-
 hipError_t launch_cache_write(const CacheWriteParams& p, hipStream_t s);
 hipError_t launch_append(const AppendParams& p, hipStream_t s);
 hipError_t launch_paged_write(const PagedWriteParams& p, hipStream_t s);
@@ -227,13 +180,5 @@ hipError_t launch_split_rows(const SplitParams& p, int d, hipStream_t s);
 hipError_t launch_merge(const MergeParams& p, hipStream_t s);
 hipError_t launch_band(const BandParams& p, int d, hipStream_t s);
 hipError_t launch_rows_f32(const RowsF32Params& p, hipStream_t s);
-hipError_t launch_bwd_q_f32(const BwdQParams& p, int d, hipStream_t s);
-hipError_t launch_bwd_kv_f32(const BwdKVParams& p, int d, hipStream_t s);
-hipError_t launch_bwd_q_bf16(const BwdQParams& p, int d, hipStream_t s);
-hipError_t launch_bwd_kv_bf16(const BwdKVParams& p, int d, hipStream_t s);
-hipError_t launch_affine_grad(const AffineGradParams& p, hipStream_t s);
-hipError_t launch_qprep(const void* q0, const void* q1, const float* a0, const float* b0,
-                        const float* a1, const float* b1, void* o0, void* o1, idx_t n, int hd,
-                        float c, hipStream_t s);
 
 }  // namespace orthros
