@@ -50,15 +50,17 @@ CSRC = os.path.join(ROOT, "efficient_attention_amd", "csrc")
 # in the same run. Recorded with the sha256 of the kernel's sources: when they change, the
 # figure no longer describes the kernel and `traffic` is reported as null.
 TRAFFIC = {
-    "band_kernel": {"sha": "06973e7d56491b46", "bytes_per_launch": 2.7852e+09},
-    "split_rows_kernel": {"sha": "e085bb09a032e91f", "bytes_per_launch": 8.5975e+09},
+    "band_kernel": {"sha": "815165b5561f0ce5", "bytes_per_launch": 2.7554e+09},
+    "split_rows_kernel": {"sha": "9894888fdb3c3a5b", "bytes_per_launch": 8.5975e+09},
+    "split_rows_kernel_paged": {"sha": "9894888fdb3c3a5b", "bytes_per_launch": 8.5979e+09},
 }
 
 
 def kernel_sources_sha(kernel: str) -> str:
     import hashlib
     files = {"band_kernel": ["k_band.hip", "lds_mfma.h"],
-             "split_rows_kernel": ["k_split.hip"]}[kernel]
+             "split_rows_kernel": ["k_split.hip"],
+             "split_rows_kernel_paged": ["k_split.hip"]}[kernel]
     h = hashlib.sha256()
     for f in files + ["common.h", "launch.h"]:
         with open(os.path.join(CSRC, f), "rb") as fh:
@@ -451,6 +453,7 @@ def main():
             "roofline": {"bound": "hbm", "achieved": round(ach / 1e9, 1),
                          "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
                          "frac": round(ach / PEAK_HBM_BYTES, 4),
+                         "traffic": traffic_for("split_rows_kernel_paged"),
                          "kernel": "split_rows_kernel (paged)",
                          "launch_us": round(dp["split_s"] * 1e6, 2),
                          "bytes_per_launch": dp["split_bytes"]},
