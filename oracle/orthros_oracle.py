@@ -63,6 +63,8 @@ __all__ = [
     "decode_step_paged",
     "lse_pt",
     "backward_pt",
+    "lse_sft",
+    "backward_sft",
 ]
 
 
@@ -372,21 +374,28 @@ def lse_pt(q_base, q_out, k, alpha_b, beta_b, alpha_o, beta_o, window, scale=Non
     return out[0], out[1]
 
 
-def _stream_backward(q_raw, a, bt, K, V, dO, window, s):
+def _row_ranges(positions, window):
+    """Key range [lo, t] of rows at the given positions (window None: Eq. 5, all keys <= t)."""
+    return [(0 if window is None else max(0, int(t) - window + 1), int(t)) for t in positions]
+
+
+def _stream_backward(q_raw, a, bt, K, V, dO, window, s, positions=None):
     """Backward of one stream for one (sequence, query head).
 
-    q_raw [T, d] raw queries with their scale-offset a, bt [d]; K, V [T, d] of the kv head;
-    dO [T, d] the gradient of the loss with respect to the stream's outputs. With
+    q_raw [R, d] raw queries with their scale-offset a, bt [d] (R = T rows at positions
+    0 .. T-1, or the rows at ``positions``); K, V [T, d] of the kv head; dO [R, d] the gradient
+    of the loss with respect to the stream's outputs. With
     q = a (.) q_raw + bt, P the row-softmax weights of s q K^T over each row's keys and
     O = P V: dV = P^T dO; dP = dO V^T; the softmax Jacobian gives
     dZ_tj = P_tj (dP_tj - sum_m P_tm dP_tm); dq = s dZ K; dK = s dZ^T q; and through the
     scale-offset dq_raw = a (.) dq, da = sum_t dq (.) q_raw, db = sum_t dq.
     """
     q = a * q_raw + bt
-    T = q.shape[0]
-    P = np.zeros((T, T))
-    for t, (lo, hi) in enumerate(_stream_rows(T, window)):
-        P[t, lo:hi + 1] = attention_weights(q[t], K[lo:hi + 1], s)
+    T = K.shape[0]
+    ranges = _stream_rows(T, window) if positions is None else _row_ranges(positions, window)
+    P = np.zeros((len(ranges), T))
+    for r, (lo, hi) in enumerate(ranges):
+        P[r, lo:hi + 1] = attention_weights(q[r], K[lo:hi + 1], s)
     dV = P.T @ dO
     dP = dO @ V.T
     dZ = P * (dP - np.sum(P * dP, axis=1, keepdims=True))
@@ -426,6 +435,72 @@ def backward_pt(q_base, q_out, k, v, alpha_b, beta_b, alpha_o, beta_o, do_base, 
                 g = _kv_head(h, hq, hkv)
                 dqr, dah, dbh, dK, dV = _stream_backward(q_raw[b, :, h], A[h], Bt[h], k[b, :, g],
                                                          v[b, :, g], dO[b, :, h], w, s)
+                dq_all[b, :, h] = dqr
+                da[h] += dah
+                db[h] += dbh
+                res["dk"][b, :, g] += dK
+                res["dv"][b, :, g] += dV
+        res["dalpha_" + name] = da.reshape(-1)
+        res["dbeta_" + name] = db.reshape(-1)
+    return res
+
+
+def lse_sft(q_base, q_out, k, out_positions, alpha_b, beta_b, alpha_o, beta_o, window,
+            scale=None):
+    """Per-row log-sum-exp of the Supervised Fine-Tuning regime (§3.2): base rows at every
+    position ([B, H_q, T], Eq. 4 ranges) and output rows at the response positions
+    ([B, H_q, R], Eq. 5 ranges, in the order of ``out_positions``)."""
+    k = _f64(k)
+    B, T, hq, d = np.shape(q_base)
+    hkv = k.shape[2]
+    s = default_scale(d) if scale is None else scale
+    out = []
+    for q_raw, a, bt, ranges in ((q_base, alpha_b, beta_b, _stream_rows(T, window)),
+                                 (q_out, alpha_o, beta_o, _row_ranges(out_positions, None))):
+        q = scale_offset(q_raw, a, bt)
+        lse = np.empty((B, hq, len(ranges)))
+        for b in range(B):
+            for h in range(hq):
+                g = _kv_head(h, hq, hkv)
+                for r, (lo, hi) in enumerate(ranges):
+                    z = s * (k[b, lo:hi + 1, g] @ q[b, r, h])
+                    m = z.max()
+                    lse[b, h, r] = m + np.log(np.exp(z - m).sum())
+        out.append(lse)
+    return out[0], out[1]
+
+
+def backward_sft(q_base, q_out, k, v, out_positions, alpha_b, beta_b, alpha_o, beta_o, do_base,
+                 do_out, window, scale=None):
+    """Gradients of the Supervised Fine-Tuning regime (§3.2): base rows at every position
+    (Eq. 4), output rows only at ``out_positions`` (Eq. 5) with q_out, do_out [B, R, H_q, d].
+
+    Same quantities as ``backward_pt`` (dq_out is [B, R, H_q, d]); with every position listed
+    in order it is ``backward_pt``.
+    """
+    k = _f64(k)
+    v = _f64(v)
+    B, T, hq, d = np.shape(q_base)
+    R = np.shape(q_out)[1]
+    hkv = k.shape[2]
+    s = default_scale(d) if scale is None else scale
+    res = dict(dq_base=np.zeros((B, T, hq, d)), dq_out=np.zeros((B, R, hq, d)),
+               dk=np.zeros((B, T, hkv, d)), dv=np.zeros((B, T, hkv, d)))
+    for name, q_raw, a, bt, dO, w, pos in (
+            ("b", q_base, alpha_b, beta_b, do_base, window, None),
+            ("o", q_out, alpha_o, beta_o, do_out, None, out_positions)):
+        q_raw = _f64(q_raw)
+        dO = _f64(dO)
+        A = _f64(a).reshape(hq, d)
+        Bt = _f64(bt).reshape(hq, d)
+        da = np.zeros((hq, d))
+        db = np.zeros((hq, d))
+        dq_all = res["dq_base" if name == "b" else "dq_out"]
+        for b in range(B):
+            for h in range(hq):
+                g = _kv_head(h, hq, hkv)
+                dqr, dah, dbh, dK, dV = _stream_backward(q_raw[b, :, h], A[h], Bt[h], k[b, :, g],
+                                                         v[b, :, g], dO[b, :, h], w, s, pos)
                 dq_all[b, :, h] = dqr
                 da[h] += dah
                 db[h] += dbh

@@ -506,3 +506,53 @@ def test_lse_matches_library_logsumexp():
     # a row with one key (t = 0) has lse equal to its only score
     q0 = x["alpha_b"].reshape(Hq, d) * x["q_base"][0, 0] + x["beta_b"].reshape(Hq, d)
     np.testing.assert_allclose(lb[0, 0, 0], s * q0[0] @ x["k"][0, 0, 0], rtol=1e-12)
+
+
+def _sft_loss(x, g, pos, w):
+    ob, oo = oracle.forward_sft(x["q_base"], x["q_out"], x["k"], x["v"], pos, x["alpha_b"],
+                                x["beta_b"], x["alpha_o"], x["beta_o"], window=w)
+    return float(np.sum(ob * g["do_base"]) + np.sum(oo * g["do_out"]))
+
+
+@pytest.mark.parametrize("pos,w", [([7, 2, 5], 3), ([0], 2), ([4, 4, 7, 1], 8)])
+def test_sft_backward_matches_central_differences(pos, w):
+    """SFT gradients (response rows in any order, repeats allowed) against central differences
+    of the separately pinned SFT forward."""
+    x, g = _train_case(B=1, T=8, Hq=2, Hkv=1, d=4, seed=30 + w)
+    r = np.random.default_rng(31)
+    R = len(pos)
+    x["q_out"] = r.standard_normal((1, R, 2, 4))
+    g["do_out"] = r.standard_normal((1, R, 2, 4))
+    grads = oracle.backward_sft(x["q_base"], x["q_out"], x["k"], x["v"], pos, x["alpha_b"],
+                                x["beta_b"], x["alpha_o"], x["beta_o"], g["do_base"],
+                                g["do_out"], window=w)
+    h = 1e-5
+    for name, gname in _GRAD_OF.items():
+        arr = x[name]
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            keep = arr[idx]
+            arr[idx] = keep + h
+            lp = _sft_loss(x, g, pos, w)
+            arr[idx] = keep - h
+            lm = _sft_loss(x, g, pos, w)
+            arr[idx] = keep
+            num[idx] = (lp - lm) / (2 * h)
+        np.testing.assert_allclose(grads[gname], num, rtol=1e-6, atol=1e-7, err_msg=gname)
+
+
+def test_sft_backward_with_every_position_is_pt_backward():
+    x, g = _train_case(B=2, T=12, Hq=4, Hkv=2, d=4, seed=8)
+    T = 12
+    a = oracle.backward_sft(x["q_base"], x["q_out"], x["k"], x["v"], list(range(T)), x["alpha_b"],
+                            x["beta_b"], x["alpha_o"], x["beta_o"], g["do_base"], g["do_out"],
+                            window=5)
+    b = oracle.backward_pt(x["q_base"], x["q_out"], x["k"], x["v"], x["alpha_b"], x["beta_b"],
+                           x["alpha_o"], x["beta_o"], g["do_base"], g["do_out"], window=5)
+    for n in a:
+        np.testing.assert_array_equal(a[n], b[n], err_msg=n)
+    la = oracle.lse_sft(x["q_base"], x["q_out"], x["k"], list(range(T)), x["alpha_b"],
+                        x["beta_b"], x["alpha_o"], x["beta_o"], window=5)
+    lb = oracle.lse_pt(x["q_base"], x["q_out"], x["k"], x["alpha_b"], x["beta_b"], x["alpha_o"],
+                       x["beta_o"], window=5)
+    np.testing.assert_array_equal(la[1], lb[1])
