@@ -234,18 +234,22 @@ struct BwdLayout {
   size_t qp[2], D[2], dq[2], part, total;
   int chunk_rows, nchunk;
 };
-BwdLayout bwd_layout(const orthros_shape* s, int64_t T) {
+// R: rows of the output stream (T for pre-training, the response rows for fine-tuning).
+BwdLayout bwd_layout(const orthros_shape* s, int64_t T, int64_t R) {
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
-  const size_t rows = (size_t)s->batch * (size_t)T;
+  const size_t rows[2] = {(size_t)s->batch * (size_t)T, (size_t)s->batch * (size_t)R};
   const size_t n = (size_t)s->num_q_heads * s->head_dim;
   BwdLayout L;
   L.chunk_rows = 32;
-  L.nchunk = (int)((rows + L.chunk_rows - 1) / L.chunk_rows);
+  const size_t rmax = rows[0] > rows[1] ? rows[0] : rows[1];
+  L.nchunk = (int)((rmax + L.chunk_rows - 1) / L.chunk_rows);
   size_t off = kStatusBytes;
-  const size_t qpb = s->dtype == ORTHROS_BF16 ? up(rows * n * 2) : 0;
-  for (int i = 0; i < 2; ++i) { L.qp[i] = off; off += qpb; }
-  for (int i = 0; i < 2; ++i) { L.D[i] = off; off += up((size_t)s->batch * s->num_q_heads * T * 4); }
-  for (int i = 0; i < 2; ++i) { L.dq[i] = off; off += up(rows * n * 4); }
+  for (int i = 0; i < 2; ++i) {
+    L.qp[i] = off;
+    off += s->dtype == ORTHROS_BF16 ? up(rows[i] * n * 2) : 0;
+  }
+  for (int i = 0; i < 2; ++i) { L.D[i] = off; off += up(rows[i] * s->num_q_heads * 4); }
+  for (int i = 0; i < 2; ++i) { L.dq[i] = off; off += up(rows[i] * n * 4); }
   L.part = off;
   off += up((size_t)L.nchunk * 2 * n * 4);
   L.total = off;
@@ -318,6 +322,206 @@ int forward_pt_impl(const orthros_shape* s, int64_t T, const void* q_base, const
   return launch_rc(run_stage(ORTHROS_STAGE_BAND, st, [&] { return launch_band(op, d, st); }));
 }
 
+
+// Backward of pre-training (out_pos == nullptr, R == T) or fine-tuning (R response rows at
+// out_pos).
+int backward_impl(const orthros_shape* s, int64_t T, const void* q_base, const void* q_out,
+                  const int32_t* out_pos, int64_t R, const void* k, const void* v,
+                  const orthros_affine* aff, const void* o_base, const void* o_out,
+                  const float* lse_base, const float* lse_out, const void* do_base,
+                  const void* do_out, void* dq_base, void* dq_out, void* dk, void* dv,
+                  const orthros_affine_grad* dg, void* ws, size_t ws_bytes, hipStream_t st) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if (T < 1 || T > INT_MAX / 2 || R < 1 || R > INT_MAX / 2) return ORTHROS_E_INVALID;
+  if (out_pos && ((uintptr_t)out_pos & 3u)) return ORTHROS_E_INVALID;
+  if ((rc = check_affine(aff))) return rc;
+  if ((rc = check_ptrs({q_base, q_out, k, v, o_base, o_out, lse_base, lse_out, do_base, do_out,
+                        dq_base, dq_out, dk, dv}))) return rc;
+  if (!dg || check_ptrs({dg->dalpha_base, dg->dbeta_base, dg->dalpha_out, dg->dbeta_out}))
+    return ORTHROS_E_INVALID;
+  if (!ws || !aligned16(ws)) return ORTHROS_E_WORKSPACE;
+  const BwdLayout L = bwd_layout(s, T, R);
+  if (ws_bytes < L.total) return ORTHROS_E_WORKSPACE;
+
+  const int B = s->batch, Hq = s->num_q_heads, Hkv = s->num_kv_heads, d = s->head_dim;
+  const int G = Hq / Hkv;
+  const float scale = scale_of(s);
+  char* w = static_cast<char*>(ws);
+  const bool bf = s->dtype == ORTHROS_BF16;
+  const int wb = s->window < (int)T ? s->window : (int)T;
+
+  const void* qs[2] = {q_base, q_out};
+  const float* al[2] = {aff->alpha_base, aff->alpha_out};
+  const float* be[2] = {aff->beta_base, aff->beta_out};
+  const void* os[2] = {o_base, o_out};
+  const void* dos[2] = {do_base, do_out};
+  const float* lses[2] = {lse_base, lse_out};
+  float* Ds[2] = {reinterpret_cast<float*>(w + L.D[0]), reinterpret_cast<float*>(w + L.D[1])};
+  float* dqs[2] = {reinterpret_cast<float*>(w + L.dq[0]), reinterpret_cast<float*>(w + L.dq[1])};
+  void* qps[2] = {w + L.qp[0], w + L.qp[1]};
+  const int wins[2] = {wb, (int)T};
+  const int nrows[2] = {(int)T, (int)R};
+  const int32_t* poss[2] = {nullptr, out_pos};
+  if (bf) {
+    for (int i = 0; i < 2; ++i) {
+      rc = launch_rc(run_stage(ORTHROS_STAGE_BWD_Q, st, [&] {
+        return launch_qprep(qs[i], qs[i], al[i], be[i], al[i], be[i], qps[i], qps[i],
+                            (idx_t)B * nrows[i] * Hq * d, Hq * d, scale * kLog2e, st, 1);
+      }));
+      if (rc) return rc;
+    }
+  }
+  for (int i = 0; i < 2; ++i) {
+    BwdQParams q{};
+    q.q = bf ? qps[i] : qs[i];
+    q.alpha = al[i]; q.beta = be[i];
+    q.k = k; q.v = v; q.o = os[i]; q.dout = dos[i]; q.lse = lses[i];
+    q.D = Ds[i]; q.dq = dqs[i];
+    q.pos = poss[i]; q.nrows = nrows[i];
+    q.B = B; q.T = (int)T; q.Hq = Hq; q.Hkv = Hkv; q.G = G; q.window = wins[i]; q.scale = scale;
+    rc = launch_rc(run_stage(ORTHROS_STAGE_BWD_Q, st, [&] {
+      return bf ? launch_bwd_q_bf16(q, d, st) : launch_bwd_q_f32(q, d, st);
+    }));
+    if (rc) return rc;
+  }
+  BwdKVParams kv{};
+  for (int i = 0; i < 2; ++i) {
+    kv.q[i] = bf ? qps[i] : qs[i];
+    kv.alpha[i] = al[i]; kv.beta[i] = be[i];
+    kv.dout[i] = dos[i]; kv.lse[i] = lses[i]; kv.D[i] = Ds[i]; kv.window[i] = wins[i];
+    kv.pos[i] = poss[i]; kv.nrows[i] = nrows[i];
+  }
+  kv.k = k; kv.v = v; kv.dk = dk; kv.dv = dv;
+  kv.B = B; kv.T = (int)T; kv.Hq = Hq; kv.Hkv = Hkv; kv.G = G; kv.scale = scale;
+  rc = launch_rc(run_stage(ORTHROS_STAGE_BWD_KV, st, [&] {
+    return bf ? launch_bwd_kv_bf16(kv, d, st) : launch_bwd_kv_f32(kv, d, st);
+  }));
+  if (rc) return rc;
+  void* dqo[2] = {dq_base, dq_out};
+  float* da[2] = {dg->dalpha_base, dg->dalpha_out};
+  float* db[2] = {dg->dbeta_base, dg->dbeta_out};
+  for (int i = 0; i < 2; ++i) {
+    AffineGradParams ag{};
+    ag.dq = dqs[i]; ag.q = qs[i]; ag.alpha = al[i]; ag.dq_raw = dqo[i];
+    ag.part = reinterpret_cast<float*>(w + L.part);
+    ag.dalpha = da[i]; ag.dbeta = db[i];
+    ag.rows = B * nrows[i]; ag.n = Hq * d; ag.chunk_rows = L.chunk_rows; ag.nchunk = L.nchunk;
+    ag.bf16 = bf ? 1 : 0;
+    rc = launch_rc(run_stage(ORTHROS_STAGE_BWD_AFFINE, st, [&] { return launch_affine_grad(ag, st); }));
+    if (rc) return rc;
+  }
+  return ORTHROS_OK;
+}
+
+// Fine-tuning forward; with lse_b / lse_o set it also writes the rows' log-sum-exp.
+int forward_sft_impl(const orthros_shape* s, int64_t T, const void* q_base, const void* q_out,
+                     const int32_t* out_pos, int64_t R, const void* k, const void* v,
+                     const orthros_affine* aff, void* cache_k, void* cache_v,
+                     int32_t* cache_len, void* o_base, void* o_out, float* lse_b, float* lse_o,
+                     void* ws, size_t ws_bytes, hipStream_t st) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if (T < 1 || T > INT_MAX / 2 || R < 1 || R > INT_MAX / 2) return ORTHROS_E_INVALID;
+  if ((rc = check_affine(aff))) return rc;
+  if ((rc = check_ptrs({q_base, q_out, k, v, o_base, o_out}))) return rc;
+  if (!out_pos || ((uintptr_t)out_pos & 3u)) return ORTHROS_E_INVALID;
+  const bool any_cache = cache_k || cache_v || cache_len;
+  if (any_cache && (rc = check_ptrs({cache_k, cache_v, cache_len}))) return rc;
+  if ((rc = check_ws(s, ws, ws_bytes, sft_rows_per_head(R)))) return rc;
+  if (any_cache && T > s->capacity) return ORTHROS_E_CAPACITY;
+
+  const int B = s->batch, Hq = s->num_q_heads, Hkv = s->num_kv_heads, d = s->head_dim;
+  const int G = Hq / Hkv;
+  const float scale = scale_of(s);
+  const WsLayout L = ws_layout(s, sft_rows_per_head(R));
+  char* wsc = static_cast<char*>(ws);
+
+  if (any_cache) {
+    CacheWriteParams cw{k, v, cache_k, cache_v, cache_len, B, (int)T, Hkv, d, esize(s), s->capacity};
+    rc = launch_rc(run_stage(ORTHROS_STAGE_CACHE_WRITE, st, [&] { return launch_cache_write(cw, st); }));
+    if (rc) return rc;
+  }
+
+  if (s->dtype == ORTHROS_F32) {
+    RowsF32Params r{};
+    r.q = static_cast<const float*>(q_base);
+    r.q_sb = T * Hq * d; r.q_st = (idx_t)Hq * d; r.q_sh = d;
+    r.alpha = aff->alpha_base; r.beta = aff->beta_base;
+    r.k = static_cast<const float*>(k); r.v = static_cast<const float*>(v);
+    r.k_sb = T * Hkv * d; r.k_st = (idx_t)Hkv * d; r.k_sh = d;
+    r.o = static_cast<float*>(o_base);
+    r.o_sb = T * Hq * d; r.o_st = (idx_t)Hq * d; r.o_sh = d;
+    r.B = B; r.Hq = Hq; r.Hkv = Hkv; r.G = G; r.d = d; r.nrows = (int)T; r.t0 = 0;
+    r.window = s->window; r.scale = scale; r.nkeys = T;
+    r.lse = lse_b; r.lse_sb = (idx_t)Hq * T; r.lse_sh = T;
+    rc = launch_rc(run_stage(ORTHROS_STAGE_ROWS_F32, st, [&] { return launch_rows_f32(r, st); }));
+    if (rc) return rc;
+    RowsF32Params o = r;
+    o.q = static_cast<const float*>(q_out);
+    o.q_sb = R * Hq * d; o.q_st = (idx_t)Hq * d;
+    o.alpha = aff->alpha_out; o.beta = aff->beta_out;
+    o.o = static_cast<float*>(o_out);
+    o.o_sb = R * Hq * d; o.o_st = (idx_t)Hq * d;
+    o.nrows = (int)R; o.pos = out_pos; o.window = INT_MAX;
+    o.lse = lse_o; o.lse_sb = (idx_t)Hq * R; o.lse_sh = R;
+    return launch_rc(run_stage(ORTHROS_STAGE_ROWS_F32, st, [&] { return launch_rows_f32(o, st); }));
+  }
+
+  // Base rows: Eq. 4 at every position.
+  BandParams bp{};
+  bp.q = q_base; bp.q_sb = T * Hq * d; bp.q_st = (idx_t)Hq * d; bp.q_sh = d;
+  bp.alpha = aff->alpha_base; bp.beta = aff->beta_base;
+  bp.k = k; bp.v = v; bp.k_sb = T * Hkv * d; bp.k_st = (idx_t)Hkv * d; bp.k_sh = d;
+  bp.o = o_base; bp.o_sb = T * Hq * d; bp.o_st = (idx_t)Hq * d; bp.o_sh = d;
+  bp.B = B; bp.nrows = (int)T; bp.nkeys = (int)T; bp.t_first = 0; bp.pos = nullptr;
+  bp.Hq = Hq; bp.Hkv = Hkv; bp.G = G;
+  bp.window = s->window < (int)T ? s->window : (int)T;
+  bp.scale_log2 = scale * kLog2e;
+  bp.lse = lse_b; bp.lse_sb = (idx_t)Hq * T; bp.lse_sh = T;
+  rc = launch_rc(run_stage(ORTHROS_STAGE_BAND, st, [&] { return launch_band(bp, d, st); }));
+  if (rc) return rc;
+
+  if (R > kSftSplitRows) {
+    // Many response rows: the banded kernel with the row positions, full causal windows.
+    BandParams op = bp;
+    op.q = q_out; op.q_sb = R * Hq * d; op.q_st = (idx_t)Hq * d;
+    op.alpha = aff->alpha_out; op.beta = aff->beta_out;
+    op.o = o_out; op.o_sb = R * Hq * d; op.o_st = (idx_t)Hq * d;
+    op.nrows = (int)R; op.pos = out_pos;
+    op.window = (int)T;
+    op.lse = lse_o; op.lse_sb = (idx_t)Hq * R; op.lse_sh = R;
+    return launch_rc(run_stage(ORTHROS_STAGE_BAND, st, [&] { return launch_band(op, d, st); }));
+  }
+
+  // Few response rows: split-key rows, each (row, head) pair over keys 0 .. pos[row].
+  SplitParams sp{};
+  sp.q_out = q_out; sp.q_sb = R * Hq * d; sp.q_st = (idx_t)Hq * d; sp.q_sh = d;
+  sp.a_out = aff->alpha_out; sp.b_out = aff->beta_out;
+  sp.a_base = aff->alpha_base; sp.b_base = aff->beta_base;
+  sp.k = k; sp.v = v;
+  sp.k_sb = T * Hkv * d; sp.k_sh = d; sp.k_st = (idx_t)Hkv * d;
+  sp.n_fixed = T;
+  sp.pos = out_pos; sp.R = (int)R;
+  sp.B = B; sp.Hq = Hq; sp.Hkv = Hkv; sp.G = G;
+  sp.HC = 16;
+  sp.nchunks = (int)((R * G + 15) / 16);
+  sp.window = s->window; sp.with_base = 0;
+  sp.nsplit = nsplit_for(T, (int64_t)B * Hkv * sp.nchunks);
+  sp.scale_log2 = scale * kLog2e;
+  sp.pm = reinterpret_cast<float*>(wsc + L.pm);
+  sp.pl = reinterpret_cast<float*>(wsc + L.pl);
+  sp.po = reinterpret_cast<float*>(wsc + L.po);
+  rc = launch_rc(run_stage(ORTHROS_STAGE_SPLIT_ROWS, st, [&] { return launch_split_rows(sp, d, st); }));
+  if (rc) return rc;
+  MergeParams mp{};
+  mp.pm = sp.pm; mp.pl = sp.pl; mp.po = sp.po;
+  mp.out0 = o_out; mp.o_sb0 = R * Hq * d; mp.o_st0 = (idx_t)Hq * d; mp.o_sh0 = d;
+  mp.rows = (int)(B * Hq * R); mp.nsplit = sp.nsplit; mp.d = d; mp.Hq = Hq;
+  mp.nstreams = (int)R; mp.rows_out0 = 1; mp.bf16 = 1;
+  mp.lse = lse_o;  // row (b Hq + h) R + r: the [B, Hq, R] layout
+  return launch_rc(run_stage(ORTHROS_STAGE_MERGE, st, [&] { return launch_merge(mp, st); }));
+}
 
 }  // namespace
 
@@ -488,7 +692,13 @@ int orthros_forward_pt_lse(const orthros_shape* s, int64_t T, const void* q_base
 
 size_t orthros_backward_workspace_bytes(const orthros_shape* s, int64_t T) {
   if (check_shape(s) != ORTHROS_OK || T < 1 || T > INT_MAX / 2) return 0;
-  return bwd_layout(s, T).total;
+  return bwd_layout(s, T, T).total;
+}
+
+size_t orthros_backward_sft_workspace_bytes(const orthros_shape* s, int64_t T, int64_t R) {
+  if (check_shape(s) != ORTHROS_OK || T < 1 || T > INT_MAX / 2 || R < 1 || R > INT_MAX / 2)
+    return 0;
+  return bwd_layout(s, T, R).total;
 }
 
 int orthros_backward_pt(const orthros_shape* s, int64_t T, const void* q_base, const void* q_out,
@@ -498,80 +708,20 @@ int orthros_backward_pt(const orthros_shape* s, int64_t T, const void* q_base, c
                         void* dq_base, void* dq_out, void* dk, void* dv,
                         const orthros_affine_grad* dg, void* ws, size_t ws_bytes,
                         hipStream_t st) {
-  int rc = check_shape(s);
-  if (rc) return rc;
-  if (T < 1 || T > INT_MAX / 2) return ORTHROS_E_INVALID;
-  if ((rc = check_affine(aff))) return rc;
-  if ((rc = check_ptrs({q_base, q_out, k, v, o_base, o_out, lse_base, lse_out, do_base, do_out,
-                        dq_base, dq_out, dk, dv}))) return rc;
-  if (!dg || check_ptrs({dg->dalpha_base, dg->dbeta_base, dg->dalpha_out, dg->dbeta_out}))
-    return ORTHROS_E_INVALID;
-  if (!ws || !aligned16(ws)) return ORTHROS_E_WORKSPACE;
-  const BwdLayout L = bwd_layout(s, T);
-  if (ws_bytes < L.total) return ORTHROS_E_WORKSPACE;
+  return backward_impl(s, T, q_base, q_out, nullptr, T, k, v, aff, o_base, o_out, lse_base,
+                       lse_out, do_base, do_out, dq_base, dq_out, dk, dv, dg, ws, ws_bytes, st);
+}
 
-  const int B = s->batch, Hq = s->num_q_heads, Hkv = s->num_kv_heads, d = s->head_dim;
-  const int G = Hq / Hkv;
-  const float scale = scale_of(s);
-  char* w = static_cast<char*>(ws);
-  const bool bf = s->dtype == ORTHROS_BF16;
-  const int wb = s->window < (int)T ? s->window : (int)T;
-
-  const void* qs[2] = {q_base, q_out};
-  const float* al[2] = {aff->alpha_base, aff->alpha_out};
-  const float* be[2] = {aff->beta_base, aff->beta_out};
-  const void* os[2] = {o_base, o_out};
-  const void* dos[2] = {do_base, do_out};
-  const float* lses[2] = {lse_base, lse_out};
-  float* Ds[2] = {reinterpret_cast<float*>(w + L.D[0]), reinterpret_cast<float*>(w + L.D[1])};
-  float* dqs[2] = {reinterpret_cast<float*>(w + L.dq[0]), reinterpret_cast<float*>(w + L.dq[1])};
-  void* qps[2] = {w + L.qp[0], w + L.qp[1]};
-  const int wins[2] = {wb, (int)T};
-  if (bf) {
-    rc = launch_rc(run_stage(ORTHROS_STAGE_BWD_Q, st, [&] {
-      return launch_qprep(q_base, q_out, al[0], be[0], al[1], be[1], qps[0], qps[1],
-                          (idx_t)B * T * Hq * d, Hq * d, scale * kLog2e, st);
-    }));
-    if (rc) return rc;
-  }
-  for (int i = 0; i < 2; ++i) {
-    BwdQParams q{};
-    q.q = bf ? qps[i] : qs[i];
-    q.alpha = al[i]; q.beta = be[i];
-    q.k = k; q.v = v; q.o = os[i]; q.dout = dos[i]; q.lse = lses[i];
-    q.D = Ds[i]; q.dq = dqs[i];
-    q.B = B; q.T = (int)T; q.Hq = Hq; q.Hkv = Hkv; q.G = G; q.window = wins[i]; q.scale = scale;
-    rc = launch_rc(run_stage(ORTHROS_STAGE_BWD_Q, st, [&] {
-      return bf ? launch_bwd_q_bf16(q, d, st) : launch_bwd_q_f32(q, d, st);
-    }));
-    if (rc) return rc;
-  }
-  BwdKVParams kv{};
-  for (int i = 0; i < 2; ++i) {
-    kv.q[i] = bf ? qps[i] : qs[i];
-    kv.alpha[i] = al[i]; kv.beta[i] = be[i];
-    kv.dout[i] = dos[i]; kv.lse[i] = lses[i]; kv.D[i] = Ds[i]; kv.window[i] = wins[i];
-  }
-  kv.k = k; kv.v = v; kv.dk = dk; kv.dv = dv;
-  kv.B = B; kv.T = (int)T; kv.Hq = Hq; kv.Hkv = Hkv; kv.G = G; kv.scale = scale;
-  rc = launch_rc(run_stage(ORTHROS_STAGE_BWD_KV, st, [&] {
-    return bf ? launch_bwd_kv_bf16(kv, d, st) : launch_bwd_kv_f32(kv, d, st);
-  }));
-  if (rc) return rc;
-  void* dqo[2] = {dq_base, dq_out};
-  float* da[2] = {dg->dalpha_base, dg->dalpha_out};
-  float* db[2] = {dg->dbeta_base, dg->dbeta_out};
-  for (int i = 0; i < 2; ++i) {
-    AffineGradParams ag{};
-    ag.dq = dqs[i]; ag.q = qs[i]; ag.alpha = al[i]; ag.dq_raw = dqo[i];
-    ag.part = reinterpret_cast<float*>(w + L.part);
-    ag.dalpha = da[i]; ag.dbeta = db[i];
-    ag.rows = B * (int)T; ag.n = Hq * d; ag.chunk_rows = L.chunk_rows; ag.nchunk = L.nchunk;
-    ag.bf16 = bf ? 1 : 0;
-    rc = launch_rc(run_stage(ORTHROS_STAGE_BWD_AFFINE, st, [&] { return launch_affine_grad(ag, st); }));
-    if (rc) return rc;
-  }
-  return ORTHROS_OK;
+int orthros_backward_sft(const orthros_shape* s, int64_t T, const void* q_base,
+                         const void* q_out, const int32_t* out_pos, int64_t R, const void* k,
+                         const void* v, const orthros_affine* aff, const void* o_base,
+                         const void* o_out, const float* lse_base, const float* lse_out,
+                         const void* do_base, const void* do_out, void* dq_base, void* dq_out,
+                         void* dk, void* dv, const orthros_affine_grad* dg, void* ws,
+                         size_t ws_bytes, hipStream_t st) {
+  if (!out_pos) return ORTHROS_E_INVALID;
+  return backward_impl(s, T, q_base, q_out, out_pos, R, k, v, aff, o_base, o_out, lse_base,
+                       lse_out, do_base, do_out, dq_base, dq_out, dk, dv, dg, ws, ws_bytes, st);
 }
 
 int orthros_prefill_chunk(const orthros_shape* s, int64_t past_len, int64_t C,
@@ -668,102 +818,18 @@ int orthros_forward_sft(const orthros_shape* s, int64_t T, const void* q_base, c
                         const orthros_affine* aff, void* cache_k, void* cache_v,
                         int32_t* cache_len, void* o_base, void* o_out, void* ws,
                         size_t ws_bytes, hipStream_t st) {
-  int rc = check_shape(s);
-  if (rc) return rc;
-  if (T < 1 || T > INT_MAX / 2 || R < 1 || R > INT_MAX / 2) return ORTHROS_E_INVALID;
-  if ((rc = check_affine(aff))) return rc;
-  if ((rc = check_ptrs({q_base, q_out, k, v, o_base, o_out}))) return rc;
-  if (!out_pos || ((uintptr_t)out_pos & 3u)) return ORTHROS_E_INVALID;
-  const bool any_cache = cache_k || cache_v || cache_len;
-  if (any_cache && (rc = check_ptrs({cache_k, cache_v, cache_len}))) return rc;
-  if ((rc = check_ws(s, ws, ws_bytes, sft_rows_per_head(R)))) return rc;
-  if (any_cache && T > s->capacity) return ORTHROS_E_CAPACITY;
+  return forward_sft_impl(s, T, q_base, q_out, out_pos, R, k, v, aff, cache_k, cache_v,
+                          cache_len, o_base, o_out, nullptr, nullptr, ws, ws_bytes, st);
+}
 
-  const int B = s->batch, Hq = s->num_q_heads, Hkv = s->num_kv_heads, d = s->head_dim;
-  const int G = Hq / Hkv;
-  const float scale = scale_of(s);
-  const WsLayout L = ws_layout(s, sft_rows_per_head(R));
-  char* wsc = static_cast<char*>(ws);
-
-  if (any_cache) {
-    CacheWriteParams cw{k, v, cache_k, cache_v, cache_len, B, (int)T, Hkv, d, esize(s), s->capacity};
-    rc = launch_rc(run_stage(ORTHROS_STAGE_CACHE_WRITE, st, [&] { return launch_cache_write(cw, st); }));
-    if (rc) return rc;
-  }
-
-  if (s->dtype == ORTHROS_F32) {
-    RowsF32Params r{};
-    r.q = static_cast<const float*>(q_base);
-    r.q_sb = T * Hq * d; r.q_st = (idx_t)Hq * d; r.q_sh = d;
-    r.alpha = aff->alpha_base; r.beta = aff->beta_base;
-    r.k = static_cast<const float*>(k); r.v = static_cast<const float*>(v);
-    r.k_sb = T * Hkv * d; r.k_st = (idx_t)Hkv * d; r.k_sh = d;
-    r.o = static_cast<float*>(o_base);
-    r.o_sb = T * Hq * d; r.o_st = (idx_t)Hq * d; r.o_sh = d;
-    r.B = B; r.Hq = Hq; r.Hkv = Hkv; r.G = G; r.d = d; r.nrows = (int)T; r.t0 = 0;
-    r.window = s->window; r.scale = scale; r.nkeys = T;
-    rc = launch_rc(run_stage(ORTHROS_STAGE_ROWS_F32, st, [&] { return launch_rows_f32(r, st); }));
-    if (rc) return rc;
-    RowsF32Params o = r;
-    o.q = static_cast<const float*>(q_out);
-    o.q_sb = R * Hq * d; o.q_st = (idx_t)Hq * d;
-    o.alpha = aff->alpha_out; o.beta = aff->beta_out;
-    o.o = static_cast<float*>(o_out);
-    o.o_sb = R * Hq * d; o.o_st = (idx_t)Hq * d;
-    o.nrows = (int)R; o.pos = out_pos; o.window = INT_MAX;
-    return launch_rc(run_stage(ORTHROS_STAGE_ROWS_F32, st, [&] { return launch_rows_f32(o, st); }));
-  }
-
-  // Base rows: Eq. 4 at every position.
-  BandParams bp{};
-  bp.q = q_base; bp.q_sb = T * Hq * d; bp.q_st = (idx_t)Hq * d; bp.q_sh = d;
-  bp.alpha = aff->alpha_base; bp.beta = aff->beta_base;
-  bp.k = k; bp.v = v; bp.k_sb = T * Hkv * d; bp.k_st = (idx_t)Hkv * d; bp.k_sh = d;
-  bp.o = o_base; bp.o_sb = T * Hq * d; bp.o_st = (idx_t)Hq * d; bp.o_sh = d;
-  bp.B = B; bp.nrows = (int)T; bp.nkeys = (int)T; bp.t_first = 0; bp.pos = nullptr;
-  bp.Hq = Hq; bp.Hkv = Hkv; bp.G = G;
-  bp.window = s->window < (int)T ? s->window : (int)T;
-  bp.scale_log2 = scale * kLog2e;
-  rc = launch_rc(run_stage(ORTHROS_STAGE_BAND, st, [&] { return launch_band(bp, d, st); }));
-  if (rc) return rc;
-
-  if (R > kSftSplitRows) {
-    // Many response rows: the banded kernel with the row positions, full causal windows.
-    BandParams op = bp;
-    op.q = q_out; op.q_sb = R * Hq * d; op.q_st = (idx_t)Hq * d;
-    op.alpha = aff->alpha_out; op.beta = aff->beta_out;
-    op.o = o_out; op.o_sb = R * Hq * d; op.o_st = (idx_t)Hq * d;
-    op.nrows = (int)R; op.pos = out_pos;
-    op.window = (int)T;
-    return launch_rc(run_stage(ORTHROS_STAGE_BAND, st, [&] { return launch_band(op, d, st); }));
-  }
-
-  // Few response rows: split-key rows, each (row, head) pair over keys 0 .. pos[row].
-  SplitParams sp{};
-  sp.q_out = q_out; sp.q_sb = R * Hq * d; sp.q_st = (idx_t)Hq * d; sp.q_sh = d;
-  sp.a_out = aff->alpha_out; sp.b_out = aff->beta_out;
-  sp.a_base = aff->alpha_base; sp.b_base = aff->beta_base;
-  sp.k = k; sp.v = v;
-  sp.k_sb = T * Hkv * d; sp.k_sh = d; sp.k_st = (idx_t)Hkv * d;
-  sp.n_fixed = T;
-  sp.pos = out_pos; sp.R = (int)R;
-  sp.B = B; sp.Hq = Hq; sp.Hkv = Hkv; sp.G = G;
-  sp.HC = 16;
-  sp.nchunks = (int)((R * G + 15) / 16);
-  sp.window = s->window; sp.with_base = 0;
-  sp.nsplit = nsplit_for(T, (int64_t)B * Hkv * sp.nchunks);
-  sp.scale_log2 = scale * kLog2e;
-  sp.pm = reinterpret_cast<float*>(wsc + L.pm);
-  sp.pl = reinterpret_cast<float*>(wsc + L.pl);
-  sp.po = reinterpret_cast<float*>(wsc + L.po);
-  rc = launch_rc(run_stage(ORTHROS_STAGE_SPLIT_ROWS, st, [&] { return launch_split_rows(sp, d, st); }));
-  if (rc) return rc;
-  MergeParams mp{};
-  mp.pm = sp.pm; mp.pl = sp.pl; mp.po = sp.po;
-  mp.out0 = o_out; mp.o_sb0 = R * Hq * d; mp.o_st0 = (idx_t)Hq * d; mp.o_sh0 = d;
-  mp.rows = (int)(B * Hq * R); mp.nsplit = sp.nsplit; mp.d = d; mp.Hq = Hq;
-  mp.nstreams = (int)R; mp.rows_out0 = 1; mp.bf16 = 1;
-  return launch_rc(run_stage(ORTHROS_STAGE_MERGE, st, [&] { return launch_merge(mp, st); }));
+int orthros_forward_sft_lse(const orthros_shape* s, int64_t T, const void* q_base,
+                            const void* q_out, const int32_t* out_pos, int64_t R, const void* k,
+                            const void* v, const orthros_affine* aff, void* o_base, void* o_out,
+                            float* lse_base, float* lse_out, void* ws, size_t ws_bytes,
+                            hipStream_t st) {
+  if (check_ptrs({lse_base, lse_out})) return ORTHROS_E_INVALID;
+  return forward_sft_impl(s, T, q_base, q_out, out_pos, R, k, v, aff, nullptr, nullptr, nullptr,
+                          o_base, o_out, lse_base, lse_out, ws, ws_bytes, st);
 }
 
 int orthros_read_device_status(void* ws, size_t ws_bytes, int32_t* host_status, int clear,

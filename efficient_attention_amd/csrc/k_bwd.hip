@@ -102,7 +102,8 @@ __global__ __launch_bounds__(256) void qprep_kernel(QPrepParams p) {
 
 // ---- query side ------------------------------------------------------------------------------
 // Work-group: 8 wavefronts, HPW query heads of one kv head x (8 / HPW) blocks of 32 rows. p.q
-// is q' (prepared); K and V tiles of 64 keys go through a two-slot LDS ring.
+// is q' (prepared); K and V tiles of 64 keys go through a two-slot LDS ring. Rows are positions,
+// or (with p.pos) row r sits at position pos[r].
 template <int D, int HPW>
 __global__ __launch_bounds__(64 * kQNW) void bwd_q_kernel(BwdQParams p) {
   constexpr int NCH = D / 8, ROWB = D * 2, TILEB = kTK * ROWB, STAGEB = 2 * TILEB;
@@ -110,13 +111,14 @@ __global__ __launch_bounds__(64 * kQNW) void bwd_q_kernel(BwdQParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGEB];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int T = p.T;
+  const int T = p.T, NR = p.nrows;
   const int nhc = p.G / HPW;
-  const int npb = (T + BMP - 1) / BMP;
+  const int npb = (NR + BMP - 1) / BMP;
   const uint32_t total = (uint32_t)p.B * p.Hkv * nhc * npb;
   const uint32_t lid = xcd_swizzle(blockIdx.x, total);
   const int inner = p.B * p.Hkv * nhc;
   const int pb = __builtin_amdgcn_readfirstlane(npb - 1 - (int)(lid / inner));  // longest first
+  if (pb < 0) return;  // the grid covers exactly npb row blocks; nothing past them
   int rest = (int)(lid % inner);
   const int hc = __builtin_amdgcn_readfirstlane(rest % nhc);
   rest /= nhc;
@@ -127,13 +129,13 @@ __global__ __launch_bounds__(64 * kQNW) void bwd_q_kernel(BwdQParams p) {
   const int r0w = r0 + kQW * (wv / HPW);
   const int j = lane & 31, hh = lane >> 5;
   const int row = r0w + j;
-  const bool rvalid = row < T;
-  const bool wactive = r0w < T;
-  const int qrow = rvalid ? row : T - 1;
+  const bool rvalid = row < NR;
+  const bool wactive = r0w < NR;
+  const int qrow = rvalid ? row : NR - 1;
   const int w = p.window < T ? p.window : T;
 
   // Row data: q' and dO fragments (B operands), D_t = dO . O, lse in log2 units.
-  const idx_t rbase = ((idx_t)b * T + qrow) * p.Hq * D + (idx_t)h * D;
+  const idx_t rbase = ((idx_t)b * NR + qrow) * p.Hq * D + (idx_t)h * D;
   bf16x8 qf[NKS], dof[NKS];
   float dsum = 0.f;
 #pragma unroll
@@ -148,21 +150,54 @@ __global__ __launch_bounds__(64 * kQNW) void bwd_q_kernel(BwdQParams p) {
       dsum += bf16_lo(dr[e]) * bf16_lo(orr[e]) + bf16_hi(dr[e]) * bf16_hi(orr[e]);
   }
   const float Dt = lane_pair_sum(dsum);
-  const idx_t lrow = ((idx_t)b * p.Hq + h) * T + qrow;
+  const idx_t lrow = ((idx_t)b * p.Hq + h) * NR + qrow;
   const float lse2 = p.lse[lrow] * kLog2e;
   if (rvalid && hh == 0) p.D[lrow] = Dt;
 
+  // Row positions: the lowest and highest of this wavefront's rows and of the work-group's.
+  int qmin_w, qmax_w, qmin_b, qmax_b, tq;
+  if (!p.pos) {
+    const int last_w = r0w + kQW - 1 < NR - 1 ? r0w + kQW - 1 : NR - 1;
+    const int last_b = r0 + BMP - 1 < NR - 1 ? r0 + BMP - 1 : NR - 1;
+    qmin_w = r0w;
+    qmax_w = last_w;
+    qmin_b = r0;
+    qmax_b = last_b;
+    tq = rvalid ? row : last_w;
+  } else {
+    __shared__ int wrange[2 * kQNW];
+    int mine = p.pos[qrow];
+    mine = mine < 0 ? 0 : (mine > T - 1 ? T - 1 : mine);  // clamped into [0, T)
+    int lo = rvalid ? mine : 0x7fffffff, hi = rvalid ? mine : -1;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      lo = min(lo, __shfl_xor(lo, off, 64));
+      hi = max(hi, __shfl_xor(hi, off, 64));
+    }
+    qmin_w = __builtin_amdgcn_readfirstlane(lo);
+    qmax_w = __builtin_amdgcn_readfirstlane(hi);
+    if (lane == 0) {
+      wrange[2 * wv] = qmin_w;
+      wrange[2 * wv + 1] = qmax_w;
+    }
+    __syncthreads();
+    qmin_b = 0x7fffffff;
+    qmax_b = -1;
+#pragma unroll
+    for (int i = 0; i < kQNW; ++i) {
+      qmin_b = min(qmin_b, wrange[2 * i]);
+      qmax_b = max(qmax_b, wrange[2 * i + 1]);
+    }
+    tq = rvalid ? mine : qmax_w;  // rows past the end compute on a valid position, unstored
+  }
   // Key range of the work-group and of this wavefront (tiles ascending from tile_lo).
-  const int last_w = r0w + kQW - 1 < T - 1 ? r0w + kQW - 1 : T - 1;
-  const int last_b = r0 + BMP - 1 < T - 1 ? r0 + BMP - 1 : T - 1;
-  const int tq = rvalid ? row : last_w;
-  const int glo = r0 - w + 1 > 0 ? r0 - w + 1 : 0;
+  const int glo = qmin_b - w + 1 > 0 ? qmin_b - w + 1 : 0;
   const int tile_lo = __builtin_amdgcn_readfirstlane(glo / kTK * kTK);
-  const int ntiles = __builtin_amdgcn_readfirstlane((last_b / kTK * kTK - glo / kTK * kTK) / kTK + 1);
-  const int wlo = r0w - w + 1 > 0 ? r0w - w + 1 : 0;
+  const int ntiles = __builtin_amdgcn_readfirstlane((qmax_b / kTK * kTK - glo / kTK * kTK) / kTK + 1);
+  const int wlo = qmin_w - w + 1 > 0 ? qmin_w - w + 1 : 0;
   const int ea = (wlo / kTK * kTK - tile_lo) / kTK;
-  const int eb = (last_w / kTK * kTK - tile_lo) / kTK;
-  auto full = [&](int tb) { return tb + kTK - 1 <= r0w && tb >= last_w - w + 1 && tb + kTK - 1 <= T - 1; };
+  const int eb = (qmax_w / kTK * kTK - tile_lo) / kTK;
+  auto full = [&](int tb) { return tb + kTK - 1 <= qmin_w && tb >= qmax_w - w + 1 && tb + kTK - 1 <= T - 1; };
 
   // Tile copies (global side swizzled; wave wv fills rows (wv NINST + i) LROWS .. of a tile).
   constexpr int LROWS = 1024 / ROWB;
@@ -266,7 +301,7 @@ __global__ __launch_bounds__(64 * kQNW) void bwd_q_kernel(BwdQParams p) {
   }
 
   if (rvalid) {
-    float* out = p.dq + ((idx_t)b * T + row) * p.Hq * D + (idx_t)h * D;
+    float* out = p.dq + ((idx_t)b * NR + row) * p.Hq * D + (idx_t)h * D;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -282,14 +317,15 @@ __global__ __launch_bounds__(64 * kQNW) void bwd_q_kernel(BwdQParams p) {
 // ---- key side --------------------------------------------------------------------------------
 // Work-group: 4 wavefronts, 128 keys of one kv head (wavefront wv owns keys k0 + 32 wv ..).
 // The keys' fragments stay in registers, their values in LDS; 32-row query tiles (q', dO,
-// lse, D) of both streams and every head of the group go through a two-slot LDS ring.
+// lse, D and the rows' positions) of both streams and every head of the group go through a
+// two-slot LDS ring. A stream's rows are its positions, or a row list (every tile visited).
 template <int D>
 __global__ __launch_bounds__(64 * kKNW, 2) void bwd_kv_kernel(BwdKVParams p) {
   constexpr int NCH = D / 8, ROWB = D * 2, NKS = D / 16, NDT = D / 32;
   constexpr int KB = kKNW * 32;                  // keys per work-group
   constexpr int VBYTES = KB * ROWB;              // value block
   constexpr int QTB = kQW * ROWB;                // one 32-row tile
-  constexpr int STG = 2 * QTB + 2 * kQW * 4;     // q', dO, lse, D
+  constexpr int STG = 2 * QTB + 3 * kQW * 4;     // q', dO, lse, D, positions
   __shared__ __attribute__((aligned(16))) unsigned char smem[VBYTES + 2 * STG];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -333,14 +369,20 @@ __global__ __launch_bounds__(64 * kKNW, 2) void bwd_kv_kernel(BwdKVParams p) {
     }
   }
 
-  // Row tiles: stream st covers rows k0 .. min(T-1, k0 + KB - 1 + w_st - 1).
+  // Row tiles: a stream whose rows are positions covers rows k0 .. min(T-1, k0 + KB - 1 +
+  // w_st - 1); a row list is visited whole.
   int wst[2], qt0[2], nqt[2];
 #pragma unroll
   for (int st = 0; st < 2; ++st) {
     wst[st] = p.window[st] < T ? p.window[st] : T;
-    const int hi = k0 + KB - 1 + wst[st] - 1 < T - 1 ? k0 + KB - 1 + wst[st] - 1 : T - 1;
-    qt0[st] = k0 / kQW;
-    nqt[st] = hi / kQW - qt0[st] + 1;
+    if (p.pos[st]) {
+      qt0[st] = 0;
+      nqt[st] = (p.nrows[st] + kQW - 1) / kQW;
+    } else {
+      const int hi = k0 + KB - 1 + wst[st] - 1 < T - 1 ? k0 + KB - 1 + wst[st] - 1 : T - 1;
+      qt0[st] = k0 / kQW;
+      nqt[st] = hi / kQW - qt0[st] + 1;
+    }
   }
   const int n0 = p.G * nqt[0];
   const int nitems = n0 + p.G * nqt[1];
@@ -366,27 +408,32 @@ __global__ __launch_bounds__(64 * kKNW, 2) void bwd_kv_kernel(BwdKVParams p) {
   }
   const uint32_t rowq = (uint32_t)p.Hq * D * 2;
   float ld_lse = 0.f, ld_D = 0.f;  // thread tid < 32: row tid of the next tile
+  int ld_pos = -1;                 // its position, -1 past the last row
   auto load_item = [&](int i, int slot) {
     int st, hd, qt;
     item(i, st, hd, qt);
     const int t0 = qt * kQW;
-    const idx_t off0 = ((idx_t)b * T + t0) * p.Hq * D + (idx_t)hd * D;
+    const int NR = p.nrows[st];
+    const idx_t off0 = ((idx_t)b * NR + t0) * p.Hq * D + (idx_t)hd * D;
     const unsigned char* qg = reinterpret_cast<const unsigned char*>(static_cast<const uint16_t*>(p.q[st]) + off0);
     const unsigned char* dg = reinterpret_cast<const unsigned char*>(static_cast<const uint16_t*>(p.dout[st]) + off0);
     const uint32_t sb = lds0 + VBYTES + (uint32_t)(slot * STG);
 #pragma unroll
     for (int k = 0; k < NQI; ++k) {
-      const int over = crow[k] - (T - 1 - t0);
+      const int over = crow[k] - (NR - 1 - t0);  // rows past the end re-read the last row
       const uint32_t back = over > 0 ? (uint32_t)over * rowq : 0u;
       const uint32_t dst = sb + (uint32_t)(wk_s * NQI + k) * 1024u;
       copy_to_lds(qg, coff[k] - back, dst);
       copy_to_lds(dg, coff[k] - back, dst + QTB);
     }
     if (tid < kQW) {
-      const int t = t0 + tid < T ? t0 + tid : T - 1;
-      const idx_t lr = ((idx_t)b * p.Hq + hd) * T + t;
+      const int r = t0 + tid < NR ? t0 + tid : NR - 1;
+      const idx_t lr = ((idx_t)b * p.Hq + hd) * NR + r;
       ld_lse = p.lse[st][lr] * kLog2e;
       ld_D = p.D[st][lr];
+      int ps = p.pos[st] ? p.pos[st][r] : r;
+      ps = ps < 0 ? 0 : (ps > T - 1 ? T - 1 : ps);
+      ld_pos = t0 + tid < NR ? ps : -1;
     }
   };
   auto store_rowdata = [&](int slot) {
@@ -394,6 +441,7 @@ __global__ __launch_bounds__(64 * kKNW, 2) void bwd_kv_kernel(BwdKVParams p) {
       float* f = reinterpret_cast<float*>(smem + VBYTES + slot * STG + 2 * QTB);
       f[tid] = ld_lse;
       f[kQW + tid] = ld_D;
+      reinterpret_cast<int*>(f)[2 * kQW + tid] = ld_pos;
     }
   };
 
@@ -432,13 +480,29 @@ __global__ __launch_bounds__(64 * kKNW, 2) void bwd_kv_kernel(BwdKVParams p) {
     (void)hd;
     const int t0 = qt * kQW;
     const int w = wst[st];
-    // rows t0 .. t0+31 against keys k0w .. k0w+31: any pair with key <= t < key + w?
-    const bool need = t0 + kQW - 1 >= k0w && t0 <= k0w + 31 + w - 1 && k0w < T;
+    const bool listed = p.pos[st] != nullptr;
+    const unsigned char* sq = smem + VBYTES + slot * STG;
+    const float* rowf = reinterpret_cast<const float*>(sq + 2 * QTB);
+    const int* rowp = reinterpret_cast<const int*>(rowf + 2 * kQW);
+    // rows against keys k0w .. k0w+31: any pair with key <= t < key + w?
+    bool need, fl;
+    if (!listed) {
+      need = t0 + kQW - 1 >= k0w && t0 <= k0w + 31 + w - 1 && k0w < T;
+      fl = t0 >= k0w + 31 && t0 + kQW - 1 <= k0w + w - 1 && t0 + kQW - 1 < T && k0w + 31 < T;
+    } else {
+      bool any = false;  // this lane's 16 rows (both lane halves together cover the tile)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int4 p4 = *reinterpret_cast<const int4*>(rowp + 8 * q4 + 4 * hh);
+        const int pv[4] = {p4.x, p4.y, p4.z, p4.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) any = any || (pv[k] >= k0w && pv[k] <= k0w + 31 + w - 1);
+      }
+      need = __builtin_amdgcn_ballot_w64(any) != 0 && k0w < T;
+      fl = false;
+    }
     if (need) {
-      const bool fl = t0 >= k0w + 31 && t0 + kQW - 1 <= k0w + w - 1 && t0 + kQW - 1 < T && k0w + 31 < T;
-      const unsigned char* sq = smem + VBYTES + slot * STG;
       const unsigned char* sd = sq + QTB;
-      const float* rowf = reinterpret_cast<const float*>(sq + 2 * QTB);
       f32x16 S = zero16, dP = zero16;
 #pragma unroll
       for (int s = 0; s < NKS; ++s) {
@@ -457,13 +521,15 @@ __global__ __launch_bounds__(64 * kKNW, 2) void bwd_kv_kernel(BwdKVParams p) {
       for (int q4 = 0; q4 < 4; ++q4) {
         const f32x4 l4 = *reinterpret_cast<const f32x4*>(rowf + 8 * q4 + 4 * hh);
         const f32x4 d4 = *reinterpret_cast<const f32x4*>(rowf + kQW + 8 * q4 + 4 * hh);
+        const int4 p4 = *reinterpret_cast<const int4*>(rowp + 8 * q4 + 4 * hh);
+        const int pv[4] = {p4.x, p4.y, p4.z, p4.w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const int r = 4 * q4 + k;
           float s = S[r];
           if (!fl) {
-            const int t = t0 + 8 * q4 + 4 * hh + k;
-            const bool ok = key <= t && key > t - w && t < T && kvalid;
+            const int t = pv[k];  // -1 past the last row: masked
+            const bool ok = key <= t && key > t - w && kvalid;
             s = ok ? s : kNegInf;
           }
           const float pr = fast_exp2(s - l4[k]);
@@ -512,12 +578,12 @@ __global__ __launch_bounds__(64 * kKNW, 2) void bwd_kv_kernel(BwdKVParams p) {
 // ---- launchers -------------------------------------------------------------------------------
 hipError_t launch_qprep(const void* q0, const void* q1, const float* a0, const float* b0,
                         const float* a1, const float* b1, void* o0, void* o1, idx_t n, int hd,
-                        float c, hipStream_t s) {
+                        float c, hipStream_t s, int nstreams) {
   QPrepParams p{{q0, q1}, {a0, a1}, {b0, b1}, {o0, o1}, n, hd, c};
   idx_t blocks = (n / 8 + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(qprep_kernel, dim3((unsigned)blocks, 2), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(qprep_kernel, dim3((unsigned)blocks, (unsigned)nstreams), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
@@ -527,7 +593,7 @@ hipError_t launch_bwd_q_bf16(const BwdQParams& p, int d, hipStream_t s) {
   else if (p.G % 4 == 0) hpw = 4;
   else if (p.G % 2 == 0) hpw = 2;
   const int bmp = kQW * (kQNW / hpw);
-  const int npb = (p.T + bmp - 1) / bmp;
+  const int npb = (p.nrows + bmp - 1) / bmp;  // row blocks, as the kernel derives them
   dim3 grid((unsigned)(p.B * p.Hkv * (p.G / hpw) * npb)), block(64 * kQNW);
 #define ORTHROS_BWDQ(DD, HH) hipLaunchKernelGGL((bwd_q_kernel<DD, HH>), grid, block, 0, s, p)
   if (d == 128) {

@@ -24,15 +24,18 @@ __device__ __forceinline__ float wave_sum64(float x) {
 }
 }  // namespace
 
-// One wavefront per (row t, query head h, sequence b) of one stream: D_t and the post-affine
-// query gradient (times nothing: dq already includes the score scale s).
+// One wavefront per (row, query head h, sequence b) of one stream: D_t and the post-affine
+// query gradient (which includes the score scale s). The row sits at position pos[row] with a
+// row list, else at position row.
 template <int DIM>
 __global__ __launch_bounds__(64) void bwd_q_f32_kernel(BwdQParams p) {
   constexpr int E = DIM / 64;
-  const int t = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int r = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x;
   const int g = h / p.G;
-  const idx_t row = ((idx_t)b * p.T + t) * p.Hq + h;  // [B, T, Hq] row of q / o / dout / dq
+  int t = p.pos ? p.pos[r] : r;
+  t = t < 0 ? 0 : (t > p.T - 1 ? p.T - 1 : t);
+  const idx_t row = ((idx_t)b * p.nrows + r) * p.Hq + h;  // [B, nrows, Hq] row of q / o / dq
   const float* qr = static_cast<const float*>(p.q) + row * DIM;
   const float* orow = static_cast<const float*>(p.o) + row * DIM;
   const float* dor = static_cast<const float*>(p.dout) + row * DIM;
@@ -47,7 +50,7 @@ __global__ __launch_bounds__(64) void bwd_q_f32_kernel(BwdQParams p) {
     dq[e] = 0.f;
   }
   const float Dt = wave_sum64(dsum);
-  const idx_t lrow = ((idx_t)b * p.Hq + h) * p.T + t;
+  const idx_t lrow = ((idx_t)b * p.Hq + h) * p.nrows + r;
   if (lane == 0) p.D[lrow] = Dt;
   const float lse = p.lse[lrow];
   const int w = p.window < p.T ? p.window : p.T;
@@ -76,7 +79,8 @@ __global__ __launch_bounds__(64) void bwd_q_f32_kernel(BwdQParams p) {
 }
 
 // One wavefront per (key j, kv head g, sequence b): dk_j and dv_j over both streams' rows that
-// see key j (base rows j .. j + w - 1, output rows j .. T - 1) of every query head of the group.
+// see key j (positions j .. j + w - 1 with the stream's window w) of every query head of the
+// group. A stream with a row list visits every listed row and keeps those at such positions.
 template <int DIM>
 __global__ __launch_bounds__(64) void bwd_kv_f32_kernel(BwdKVParams p) {
   constexpr int E = DIM / 64;
@@ -97,6 +101,8 @@ __global__ __launch_bounds__(64) void bwd_kv_f32_kernel(BwdKVParams p) {
   for (int st = 0; st < 2; ++st) {
     const int w = p.window[st] < p.T ? p.window[st] : p.T;  // window >= T: causal
     const int hi = j + w - 1 < p.T - 1 ? j + w - 1 : p.T - 1;
+    const int NR = p.nrows[st];
+    const int32_t* pos = p.pos[st];
     for (int hg = 0; hg < p.G; ++hg) {
       const int h = g * p.G + hg;
       float a[E], bb[E];
@@ -105,10 +111,16 @@ __global__ __launch_bounds__(64) void bwd_kv_f32_kernel(BwdKVParams p) {
         a[e] = p.alpha[st][h * DIM + lane + 64 * e] * p.scale;
         bb[e] = p.beta[st][h * DIM + lane + 64 * e] * p.scale;
       }
-      const float* lse = p.lse[st] + ((idx_t)b * p.Hq + h) * p.T;
-      const float* Dr = p.D[st] + ((idx_t)b * p.Hq + h) * p.T;
-      for (int t = j; t <= hi; ++t) {
-        const idx_t row = ((idx_t)b * p.T + t) * p.Hq + h;
+      const float* lse = p.lse[st] + ((idx_t)b * p.Hq + h) * NR;
+      const float* Dr = p.D[st] + ((idx_t)b * p.Hq + h) * NR;
+      const int r_lo = pos ? 0 : j, r_hi = pos ? NR - 1 : hi;
+      for (int t = r_lo; t <= r_hi; ++t) {  // t: row index (the position without a list)
+        if (pos) {
+          int ps = pos[t];
+          ps = ps < 0 ? 0 : (ps > p.T - 1 ? p.T - 1 : ps);
+          if (ps < j || ps > hi) continue;
+        }
+        const idx_t row = ((idx_t)b * NR + t) * p.Hq + h;
         const float* qr = static_cast<const float*>(p.q[st]) + row * DIM;
         const float* dor = static_cast<const float*>(p.dout[st]) + row * DIM;
         float q[E], dO[E];
@@ -197,7 +209,7 @@ __global__ __launch_bounds__(256) void affine_grad_final_kernel(AffineGradParams
 }
 
 hipError_t launch_bwd_q_f32(const BwdQParams& p, int d, hipStream_t s) {
-  dim3 grid(p.T, p.Hq, p.B);
+  dim3 grid(p.nrows, p.Hq, p.B);
   if (d == 128)
     hipLaunchKernelGGL(bwd_q_f32_kernel<128>, grid, dim3(64), 0, s, p);
   else

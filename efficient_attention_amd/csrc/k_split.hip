@@ -375,6 +375,8 @@ __global__ __launch_bounds__(64) void merge_kernel(MergeParams p) {
   wgt[lane] = f;
   __syncthreads();
   const float inv = 1.f / den;
+  // log-sum-exp of the row's scores (scores here are in log2 units), natural log
+  if (p.lse && lane == 0) p.lse[row] = (M + __log2f(den)) * 0.69314718055994531f;
   void* out = (st == 0 || p.rows_out0) ? p.out0 : p.out1;
   const idx_t off = p.rows_out0 ? b * p.o_sb0 + (idx_t)st * p.o_st0 + (idx_t)h * p.o_sh0
                     : st == 0  ? b * p.o_sb0 + (idx_t)h * p.o_sh0

@@ -124,6 +124,7 @@ struct MergeParams {
   void* out0;  // stream 0 (output stream)
   void* out1;  // stream 1 (base stream, decode)
   idx_t o_sb0, o_sh0, o_sb1, o_sh1, o_st0;
+  float* lse;  // optional: natural-log log-sum-exp of row r at lse[r]
   int rows, nsplit, d, Hq, nstreams, bf16, rows_out0;
 };
 

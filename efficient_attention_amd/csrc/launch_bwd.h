@@ -5,7 +5,7 @@
 
 namespace orthros {
 
-// Training backward of one stream's rows (pre-training regime): row t of [B, T, Hq, d] attends
+// Training backward of one stream's rows: the row at position t (of [B, nrows, Hq, d]) attends
 // keys lo(t) .. t with lo(t) = max(0, t - window + 1) of k, v [B, T, Hkv, d].
 struct BwdQParams {
   const void* q;           // raw queries of the stream
@@ -15,15 +15,21 @@ struct BwdQParams {
   const void* v;
   const void* o;           // forward output of the stream
   const void* dout;        // its gradient
-  const float* lse;        // [B, Hq, T] natural-log log-sum-exp of the forward rows
-  float* D;                // out: [B, Hq, T] rowsum(dout * o)
-  float* dq;               // out: [B, T, Hq, d] fp32 gradient of the post-affine query
+  const float* lse;        // [B, Hq, nrows] natural-log log-sum-exp of the forward rows
+  float* D;                // out: [B, Hq, nrows] rowsum(dout * o)
+  float* dq;               // out: [B, nrows, Hq, d] fp32 gradient of the post-affine query
+  const int32_t* pos;      // optional: row r sits at position pos[r] (clamped into [0, T));
+                           // without it, rows are positions (nrows = T)
+  int nrows;
   int B, T, Hq, Hkv, G, window;
   float scale;
 };
 
-// Key-side backward: dk, dv [B, T, Hkv, d] from both streams' rows (index 0 base, 1 output).
+// Key-side backward: dk, dv [B, T, Hkv, d] from both streams' rows (index 0 base, 1 output);
+// a stream's rows are its positions (nrows = T) or a row list pos (as in BwdQParams).
 struct BwdKVParams {
+  const int32_t* pos[2];
+  int nrows[2];
   const void* q[2];
   const float* alpha[2];
   const float* beta[2];
@@ -59,6 +65,6 @@ hipError_t launch_bwd_kv_bf16(const BwdKVParams& p, int d, hipStream_t s);
 hipError_t launch_affine_grad(const AffineGradParams& p, hipStream_t s);
 hipError_t launch_qprep(const void* q0, const void* q1, const float* a0, const float* b0,
                         const float* a1, const float* b1, void* o0, void* o1, idx_t n, int hd,
-                        float c, hipStream_t s);
+                        float c, hipStream_t s, int nstreams);
 
 }  // namespace orthros

@@ -19,7 +19,8 @@ __all__ = [
     "PagedKV", "lib", "library_path", "workspace_bytes", "sft_workspace_bytes",
     "make_workspace", "prefill", "prefill_chunk", "decode_step", "decode_step_paged",
     "paged_write", "forward_pt", "forward_sft", "forward_pt_lse", "backward_workspace_bytes",
-    "backward_pt", "read_device_status", "status_string",
+    "backward_pt", "forward_sft_lse", "backward_sft_workspace_bytes", "backward_sft",
+    "read_device_status", "status_string",
     "timing_begin", "timing_end", "EXPORTED_SYMBOLS",
 ]
 
@@ -34,6 +35,7 @@ EXPORTED_SYMBOLS = (
     "orthros_prefill_chunk", "orthros_decode_step", "orthros_decode_step_paged",
     "orthros_paged_write", "orthros_forward_pt", "orthros_forward_sft",
     "orthros_forward_pt_lse", "orthros_backward_workspace_bytes", "orthros_backward_pt",
+    "orthros_forward_sft_lse", "orthros_backward_sft_workspace_bytes", "orthros_backward_sft",
     "orthros_read_device_status", "orthros_status_string", "orthros_timing_begin",
     "orthros_timing_end",
 )
@@ -118,6 +120,15 @@ def lib() -> ctypes.CDLL:
                                           vp, vp, vp, vp, ctypes.POINTER(_CAffineGrad), vp, sz,
                                           vp]
         L.orthros_backward_pt.restype = ctypes.c_int
+        L.orthros_forward_sft_lse.argtypes = [sp, i64, vp, vp, vp, i64, vp, vp, ap, vp, vp, vp,
+                                              vp, vp, sz, vp]
+        L.orthros_forward_sft_lse.restype = ctypes.c_int
+        L.orthros_backward_sft_workspace_bytes.argtypes = [sp, i64, i64]
+        L.orthros_backward_sft_workspace_bytes.restype = sz
+        L.orthros_backward_sft.argtypes = [sp, i64, vp, vp, vp, i64, vp, vp, ap, vp, vp, vp, vp,
+                                           vp, vp, vp, vp, vp, vp, ctypes.POINTER(_CAffineGrad),
+                                           vp, sz, vp]
+        L.orthros_backward_sft.restype = ctypes.c_int
         L.orthros_read_device_status.argtypes = [vp, sz, ctypes.POINTER(i32), ctypes.c_int, vp]
         L.orthros_read_device_status.restype = ctypes.c_int
         L.orthros_status_string.argtypes = [ctypes.c_int]
@@ -452,6 +463,65 @@ def backward_pt(shape: Shape, q_base, q_out, k, v, affine: Affine, o_base, o_out
         dq_base.data_ptr(), dq_out.data_ptr(), dk.data_ptr(), dv.data_ptr(), ctypes.byref(g),
         workspace.data_ptr(), workspace.numel(), _stream(stream))
     _rc(rc, "orthros_backward_pt")
+
+
+def forward_sft_lse(shape: Shape, q_base, q_out, out_pos, k, v, affine: Affine, o_base, o_out,
+                    lse_base, lse_out, workspace, stream=None):
+    """orthros_forward_sft_lse: the fine-tuning forward plus per-row log-sum-exp."""
+    B, Hq, Hkv, d = shape.batch, shape.num_q_heads, shape.num_kv_heads, shape.head_dim
+    T, R = q_base.shape[1], q_out.shape[1]
+    dev, dt = q_base.device, shape.dtype
+    _check(q_base, (B, T, Hq, d), dt, dev, "q_base")
+    _check(q_out, (B, R, Hq, d), dt, dev, "q_out")
+    _check(out_pos, (R,), torch.int32, dev, "out_pos")
+    _check(k, (B, T, Hkv, d), dt, dev, "k")
+    _check(v, (B, T, Hkv, d), dt, dev, "v")
+    _check(o_base, (B, T, Hq, d), dt, dev, "o_base")
+    _check(o_out, (B, R, Hq, d), dt, dev, "o_out")
+    _check(lse_base, (B, Hq, T), torch.float32, dev, "lse_base")
+    _check(lse_out, (B, Hq, R), torch.float32, dev, "lse_out")
+    aff = affine.c(Hq * d, dev)
+    rc = lib().orthros_forward_sft_lse(
+        ctypes.byref(shape.c()), T, q_base.data_ptr(), q_out.data_ptr(), out_pos.data_ptr(), R,
+        k.data_ptr(), v.data_ptr(), ctypes.byref(aff), o_base.data_ptr(), o_out.data_ptr(),
+        lse_base.data_ptr(), lse_out.data_ptr(), workspace.data_ptr(), workspace.numel(),
+        _stream(stream))
+    _rc(rc, "orthros_forward_sft_lse")
+
+
+def backward_sft_workspace_bytes(shape: Shape, T: int, R: int) -> int:
+    return int(lib().orthros_backward_sft_workspace_bytes(ctypes.byref(shape.c()), int(T),
+                                                          int(R)))
+
+
+def backward_sft(shape: Shape, q_base, q_out, out_pos, k, v, affine: Affine, o_base, o_out,
+                 lse_base, lse_out, do_base, do_out, dq_base, dq_out, dk, dv, dgrad, workspace,
+                 stream=None):
+    """orthros_backward_sft: gradients with output rows only at the response positions."""
+    B, Hq, Hkv, d = shape.batch, shape.num_q_heads, shape.num_kv_heads, shape.head_dim
+    T, R = q_base.shape[1], q_out.shape[1]
+    dev, dt = q_base.device, shape.dtype
+    for t, n in ((q_base, "q_base"), (o_base, "o_base"), (do_base, "do_base"),
+                 (dq_base, "dq_base")):
+        _check(t, (B, T, Hq, d), dt, dev, n)
+    for t, n in ((q_out, "q_out"), (o_out, "o_out"), (do_out, "do_out"), (dq_out, "dq_out")):
+        _check(t, (B, R, Hq, d), dt, dev, n)
+    for t, n in ((k, "k"), (v, "v"), (dk, "dk"), (dv, "dv")):
+        _check(t, (B, T, Hkv, d), dt, dev, n)
+    _check(out_pos, (R,), torch.int32, dev, "out_pos")
+    _check(lse_base, (B, Hq, T), torch.float32, dev, "lse_base")
+    _check(lse_out, (B, Hq, R), torch.float32, dev, "lse_out")
+    for t in dgrad:
+        _check(t, (Hq * d,), torch.float32, dev, "scale-offset gradient")
+    aff = affine.c(Hq * d, dev)
+    g = _CAffineGrad(*(t.data_ptr() for t in dgrad))
+    rc = lib().orthros_backward_sft(
+        ctypes.byref(shape.c()), T, q_base.data_ptr(), q_out.data_ptr(), out_pos.data_ptr(), R,
+        k.data_ptr(), v.data_ptr(), ctypes.byref(aff), o_base.data_ptr(), o_out.data_ptr(),
+        lse_base.data_ptr(), lse_out.data_ptr(), do_base.data_ptr(), do_out.data_ptr(),
+        dq_base.data_ptr(), dq_out.data_ptr(), dk.data_ptr(), dv.data_ptr(), ctypes.byref(g),
+        workspace.data_ptr(), workspace.numel(), _stream(stream))
+    _rc(rc, "orthros_backward_sft")
 
 
 def read_device_status(workspace, clear: bool = False, stream=None) -> int:

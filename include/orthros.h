@@ -243,6 +243,31 @@ int orthros_backward_pt(const orthros_shape* shape, int64_t T,
                         const orthros_affine_grad* dgrad,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Supervised fine-tuning (§3.2: output rows only at the R response positions) for training:
+ * orthros_forward_sft_lse is orthros_forward_sft (without the cache) that also returns the
+ * rows' log-sum-exp, lse_base fp32 [B, H_q, T] and lse_out fp32 [B, H_q, R] (response rows in
+ * the order of out_pos); orthros_backward_sft is orthros_backward_pt for those rows: q_out,
+ * o_out, do_out, dq_out are [B, R, H_q, d] and lse_out is [B, H_q, R]; the base stream is as
+ * in pre-training. out_pos: device int32 [R], any order, clamped into [0, T). The workspace
+ * holds orthros_backward_sft_workspace_bytes(shape, T, R) bytes. */
+int orthros_forward_sft_lse(const orthros_shape* shape, int64_t T,
+                            const void* q_base, const void* q_out,
+                            const int32_t* out_pos, int64_t R,
+                            const void* k, const void* v, const orthros_affine* affine,
+                            void* o_base, void* o_out, float* lse_base, float* lse_out,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+size_t orthros_backward_sft_workspace_bytes(const orthros_shape* shape, int64_t T, int64_t R);
+int orthros_backward_sft(const orthros_shape* shape, int64_t T,
+                         const void* q_base, const void* q_out,
+                         const int32_t* out_pos, int64_t R,
+                         const void* k, const void* v, const orthros_affine* affine,
+                         const void* o_base, const void* o_out,
+                         const float* lse_base, const float* lse_out,
+                         const void* do_base, const void* do_out,
+                         void* dq_base, void* dq_out, void* dk, void* dv,
+                         const orthros_affine_grad* dgrad,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Paged key/value cache: a pool of fixed-size pages shared by the batch, as a serving engine
  * keeps it (the batched decoding that "Orthros: Phase-Aware Heterogeneous Attention for
  * Efficient Transformers" names as future work in §5). Token t of sequence b lives in page

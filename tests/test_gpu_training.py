@@ -119,3 +119,54 @@ def test_backward_is_deterministic():
     b = run_training(wl, device="cpu")[3]
     for n in a:
         np.testing.assert_array_equal(a[n], b[n], err_msg=n)
+
+
+SFT_CASES = [
+    # (B, Hq, Hkv, d, T, w, positions, dtype)
+    (2, 4, 2, 128, 200, 64, list(range(150, 200)), "bf16"),                       # suffix
+    (1, 8, 2, 128, 300, 100, [5, 299, 150, 151, 0, 64, 63, 200, 201, 202], "bf16"),  # unsorted
+    (1, 4, 1, 64, 130, 17, [129], "bf16"),                                        # one row
+    (1, 4, 2, 128, 96, 40, [10, 10, 50, 95, 95, 30] * 7, "bf16"),                 # R > 32, repeats
+    (1, 4, 2, 64, 90, 20, [89, 3, 45, 46, 47], "f32"),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,d,T,w,pos,dt", SFT_CASES)
+def test_sft_training_matches_oracle(B, Hq, Hkv, d, T, w, pos, dt):
+    wl = syn.Workload("sft_train", "sft", B, Hq, Hkv, d, w, dt, T, seed=800 + T + len(pos))
+    _say("sft training", wl, "rows", len(pos))
+    inp = syn.make_sft(wl, pos)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    R = len(pos)
+    g = torch.Generator().manual_seed(wl.seed + 5)
+    do_b = torch.randn(B, T, Hq, d, generator=g).to(tdt)
+    do_o = torch.randn(B, R, Hq, d, generator=g).to(tdt)
+    shape = ox.Shape(B, Hq, Hkv, d, w, tdt, T)
+    q_base, q_out, k, v = (inp[n].to(DEV).contiguous() for n in ("q_base", "q_out", "k", "v"))
+    aff = H.device_affine(inp["affine"], DEV)
+    op = torch.tensor(pos, dtype=torch.int32, device=DEV)
+    ob, oo = H.nan_like((B, T, Hq, d), tdt, DEV), H.nan_like((B, R, Hq, d), tdt, DEV)
+    lb, lo = H.nan_like((B, Hq, T), torch.float32, DEV), H.nan_like((B, Hq, R), torch.float32, DEV)
+    ws = ox.make_workspace(shape, DEV, sft_rows=R)
+    ox.forward_sft_lse(shape, q_base, q_out, op, k, v, aff, ob, oo, lb, lo, ws)
+    bws = torch.empty(ox.backward_sft_workspace_bytes(shape, T, R), dtype=torch.uint8, device=DEV)
+    dqb, dqo = H.nan_like((B, T, Hq, d), tdt, DEV), H.nan_like((B, R, Hq, d), tdt, DEV)
+    dk, dv = H.nan_like((B, T, Hkv, d), tdt, DEV), H.nan_like((B, T, Hkv, d), tdt, DEV)
+    dg = [H.nan_like((Hq * d,), torch.float32, DEV) for _ in range(4)]
+    ox.backward_sft(shape, q_base, q_out, op, k, v, aff, ob, oo, lb, lo, do_b.to(DEV),
+                    do_o.to(DEV), dqb, dqo, dk, dv, dg, bws)
+    torch.cuda.synchronize()
+    a64 = H.affine64(inp["affine"])
+    x = [H.to64(inp[n]) for n in ("q_base", "q_out", "k", "v")]
+    rb, ro = oracle.forward_sft(*x, pos, *a64, window=w)
+    H.assert_close(H.to64(ob), rb, tdt, "o_base")
+    H.assert_close(H.to64(oo), ro, tdt, "o_out")
+    rlb, rlo = oracle.lse_sft(x[0], x[1], x[2], pos, *a64, window=w)
+    lse_tol = 1e-4 if tdt == torch.float32 else 2e-2
+    for got, r, n in ((lb, rlb, "lse_base"), (lo, rlo, "lse_out")):
+        assert H.err_stats(H.to64(got), r)[0] <= lse_tol, n
+    gr = oracle.backward_sft(*x, pos, *a64, H.to64(do_b), H.to64(do_o), window=w)
+    got = dict(dq_base=dqb, dq_out=dqo, dk=dk, dv=dv, dalpha_b=dg[0], dbeta_b=dg[1],
+               dalpha_o=dg[2], dbeta_o=dg[3])
+    for n, t in got.items():
+        _grad_close(H.to64(t), gr[n], tdt, n)
