@@ -523,6 +523,106 @@ int forward_sft_impl(const orthros_shape* s, int64_t T, const void* q_base, cons
   return launch_rc(run_stage(ORTHROS_STAGE_MERGE, st, [&] { return launch_merge(mp, st); }));
 }
 
+// A prompt chunk over a contiguous cache (pg.table == nullptr) or a paged pool.
+int prefill_chunk_impl(const orthros_shape* s, int64_t past_len, int64_t C, const void* q_base,
+                       const void* q_out, const void* k, const void* v, const orthros_affine* aff,
+                       void* cache_k, void* cache_v, const PagedKV& pg, int32_t* cache_len,
+                       void* o_base, void* o_out, void* ws, size_t ws_bytes, hipStream_t st) {
+  int rc;
+  if (past_len < 0 || C < 1 || C > INT_MAX / 2 || past_len > INT_MAX / 2) return ORTHROS_E_INVALID;
+  if ((rc = check_affine(aff))) return rc;
+  if ((rc = check_ptrs({q_base, q_out, k, v, cache_k, cache_v, cache_len, o_base, o_out}))) return rc;
+  if ((rc = check_ws(s, ws, ws_bytes))) return rc;
+  if (past_len + C > s->capacity) return ORTHROS_E_CAPACITY;
+  const bool paged = pg.table != nullptr;
+
+  const int B = s->batch, Hq = s->num_q_heads, Hkv = s->num_kv_heads, d = s->head_dim;
+  const int G = Hq / Hkv;
+  const float scale = scale_of(s);
+  const WsLayout L = ws_layout(s);
+  char* wsc = static_cast<char*>(ws);
+  const int64_t n = past_len + C;  // keys after this chunk
+  // (sequence, kv head) strides of the cache: contiguous, or kv head within the sequence's pages
+  const idx_t c_sb = paged ? 0 : (idx_t)Hkv * s->capacity * d;
+  const idx_t c_sh = paged ? pg.k_sh : (idx_t)s->capacity * d;
+
+  if (paged) {
+    PagedWriteParams wp{k, v, cache_k, cache_v, cache_len, B, (int)C, Hkv, d, esize(s),
+                        s->capacity, pg};
+    rc = launch_rc(run_stage(ORTHROS_STAGE_CACHE_WRITE, st, [&] { return launch_paged_write(wp, st); }));
+  } else {
+    CacheWriteParams cw{k, v, cache_k, cache_v, cache_len, B, (int)C, Hkv, d, esize(s),
+                        s->capacity, past_len};
+    rc = launch_rc(run_stage(ORTHROS_STAGE_CACHE_WRITE, st, [&] { return launch_cache_write(cw, st); }));
+  }
+  if (rc) return rc;
+
+  if (s->dtype == ORTHROS_F32) {
+    RowsF32Params r{};
+    r.q = static_cast<const float*>(q_base);
+    r.q_sb = C * Hq * d; r.q_st = (idx_t)Hq * d; r.q_sh = d;
+    r.alpha = aff->alpha_base; r.beta = aff->beta_base;
+    r.k = static_cast<const float*>(cache_k); r.v = static_cast<const float*>(cache_v);
+    r.k_sb = c_sb; r.k_st = d; r.k_sh = c_sh;
+    r.pg = pg; r.cap = s->capacity;
+    r.o = static_cast<float*>(o_base);
+    r.o_sb = C * Hq * d; r.o_st = (idx_t)Hq * d; r.o_sh = d;
+    r.B = B; r.Hq = Hq; r.Hkv = Hkv; r.G = G; r.d = d; r.nrows = (int)C; r.t0 = (int)past_len;
+    r.window = s->window; r.scale = scale;
+    rc = launch_rc(run_stage(ORTHROS_STAGE_ROWS_F32, st, [&] { return launch_rows_f32(r, st); }));
+    if (rc) return rc;
+    RowsF32Params o = r;
+    o.q = static_cast<const float*>(q_out);
+    o.q_sb = (idx_t)Hq * d; o.q_st = 0;
+    o.alpha = aff->alpha_out; o.beta = aff->beta_out;
+    o.o = static_cast<float*>(o_out);
+    o.o_sb = (idx_t)Hq * d; o.o_st = 0;
+    o.nrows = 1; o.t0 = (int)(n - 1); o.window = INT_MAX;
+    return launch_rc(run_stage(ORTHROS_STAGE_ROWS_F32, st, [&] { return launch_rows_f32(o, st); }));
+  }
+
+  // Base rows of the chunk (positions past_len .. n-1) over the cache, which now holds them.
+  BandParams bp{};
+  bp.q = q_base; bp.q_sb = C * Hq * d; bp.q_st = (idx_t)Hq * d; bp.q_sh = d;
+  bp.alpha = aff->alpha_base; bp.beta = aff->beta_base;
+  bp.k = cache_k; bp.v = cache_v; bp.k_sb = c_sb; bp.k_st = d; bp.k_sh = c_sh;
+  bp.pg = pg;
+  bp.o = o_base; bp.o_sb = C * Hq * d; bp.o_st = (idx_t)Hq * d; bp.o_sh = d;
+  bp.B = B; bp.nrows = (int)C; bp.nkeys = (int)n; bp.t_first = (int)past_len; bp.pos = nullptr;
+  bp.Hq = Hq; bp.Hkv = Hkv; bp.G = G;
+  bp.window = s->window < (int)n ? s->window : (int)n;
+  bp.scale_log2 = scale * kLog2e;
+  rc = launch_rc(run_stage(ORTHROS_STAGE_BAND, st, [&] { return launch_band(bp, d, st); }));
+  if (rc) return rc;
+
+  // Output row at the chunk's last token over the whole cache.
+  SplitParams sp{};
+  sp.q_out = q_out; sp.q_sb = (idx_t)Hq * d; sp.q_sh = d;
+  sp.a_out = aff->alpha_out; sp.b_out = aff->beta_out;
+  sp.a_base = aff->alpha_base; sp.b_base = aff->beta_base;
+  sp.k = cache_k; sp.v = cache_v;
+  sp.k_sb = c_sb; sp.k_sh = c_sh; sp.k_st = d;
+  sp.pg = pg; sp.cap = s->capacity;
+  sp.n_fixed = n;
+  sp.R = 1;
+  sp.B = B; sp.Hq = Hq; sp.Hkv = Hkv; sp.G = G;
+  sp.HC = heads_per_chunk(G, false);
+  sp.nchunks = (G + sp.HC - 1) / sp.HC;
+  sp.window = s->window; sp.with_base = 0;
+  sp.nsplit = nsplit_for(n, (int64_t)B * Hkv * sp.nchunks);
+  sp.scale_log2 = scale * kLog2e;
+  sp.pm = reinterpret_cast<float*>(wsc + L.pm);
+  sp.pl = reinterpret_cast<float*>(wsc + L.pl);
+  sp.po = reinterpret_cast<float*>(wsc + L.po);
+  rc = launch_rc(run_stage(ORTHROS_STAGE_SPLIT_ROWS, st, [&] { return launch_split_rows(sp, d, st); }));
+  if (rc) return rc;
+  MergeParams mp{};
+  mp.pm = sp.pm; mp.pl = sp.pl; mp.po = sp.po;
+  mp.out0 = o_out; mp.o_sb0 = (idx_t)Hq * d; mp.o_sh0 = d;
+  mp.rows = B * Hq; mp.nsplit = sp.nsplit; mp.d = d; mp.Hq = Hq; mp.nstreams = 1; mp.bf16 = 1;
+  return launch_rc(run_stage(ORTHROS_STAGE_MERGE, st, [&] { return launch_merge(mp, st); }));
+}
+
 }  // namespace
 
 extern "C" {
@@ -731,86 +831,24 @@ int orthros_prefill_chunk(const orthros_shape* s, int64_t past_len, int64_t C,
                           size_t ws_bytes, hipStream_t st) {
   int rc = check_shape(s);
   if (rc) return rc;
-  if (past_len < 0 || C < 1 || C > INT_MAX / 2 || past_len > INT_MAX / 2) return ORTHROS_E_INVALID;
-  if ((rc = check_affine(aff))) return rc;
-  if ((rc = check_ptrs({q_base, q_out, k, v, cache_k, cache_v, cache_len, o_base, o_out}))) return rc;
+  return prefill_chunk_impl(s, past_len, C, q_base, q_out, k, v, aff, cache_k, cache_v,
+                            PagedKV{}, cache_len, o_base, o_out, ws, ws_bytes, st);
+}
+
+int orthros_prefill_chunk_paged(const orthros_shape* s, int64_t past_len, int64_t C,
+                                const void* q_base, const void* q_out, const void* k,
+                                const void* v, const orthros_affine* aff,
+                                const orthros_paged_kv* cache, int32_t* cache_len, void* o_base,
+                                void* o_out, void* ws, size_t ws_bytes, hipStream_t st) {
+  int rc = check_shape(s);
+  if (rc) return rc;
   if ((rc = check_ws(s, ws, ws_bytes))) return rc;
-  if (past_len + C > s->capacity) return ORTHROS_E_CAPACITY;
-
-  const int B = s->batch, Hq = s->num_q_heads, Hkv = s->num_kv_heads, d = s->head_dim;
-  const int G = Hq / Hkv;
-  const float scale = scale_of(s);
-  const WsLayout L = ws_layout(s);
-  char* wsc = static_cast<char*>(ws);
-  const int64_t n = past_len + C;  // keys after this chunk
-  const idx_t c_sb = (idx_t)Hkv * s->capacity * d, c_sh = (idx_t)s->capacity * d;
-
-  CacheWriteParams cw{k, v, cache_k, cache_v, cache_len, B, (int)C, Hkv, d, esize(s), s->capacity,
-                      past_len};
-  rc = launch_rc(run_stage(ORTHROS_STAGE_CACHE_WRITE, st, [&] { return launch_cache_write(cw, st); }));
-  if (rc) return rc;
-
-  if (s->dtype == ORTHROS_F32) {
-    RowsF32Params r{};
-    r.q = static_cast<const float*>(q_base);
-    r.q_sb = C * Hq * d; r.q_st = (idx_t)Hq * d; r.q_sh = d;
-    r.alpha = aff->alpha_base; r.beta = aff->beta_base;
-    r.k = static_cast<const float*>(cache_k); r.v = static_cast<const float*>(cache_v);
-    r.k_sb = c_sb; r.k_st = d; r.k_sh = c_sh;
-    r.o = static_cast<float*>(o_base);
-    r.o_sb = C * Hq * d; r.o_st = (idx_t)Hq * d; r.o_sh = d;
-    r.B = B; r.Hq = Hq; r.Hkv = Hkv; r.G = G; r.d = d; r.nrows = (int)C; r.t0 = (int)past_len;
-    r.window = s->window; r.scale = scale;
-    rc = launch_rc(run_stage(ORTHROS_STAGE_ROWS_F32, st, [&] { return launch_rows_f32(r, st); }));
-    if (rc) return rc;
-    RowsF32Params o = r;
-    o.q = static_cast<const float*>(q_out);
-    o.q_sb = (idx_t)Hq * d; o.q_st = 0;
-    o.alpha = aff->alpha_out; o.beta = aff->beta_out;
-    o.o = static_cast<float*>(o_out);
-    o.o_sb = (idx_t)Hq * d; o.o_st = 0;
-    o.nrows = 1; o.t0 = (int)(n - 1); o.window = INT_MAX;
-    return launch_rc(run_stage(ORTHROS_STAGE_ROWS_F32, st, [&] { return launch_rows_f32(o, st); }));
-  }
-
-  // Base rows of the chunk (positions past_len .. n-1) over the cache, which now holds them.
-  BandParams bp{};
-  bp.q = q_base; bp.q_sb = C * Hq * d; bp.q_st = (idx_t)Hq * d; bp.q_sh = d;
-  bp.alpha = aff->alpha_base; bp.beta = aff->beta_base;
-  bp.k = cache_k; bp.v = cache_v; bp.k_sb = c_sb; bp.k_st = d; bp.k_sh = c_sh;
-  bp.o = o_base; bp.o_sb = C * Hq * d; bp.o_st = (idx_t)Hq * d; bp.o_sh = d;
-  bp.B = B; bp.nrows = (int)C; bp.nkeys = (int)n; bp.t_first = (int)past_len; bp.pos = nullptr;
-  bp.Hq = Hq; bp.Hkv = Hkv; bp.G = G;
-  bp.window = s->window < (int)n ? s->window : (int)n;
-  bp.scale_log2 = scale * kLog2e;
-  rc = launch_rc(run_stage(ORTHROS_STAGE_BAND, st, [&] { return launch_band(bp, d, st); }));
-  if (rc) return rc;
-
-  // Output row at the chunk's last token over the whole cache.
-  SplitParams sp{};
-  sp.q_out = q_out; sp.q_sb = (idx_t)Hq * d; sp.q_sh = d;
-  sp.a_out = aff->alpha_out; sp.b_out = aff->beta_out;
-  sp.a_base = aff->alpha_base; sp.b_base = aff->beta_base;
-  sp.k = cache_k; sp.v = cache_v;
-  sp.k_sb = c_sb; sp.k_sh = c_sh; sp.k_st = d;
-  sp.n_fixed = n;
-  sp.R = 1;
-  sp.B = B; sp.Hq = Hq; sp.Hkv = Hkv; sp.G = G;
-  sp.HC = heads_per_chunk(G, false);
-  sp.nchunks = (G + sp.HC - 1) / sp.HC;
-  sp.window = s->window; sp.with_base = 0;
-  sp.nsplit = nsplit_for(n, (int64_t)B * Hkv * sp.nchunks);
-  sp.scale_log2 = scale * kLog2e;
-  sp.pm = reinterpret_cast<float*>(wsc + L.pm);
-  sp.pl = reinterpret_cast<float*>(wsc + L.pl);
-  sp.po = reinterpret_cast<float*>(wsc + L.po);
-  rc = launch_rc(run_stage(ORTHROS_STAGE_SPLIT_ROWS, st, [&] { return launch_split_rows(sp, d, st); }));
-  if (rc) return rc;
-  MergeParams mp{};
-  mp.pm = sp.pm; mp.pl = sp.pl; mp.po = sp.po;
-  mp.out0 = o_out; mp.o_sb0 = (idx_t)Hq * d; mp.o_sh0 = d;
-  mp.rows = B * Hq; mp.nsplit = sp.nsplit; mp.d = d; mp.Hq = Hq; mp.nstreams = 1; mp.bf16 = 1;
-  return launch_rc(run_stage(ORTHROS_STAGE_MERGE, st, [&] { return launch_merge(mp, st); }));
+  PagedKV pg{};
+  if ((rc = check_paged(s, cache, ws, &pg))) return rc;
+  // the banded kernel reads one table entry per 64-key tile
+  if (s->dtype == ORTHROS_BF16 && cache->page_size < 64) return ORTHROS_E_UNSUPPORTED;
+  return prefill_chunk_impl(s, past_len, C, q_base, q_out, k, v, aff, cache->k_pages,
+                            cache->v_pages, pg, cache_len, o_base, o_out, ws, ws_bytes, st);
 }
 
 int orthros_forward_sft(const orthros_shape* s, int64_t T, const void* q_base, const void* q_out,

@@ -201,8 +201,20 @@ __global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
   const int wv_s = __builtin_amdgcn_readfirstlane(wv);
   auto load_tile = [&](int e) {
     const int tb = tile_hi_s - kTK * e;
-    const unsigned char* kt = reinterpret_cast<const unsigned char*>(kbase) + (idx_t)tb * rowb;
-    const unsigned char* vt = reinterpret_cast<const unsigned char*>(vbase) + (idx_t)tb * rowb;
+    idx_t toff = (idx_t)tb * rowb;  // bytes from the (sequence, kv head) base to the tile
+    if (p.pg.table) {
+      // Paged pool: a 64-key tile lies inside one page (pages hold >= 64 rows, tiles start at
+      // multiples of 64), so one table entry (a scalar read) gives the tile's base.
+      int32_t page = p.pg.table[(idx_t)b * p.pg.tbl_sb + (tb >> p.pg.ps_log2)];
+      if (page < 0 || (int64_t)page >= p.pg.num_pages) {
+        __hip_atomic_fetch_or(p.pg.status, kStatusBadPage, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        page = 0;
+      }
+      // bytes: the page's start (k_sp elements of 2 bytes per page) plus the tile's rows
+      toff = (idx_t)page * p.pg.k_sp * 2 + (idx_t)(tb & ((1 << p.pg.ps_log2) - 1)) * rowb;
+    }
+    const unsigned char* kt = reinterpret_cast<const unsigned char*>(kbase) + toff;
+    const unsigned char* vt = reinterpret_cast<const unsigned char*>(vbase) + toff;
     unsigned char* st = smem + (e % kStages) * STAGEB;
     if (tb + kTK <= nk) {
 #pragma unroll

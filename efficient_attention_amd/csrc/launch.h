@@ -143,6 +143,7 @@ struct BandParams {
   void* o;
   idx_t o_sb, o_st, o_sh;
   const int32_t* pos;  // optional device row positions (nrows of them)
+  PagedKV pg;          // optional paged pool (k / v point at it, k_st = d): pages of >= 64 rows
   float* lse;          // optional: natural-log log-sum-exp of row r, head h at b lse_sb + h lse_sh + r
   idx_t lse_sb, lse_sh;
   int B, nrows, nkeys, t_first, Hq, Hkv, G, window;

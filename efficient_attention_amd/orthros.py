@@ -17,7 +17,8 @@ __all__ = [
     "OK", "E_INVALID", "E_UNSUPPORTED", "E_WORKSPACE", "E_CAPACITY", "E_LAUNCH",
     "STATUS_CACHE_FULL", "STATUS_BAD_PAGE", "STAGES", "OrthrosError", "Shape", "Affine",
     "PagedKV", "lib", "library_path", "workspace_bytes", "sft_workspace_bytes",
-    "make_workspace", "prefill", "prefill_chunk", "decode_step", "decode_step_paged",
+    "make_workspace", "prefill", "prefill_chunk", "prefill_chunk_paged", "decode_step",
+    "decode_step_paged",
     "paged_write", "forward_pt", "forward_sft", "forward_pt_lse", "backward_workspace_bytes",
     "backward_pt", "forward_sft_lse", "backward_sft_workspace_bytes", "backward_sft",
     "read_device_status", "status_string",
@@ -32,7 +33,8 @@ STAGES = ("cache_write", "band", "split_rows", "merge", "append", "rows_f32", "b
           "bwd_affine")
 EXPORTED_SYMBOLS = (
     "orthros_workspace_bytes", "orthros_sft_workspace_bytes", "orthros_prefill",
-    "orthros_prefill_chunk", "orthros_decode_step", "orthros_decode_step_paged",
+    "orthros_prefill_chunk", "orthros_prefill_chunk_paged", "orthros_decode_step",
+    "orthros_decode_step_paged",
     "orthros_paged_write", "orthros_forward_pt", "orthros_forward_sft",
     "orthros_forward_pt_lse", "orthros_backward_workspace_bytes", "orthros_backward_pt",
     "orthros_forward_sft_lse", "orthros_backward_sft_workspace_bytes", "orthros_backward_sft",
@@ -109,6 +111,9 @@ def lib() -> ctypes.CDLL:
         L.orthros_decode_step_paged.argtypes = [sp, vp, vp, vp, vp, ap, pp, vp, i64, vp, vp, vp,
                                                 sz, vp]
         L.orthros_decode_step_paged.restype = ctypes.c_int
+        L.orthros_prefill_chunk_paged.argtypes = [sp, i64, i64, vp, vp, vp, vp, ap, pp, vp, vp,
+                                                  vp, vp, sz, vp]
+        L.orthros_prefill_chunk_paged.restype = ctypes.c_int
         L.orthros_paged_write.argtypes = [sp, i64, vp, vp, pp, vp, vp, sz, vp]
         L.orthros_paged_write.restype = ctypes.c_int
         L.orthros_forward_pt_lse.argtypes = [sp, i64, vp, vp, vp, vp, ap, vp, vp, vp, vp, vp, sz,
@@ -338,6 +343,29 @@ def decode_step_paged(shape: Shape, q_base, q_out, k_new, v_new, affine: Affine,
         int(max_len_hint), o_base.data_ptr(), o_out.data_ptr(), workspace.data_ptr(),
         workspace.numel(), _stream(stream))
     _rc(rc, "orthros_decode_step_paged")
+
+
+def prefill_chunk_paged(shape: Shape, past_len: int, q_base, q_out, k, v, affine: Affine,
+                        cache: PagedKV, cache_len, o_base, o_out, workspace, stream=None):
+    """orthros_prefill_chunk_paged: C more prompt tokens into a paged cache."""
+    B, Hq, Hkv, d = shape.batch, shape.num_q_heads, shape.num_kv_heads, shape.head_dim
+    C = q_base.shape[1]
+    dev, dt = q_base.device, shape.dtype
+    _check(q_base, (B, C, Hq, d), dt, dev, "q_base")
+    _check(q_out, (B, 1, Hq, d), dt, dev, "q_out")
+    _check(k, (B, C, Hkv, d), dt, dev, "k")
+    _check(v, (B, C, Hkv, d), dt, dev, "v")
+    _check(cache_len, (B,), torch.int32, dev, "cache_len")
+    _check(o_base, (B, C, Hq, d), dt, dev, "o_base")
+    _check(o_out, (B, 1, Hq, d), dt, dev, "o_out")
+    aff = affine.c(Hq * d, dev)
+    pc = cache.c(shape, dev)
+    rc = lib().orthros_prefill_chunk_paged(
+        ctypes.byref(shape.c()), int(past_len), C, q_base.data_ptr(), q_out.data_ptr(),
+        k.data_ptr(), v.data_ptr(), ctypes.byref(aff), ctypes.byref(pc), cache_len.data_ptr(),
+        o_base.data_ptr(), o_out.data_ptr(), workspace.data_ptr(), workspace.numel(),
+        _stream(stream))
+    _rc(rc, "orthros_prefill_chunk_paged")
 
 
 def paged_write(shape: Shape, k, v, cache: PagedKV, cache_len, workspace, stream=None):

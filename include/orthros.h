@@ -303,6 +303,19 @@ int orthros_decode_step_paged(const orthros_shape* shape,
                               void* o_base, void* o_out,
                               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* orthros_prefill_chunk over a paged cache (§3.2 prefilling, the prompt arriving in chunks):
+ * the chunk's keys/values go to positions past_len .. past_len+C-1 through the table
+ * (cache_len[b] must equal past_len on entry and becomes past_len + C), its base rows' windows
+ * and the output row read the cached tokens through the table. Same outputs as
+ * orthros_prefill_chunk. bf16 calls need pages of at least 64 rows (ORTHROS_E_UNSUPPORTED
+ * otherwise); a bad table entry sets ORTHROS_STATUS_BAD_PAGE. */
+int orthros_prefill_chunk_paged(const orthros_shape* shape, int64_t past_len, int64_t C,
+                                const void* q_base, const void* q_out,
+                                const void* k, const void* v, const orthros_affine* affine,
+                                const orthros_paged_kv* cache, int32_t* cache_len,
+                                void* o_base, void* o_out,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Appends T tokens per sequence to a paged cache: k, v [B, T, H_kv, d] go to positions
  * cache_len[b] .. cache_len[b] + T - 1 through the table, then cache_len[b] += T (prefilling a
  * prompt into pages, §3.2: the base tokens write the cache). A sequence without room for all T

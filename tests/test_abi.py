@@ -277,3 +277,19 @@ def test_paged_calls_reject_bad_shape_lengths_and_workspace():
     assert _paged_write(_shape(), T=0) == ox.E_INVALID
     assert _paged_write(_shape(), k=None) == ox.E_INVALID
     assert _paged_write(_shape(), ws_bytes=16) == ox.E_WORKSPACE
+
+
+def test_paged_prefill_chunk_validation():
+    L = ox.lib()
+    shape = _shape()  # bf16, capacity 1024
+
+    def call(cache, past=0, C=16):
+        return L.orthros_prefill_chunk_paged(
+            ctypes.byref(shape), past, C, FAKE, FAKE, FAKE, FAKE, ctypes.byref(_aff()),
+            ctypes.byref(cache), FAKE, FAKE, FAKE, FAKE,
+            L.orthros_workspace_bytes(ctypes.byref(shape)), None)
+    # the banded kernel reads one table entry per 64-key tile: bf16 needs pages of >= 64 rows
+    assert call(_paged(page_size=32, max_pages=32)) == ox.E_UNSUPPORTED
+    assert call(_paged(page_size=48)) == ox.E_INVALID
+    assert call(_paged(), past=-1) == ox.E_INVALID
+    assert call(_paged(), past=1020, C=8) == ox.E_CAPACITY

@@ -240,3 +240,75 @@ def test_paged_decode_full_and_bad_page_status():
     changed = (kp != kp_before) & ~(torch.isnan(kp) & torch.isnan(kp_before))
     slots = torch.nonzero(changed.any(dim=3).any(dim=1)).tolist()  # [page, slot] pairs
     assert slots == [[int(table[2, 20 // ps]), 20 % ps]]
+
+
+PREFILL_CASES = [
+    # (B, Hq, Hkv, d, page size, chunks, w, dtype)
+    (2, 8, 2, 128, 64, [100, 37, 200], 64, "bf16"),   # windows reach back across chunks
+    (1, 4, 4, 128, 128, [130, 130], 300, "bf16"),     # window longer than everything
+    (1, 4, 2, 64, 64, [65, 64, 63], 65, "bf16"),       # d 64, tile-boundary chunk sizes
+    (2, 4, 2, 64, 16, [40, 33], 20, "f32"),            # fp32 rows take any page size
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,d,ps,chunks,w,dt", PREFILL_CASES)
+def test_paged_prefill_in_chunks_then_decode_matches_oracle(B, Hq, Hkv, d, ps, chunks, w, dt):
+    P = sum(chunks)
+    steps = 2
+    wl = syn.Workload("paged_chunks", "prefill", B, Hq, Hkv, d, w, dt, P, seed=1100 + P + ps)
+    _say("paged prefill chunks", wl, chunks, "page", ps)
+    inp = syn.make_prefill(wl)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    max_pages = math.ceil((P + steps) / ps) + 1
+    num_pages = B * max_pages + 2
+    g = torch.Generator().manual_seed(wl.seed + 3)
+    table = torch.randperm(num_pages, generator=g)[:B * max_pages].view(B, max_pages)
+    table = table.to(torch.int32).to(DEV)
+    kp = torch.full((num_pages, Hkv, ps, d), float("nan"), dtype=tdt, device=DEV)
+    vp = torch.full_like(kp, float("nan"))
+    cache = ox.PagedKV(kp, vp, table)
+    shape = ox.Shape(B, Hq, Hkv, d, w, tdt, max_pages * ps)
+    cl = torch.zeros(B, dtype=torch.int32, device=DEV)
+    ws = ox.make_workspace(shape, DEV)
+    aff = H.device_affine(inp["affine"], DEV)
+    a64 = H.affine64(inp["affine"])
+    tbl = table.cpu().numpy()
+    rk, rv = H.to64(kp), H.to64(vp)
+    hk = np.zeros((B, 0, Hkv, d))
+    hv = np.zeros((B, 0, Hkv, d))
+    past = 0
+    for c in chunks:
+        sl = slice(past, past + c)
+        qo = torch.randn(B, 1, Hq, d, generator=g).to(tdt)
+        ob = H.nan_like((B, c, Hq, d), tdt, DEV)
+        oo = H.nan_like((B, 1, Hq, d), tdt, DEV)
+        kc, vc = inp["k"][:, sl].contiguous(), inp["v"][:, sl].contiguous()
+        ox.prefill_chunk_paged(shape, past, inp["q_base"][:, sl].contiguous().to(DEV), qo.to(DEV),
+                               kc.to(DEV), vc.to(DEV), aff, cache, cl, ob, oo, ws)
+        torch.cuda.synchronize()
+        rb, ro, hk, hv, _ = oracle.prefill_chunk(hk, hv, past, H.to64(inp["q_base"][:, sl]),
+                                                 H.to64(qo), H.to64(kc), H.to64(vc), *a64,
+                                                 window=w)
+        rk, rv, lens, _ = oracle.paged_write(rk, rv, tbl, np.full(B, past), H.to64(kc),
+                                             H.to64(vc))
+        H.assert_close(H.to64(ob), rb, tdt, f"o_base chunk at {past}")
+        H.assert_close(H.to64(oo), ro, tdt, f"o_out chunk at {past}")
+        past += c
+        assert cl.cpu().tolist() == lens.tolist() == [past] * B
+    np.testing.assert_array_equal(H.to64(kp), rk)
+    np.testing.assert_array_equal(H.to64(vp), rv)
+    lens = np.full(B, P)
+    for s in range(steps):
+        x = [torch.randn(B, Hq, d, generator=g).to(tdt) for _ in range(2)]
+        x += [torch.randn(B, Hkv, d, generator=g).to(tdt) for _ in range(2)]
+        ob = H.nan_like((B, Hq, d), tdt, DEV)
+        oo = H.nan_like((B, Hq, d), tdt, DEV)
+        ox.decode_step_paged(shape, *(t.to(DEV) for t in x), aff, cache, cl, P + s, ob, oo, ws)
+        torch.cuda.synchronize()
+        rb, ro, rk, rv, lens, _ = oracle.decode_step_paged(rk, rv, tbl, lens,
+                                                           *(H.to64(t) for t in x), *a64,
+                                                           window=w)
+        H.assert_close(H.to64(ob), rb, tdt, f"decode o_base step {s}")
+        H.assert_close(H.to64(oo), ro, tdt, f"decode o_out step {s}")
+    np.testing.assert_array_equal(H.to64(kp), rk)
+    assert ox.read_device_status(ws) == 0
