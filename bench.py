@@ -295,15 +295,26 @@ def bench_training(wl, steps, warmup, dev):
                 pairs=pairs, d=d)
 
 
-def bench_prefill_chunked(wl, chunk, steps, warmup, dev, inp):
-    """The same prompt prefilled in chunks of `chunk` tokens (cache grows chunk by chunk)."""
+def bench_prefill_chunked(wl, chunk, steps, warmup, dev, inp, page_size=0):
+    """The same prompt prefilled in chunks of `chunk` tokens (cache grows chunk by chunk); with
+    page_size > 0 into a shuffled pool of pages (cache_len is reset to 0 at the start of each
+    step, one small fill kernel)."""
     B, P, Hq, d = inp["q_base"].shape
     Hkv = inp["k"].shape[2]
-    shape = ox.Shape(B, Hq, Hkv, d, wl.window, torch.bfloat16, P)
+    cap = P if not page_size else -(-P // page_size) * page_size
+    shape = ox.Shape(B, Hq, Hkv, d, wl.window, torch.bfloat16, cap)
     aff = ox.Affine(*inp["affine"])
-    ck = torch.empty(B, Hkv, P, d, dtype=torch.bfloat16, device=dev)
-    cv = torch.empty_like(ck)
     cl = torch.zeros(B, dtype=torch.int32, device=dev)
+    if page_size:
+        max_pages = cap // page_size
+        g = torch.Generator(device=dev)
+        g.manual_seed(wl.seed + 13)
+        table = torch.randperm(B * max_pages, generator=g, device=dev).view(B, max_pages)
+        kp = torch.empty(B * max_pages, Hkv, page_size, d, dtype=torch.bfloat16, device=dev)
+        cache = ox.PagedKV(kp, torch.empty_like(kp), table.to(torch.int32).contiguous())
+    else:
+        ck = torch.empty(B, Hkv, P, d, dtype=torch.bfloat16, device=dev)
+        cv = torch.empty_like(ck)
     ws = ox.make_workspace(shape, dev)
     starts = list(range(0, P, chunk))
     views = [(s0, inp["q_base"][:, s0:s0 + chunk].contiguous(), inp["k"][:, s0:s0 + chunk].contiguous(),
@@ -312,6 +323,12 @@ def bench_prefill_chunked(wl, chunk, steps, warmup, dev, inp):
     oo = torch.empty(B, 1, Hq, d, dtype=torch.bfloat16, device=dev)
 
     def step():
+        if page_size:
+            cl.zero_()
+            for (s0, q, k, v), ob in zip(views, obs):
+                ox.prefill_chunk_paged(shape, s0, q, inp["q_out"], k, v, aff, cache, cl, ob, oo,
+                                       ws)
+            return
         for (s0, q, k, v), ob in zip(views, obs):
             ox.prefill_chunk(shape, s0, q, inp["q_out"], k, v, aff, ck, cv, cl, ob, oo, ws)
 
@@ -325,7 +342,8 @@ def bench_prefill_chunked(wl, chunk, steps, warmup, dev, inp):
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
     stages = ox.timing_end()
-    log(f"prefill in {len(starts)} chunks of {chunk}: {ms:.3f} ms/step; stages {stages}")
+    log(f"prefill in {len(starts)} chunks of {chunk}" + (f" into {page_size}-token pages" if page_size else "")
+        + f": {ms:.3f} ms/step; stages {stages}")
     return dict(ms=ms, chunks=len(starts), band_ms=stages["band"][0] / max(steps, 1))
 
 
@@ -466,6 +484,14 @@ def main():
             "workload": f"{wl.name} in chunks of 8192", "chunks": ch["chunks"],
             "ms_per_step": round(ch["ms"], 4), "tokens_per_s": round(tokens / (ch["ms"] / 1e3), 1),
             "band_frac": round(base_flops / (ch["band_ms"] / 1e3) / PEAK_BF16_FLOPS, 4),
+        }
+        chp = bench_prefill_chunked(wl, 8192, max(2, args.steps // 3), 1, dev, pf["inp"],
+                                    page_size=64)
+        rec["prefill_chunked_paged"] = {
+            "workload": f"{wl.name} in chunks of 8192 into a shuffled pool of 64-token pages",
+            "chunks": chp["chunks"], "ms_per_step": round(chp["ms"], 4),
+            "tokens_per_s": round(tokens / (chp["ms"] / 1e3), 1),
+            "band_frac": round(base_flops / (chp["band_ms"] / 1e3) / PEAK_BF16_FLOPS, 4),
         }
         sw = syn.WORKLOADS["pt_1p3b_2k"]
         sf = bench_sft(sw, 512, args.steps, args.warmup, dev)
