@@ -358,12 +358,14 @@ __global__ __launch_bounds__(64 * kKNW, 2) void bwd_kv_kernel(BwdKVParams p) {
   {
     constexpr int LROWS = 1024 / ROWB;
     constexpr int NV = KB / LROWS / kKNW;
-    const unsigned char* vg = reinterpret_cast<const unsigned char*>(static_cast<const uint16_t*>(p.v) + (idx_t)b * T * kst + (idx_t)g * D);
+    // 64-bit base at the block's first key; per-lane offsets stay within the block
+    const unsigned char* vg = reinterpret_cast<const unsigned char*>(
+        static_cast<const uint16_t*>(p.v) + ((idx_t)b * T + k0) * kst + (idx_t)g * D);
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int r = (wv * NV + i) * LROWS + lane / NCH;
       const int c = lane % NCH;
-      const int kr = k0 + r < T ? k0 + r : T - 1;
+      const int kr = k0 + r < T ? r : T - 1 - k0;  // rows past the end re-read the last key
       copy_to_lds(vg, (uint32_t)kr * (uint32_t)(kst * 2) + 16u * (uint32_t)(c ^ (r % NCH)),
                   lds0 + (uint32_t)(wk_s * NV + i) * 1024u);
     }
