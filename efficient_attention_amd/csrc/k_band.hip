@@ -199,13 +199,20 @@ __global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
   }
   const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) unsigned char*)smem);
   const int wv_s = __builtin_amdgcn_readfirstlane(wv);
+  // Paged pool: a 64-key tile lies inside one page (pages hold >= 64 rows, tiles start at
+  // multiples of 64), so one table entry (a scalar read) gives the tile's base. Tiles are
+  // requested in order 0, 1, 2, ...; the entry of the next one is read a request ahead.
+  auto page_of = [&](int e) -> int32_t {
+    const int tb = tile_hi_s - kTK * (e < ntiles_s ? e : ntiles_s - 1);
+    return p.pg.table[(idx_t)b * p.pg.tbl_sb + (tb >> p.pg.ps_log2)];
+  };
+  int32_t next_page = p.pg.table ? page_of(0) : 0;
   auto load_tile = [&](int e) {
     const int tb = tile_hi_s - kTK * e;
     idx_t toff = (idx_t)tb * rowb;  // bytes from the (sequence, kv head) base to the tile
     if (p.pg.table) {
-      // Paged pool: a 64-key tile lies inside one page (pages hold >= 64 rows, tiles start at
-      // multiples of 64), so one table entry (a scalar read) gives the tile's base.
-      int32_t page = p.pg.table[(idx_t)b * p.pg.tbl_sb + (tb >> p.pg.ps_log2)];
+      int32_t page = next_page;
+      next_page = page_of(e + 1);
       if (page < 0 || (int64_t)page >= p.pg.num_pages) {
         __hip_atomic_fetch_or(p.pg.status, kStatusBadPage, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         page = 0;
