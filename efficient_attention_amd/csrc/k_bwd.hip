@@ -447,14 +447,17 @@ __global__ __launch_bounds__(64 * kKNW, 2) void bwd_kv_kernel(BwdKVParams p) {
     }
   };
 
-  uint32_t rd_off[NKS];
-#pragma unroll
-  for (int s = 0; s < NKS; ++s) rd_off[s] = slot_off<NCH>(j, 2 * s + hh);
-  uint32_t tr_off[2][NDT];
-  tr_offsets<D>(lane, tr_off);
-  uint32_t vb_off[NKS];  // V^T B operand: key 32 wv + j, channels 16 s + 8 hh ..
-#pragma unroll
-  for (int s = 0; s < NKS; ++s) vb_off[s] = slot_off<NCH>(32 * wv + j, 2 * s + hh);
+  // LDS offsets, derived inside the loop from two registers (the swizzle is an XOR):
+  //   row read of channel slot 2 s + hh of row j:  rd0 ^ 32 s
+  //   value block, key 32 wv + j:                   32 wv ROWB + (rd0 ^ 32 s)
+  //   transposed read, channel tile dt:             tr0 ^ 64 dt, and 8 rows on:
+  //                                                 ((tr0 ^ 64 dt) ^ kTrHi) + 8 ROWB
+  const uint32_t rd0_init = slot_off<NCH>(j, hh);
+  uint32_t tr_init[2][NDT];
+  tr_offsets<D>(lane, tr_init);
+  const uint32_t tr0_init = tr_init[0][0];
+  constexpr uint32_t kTrHi = NCH == 16 ? 128u : 0u;  // the swizzle bit that 8 rows flip
+  const uint32_t vrow = (uint32_t)(32 * wv * ROWB);
 
   f32x16 dK[NDT], dV[NDT];
 #pragma unroll
@@ -505,16 +508,18 @@ __global__ __launch_bounds__(64 * kKNW, 2) void bwd_kv_kernel(BwdKVParams p) {
     }
     if (need) {
       const unsigned char* sd = sq + QTB;
+      uint32_t rd0 = rd0_init, tr0 = tr0_init;
+      asm volatile("" : "+v"(rd0), "+v"(tr0));  // derive the offsets here, not before the loop
       f32x16 S = zero16, dP = zero16;
 #pragma unroll
       for (int s = 0; s < NKS; ++s) {
-        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(sq + rd_off[s]);
+        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(sq + (rd0 ^ (32u * s)));
         S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[s], S, 0, 0, 0);
       }
 #pragma unroll
       for (int s = 0; s < NKS; ++s) {
-        const bf16x8 da = *reinterpret_cast<const bf16x8*>(sd + rd_off[s]);
-        const bf16x8 vbv = *reinterpret_cast<const bf16x8*>(smem + vb_off[s]);
+        const bf16x8 da = *reinterpret_cast<const bf16x8*>(sd + (rd0 ^ (32u * s)));
+        const bf16x8 vbv = *reinterpret_cast<const bf16x8*>(smem + vrow + (rd0 ^ (32u * s)));
         dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vbv, dP, 0, 0, 0);
       }
       // Register r holds row i(r) = 8 (r / 4) + 4 hh + r % 4 of the tile, column key j.
@@ -543,11 +548,12 @@ __global__ __launch_bounds__(64 * kKNW, 2) void bwd_kv_kernel(BwdKVParams p) {
       for (int k2 = 0; k2 < 2; ++k2) {
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-          const s16x4 dlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sd + 16 * k2 * ROWB + tr_off[0][dt]));
-          const s16x4 dhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sd + 16 * k2 * ROWB + tr_off[1][dt]));
+          const uint32_t tlo = tr0 ^ (64u * dt), thi = (tlo ^ kTrHi) + 8 * ROWB;
+          const s16x4 dlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sd + 16 * k2 * ROWB + tlo));
+          const s16x4 dhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sd + 16 * k2 * ROWB + thi));
           dV[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cat_tr(dlo, dhi), Pb[k2], dV[dt], 0, 0, 0);
-          const s16x4 qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sq + 16 * k2 * ROWB + tr_off[0][dt]));
-          const s16x4 qhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sq + 16 * k2 * ROWB + tr_off[1][dt]));
+          const s16x4 qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sq + 16 * k2 * ROWB + tlo));
+          const s16x4 qhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sq + 16 * k2 * ROWB + thi));
           dK[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cat_tr(qlo, qhi), Zb[k2], dK[dt], 0, 0, 0);
         }
       }
