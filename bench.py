@@ -50,9 +50,9 @@ CSRC = os.path.join(ROOT, "efficient_attention_amd", "csrc")
 # in the same run. Recorded with the sha256 of the kernel's sources: when they change, the
 # figure no longer describes the kernel and `traffic` is reported as null.
 TRAFFIC = {
-    "band_kernel": {"sha": "815165b5561f0ce5", "bytes_per_launch": 2.7554e+09},
-    "split_rows_kernel": {"sha": "9894888fdb3c3a5b", "bytes_per_launch": 8.5975e+09},
-    "split_rows_kernel_paged": {"sha": "9894888fdb3c3a5b", "bytes_per_launch": 8.5979e+09},
+    "band_kernel": {"sha": "3fe21cdf179013fe", "bytes_per_launch": 2.7813e+09},
+    "split_rows_kernel": {"sha": "1e7cd9911efdb7dd", "bytes_per_launch": 8.5975e+09},
+    "split_rows_kernel_paged": {"sha": "1e7cd9911efdb7dd", "bytes_per_launch": 8.5979e+09},
 }
 
 
