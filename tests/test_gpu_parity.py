@@ -77,6 +77,40 @@ def test_prefill_matches_oracle(B, Hq, Hkv, d, P, w, dt):
     assert torch.isnan(g["cache_k"][:, :, P:].float()).all()
 
 
+def test_prefill_cache_is_ready_on_the_callers_stream():
+    """Work enqueued after the call on the caller's own stream (here a non-default one, not
+    synchronised in between) already sees the whole cache and cache_len."""
+    wl = _case(batch=2, q_heads=8, kv_heads=2, head_dim=128, length=1000, window=200,
+               dtype="bf16", seed=321)
+    _say("prefill on a side stream", wl)
+    inp = syn.make_prefill(wl)
+    tdt = torch.bfloat16
+    q_base, q_out, k, v = (inp[n].to(DEV).contiguous() for n in ("q_base", "q_out", "k", "v"))
+    B, P, Hq, d = q_base.shape
+    Hkv = k.shape[2]
+    shape = ox.Shape(B, Hq, Hkv, d, wl.window, tdt, P)
+    cache_k = H.nan_like((B, Hkv, P, d), tdt, DEV)
+    cache_v = H.nan_like((B, Hkv, P, d), tdt, DEV)
+    cache_len = torch.full((B,), -7, dtype=torch.int32, device=DEV)
+    o_base = H.nan_like((B, P, Hq, d), tdt, DEV)
+    o_out = H.nan_like((B, 1, Hq, d), tdt, DEV)
+    ws = ox.make_workspace(shape, DEV)
+    aff = H.device_affine(inp["affine"], DEV)
+    torch.cuda.synchronize()
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        ox.prefill(shape, q_base, q_out, k, v, aff, cache_k, cache_v, cache_len, o_base, o_out,
+                   ws, stream=st)
+        ck = cache_k.clone()
+        cv = cache_v.clone()
+        ln = cache_len.clone()
+    torch.cuda.synchronize()
+    _, _, rk, rv, _ = H.oracle_prefill(inp, wl.window)
+    np.testing.assert_array_equal(H.cache_as_tokens(ck, P), rk)
+    np.testing.assert_array_equal(H.cache_as_tokens(cv, P), rv)
+    assert ln.cpu().tolist() == [P] * B
+
+
 def test_prefill_is_deterministic():
     wl = _case(batch=1, q_heads=8, kv_heads=2, length=700, window=256, seed=5)
     _say("determinism", wl)
