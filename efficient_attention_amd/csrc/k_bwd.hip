@@ -409,8 +409,9 @@ __global__ __launch_bounds__(64 * kKNW, 2) void bwd_kv_kernel(BwdKVParams p) {
     coff[i] = (uint32_t)r * (uint32_t)(p.Hq * D * 2) + 16u * (uint32_t)(c ^ (r % NCH));
   }
   const uint32_t rowq = (uint32_t)p.Hq * D * 2;
-  float ld_lse = 0.f, ld_D = 0.f;  // thread tid < 32: row tid of the next tile
-  int ld_pos = -1;                 // its position, -1 past the last row
+  // The rows' lse, D and raw positions go straight to LDS as well (4 bytes per lane, lanes
+  // 0..31 of wavefront 0; rows past the end re-read the last row; a stream without a row list
+  // copies its lse into the unused position slot), so no register ever waits for them.
   auto load_item = [&](int i, int slot) {
     int st, hd, qt;
     item(i, st, hd, qt);
@@ -430,20 +431,14 @@ __global__ __launch_bounds__(64 * kKNW, 2) void bwd_kv_kernel(BwdKVParams p) {
     }
     if (tid < kQW) {
       const int r = t0 + tid < NR ? t0 + tid : NR - 1;
-      const idx_t lr = ((idx_t)b * p.Hq + hd) * NR + r;
-      ld_lse = p.lse[st][lr] * kLog2e;
-      ld_D = p.D[st][lr];
-      int ps = p.pos[st] ? p.pos[st][r] : r;
-      ps = ps < 0 ? 0 : (ps > T - 1 ? T - 1 : ps);
-      ld_pos = t0 + tid < NR ? ps : -1;
-    }
-  };
-  auto store_rowdata = [&](int slot) {
-    if (tid < kQW) {
-      float* f = reinterpret_cast<float*>(smem + VBYTES + slot * STG + 2 * QTB);
-      f[tid] = ld_lse;
-      f[kQW + tid] = ld_D;
-      reinterpret_cast<int*>(f)[2 * kQW + tid] = ld_pos;
+      const idx_t lr0 = ((idx_t)b * p.Hq + hd) * NR;
+      const float* lb = p.lse[st] + lr0;
+      copy_to_lds_b32(lb, (uint32_t)r * 4u, sb + 2 * QTB);
+      copy_to_lds_b32(p.D[st] + lr0, (uint32_t)r * 4u, sb + 2 * QTB + kQW * 4);
+      if (p.pos[st])
+        copy_to_lds_b32(p.pos[st], (uint32_t)r * 4u, sb + 2 * QTB + 2 * kQW * 4);
+      else
+        copy_to_lds_b32(lb, (uint32_t)r * 4u, sb + 2 * QTB + 2 * kQW * 4);
     }
   };
 
@@ -471,10 +466,7 @@ __global__ __launch_bounds__(64 * kKNW, 2) void bwd_kv_kernel(BwdKVParams p) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) zero16[r] = 0.f;
 
-  if (nitems > 0) {
-    load_item(0, 0);
-    store_rowdata(0);
-  }
+  if (nitems > 0) load_item(0, 0);
   wait_lds_copies();
   __syncthreads();
   for (int i = 0; i < nitems; ++i) {
@@ -485,10 +477,18 @@ __global__ __launch_bounds__(64 * kKNW, 2) void bwd_kv_kernel(BwdKVParams p) {
     (void)hd;
     const int t0 = qt * kQW;
     const int w = wst[st];
+    const int NR = p.nrows[st];
     const bool listed = p.pos[st] != nullptr;
     const unsigned char* sq = smem + VBYTES + slot * STG;
     const float* rowf = reinterpret_cast<const float*>(sq + 2 * QTB);
     const int* rowp = reinterpret_cast<const int*>(rowf + 2 * kQW);
+    // Position of tile row r, -1 past the last row: its own index, or its row-list entry
+    // clamped into [0, T).
+    auto row_pos = [&](int r, int raw) {
+      int ps = listed ? raw : t0 + r;
+      ps = ps < 0 ? 0 : (ps > T - 1 ? T - 1 : ps);
+      return t0 + r < NR ? ps : -1;
+    };
     // rows against keys k0w .. k0w+31: any pair with key <= t < key + w?
     bool need, fl;
     if (!listed) {
@@ -501,7 +501,10 @@ __global__ __launch_bounds__(64 * kKNW, 2) void bwd_kv_kernel(BwdKVParams p) {
         const int4 p4 = *reinterpret_cast<const int4*>(rowp + 8 * q4 + 4 * hh);
         const int pv[4] = {p4.x, p4.y, p4.z, p4.w};
 #pragma unroll
-        for (int k = 0; k < 4; ++k) any = any || (pv[k] >= k0w && pv[k] <= k0w + 31 + w - 1);
+        for (int k = 0; k < 4; ++k) {
+          const int t = row_pos(8 * q4 + 4 * hh + k, pv[k]);
+          any = any || (t >= 0 && t >= k0w && t <= k0w + 31 + w - 1);
+        }
       }
       need = __builtin_amdgcn_ballot_w64(any) != 0 && k0w < T;
       fl = false;
@@ -528,18 +531,20 @@ __global__ __launch_bounds__(64 * kKNW, 2) void bwd_kv_kernel(BwdKVParams p) {
       for (int q4 = 0; q4 < 4; ++q4) {
         const f32x4 l4 = *reinterpret_cast<const f32x4*>(rowf + 8 * q4 + 4 * hh);
         const f32x4 d4 = *reinterpret_cast<const f32x4*>(rowf + kQW + 8 * q4 + 4 * hh);
-        const int4 p4 = *reinterpret_cast<const int4*>(rowp + 8 * q4 + 4 * hh);
+        int4 p4 = {0, 0, 0, 0};
+        if (!fl && listed) p4 = *reinterpret_cast<const int4*>(rowp + 8 * q4 + 4 * hh);
         const int pv[4] = {p4.x, p4.y, p4.z, p4.w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const int r = 4 * q4 + k;
           float s = S[r];
           if (!fl) {
-            const int t = pv[k];  // -1 past the last row: masked
+            const int t = row_pos(8 * q4 + 4 * hh + k, pv[k]);  // -1 past the last row: masked
             const bool ok = key <= t && key > t - w && kvalid;
             s = ok ? s : kNegInf;
           }
-          const float pr = fast_exp2(s - l4[k]);
+          // scores are in log2 units, lse in natural log
+          const float pr = fast_exp2(fmaf(l4[k], -kLog2e, s));
           Pb[r >> 3][r & 7] = (__bf16)pr;
           Zb[r >> 3][r & 7] = (__bf16)(pr * (dP[r] - d4[k]));
         }
@@ -558,7 +563,6 @@ __global__ __launch_bounds__(64 * kKNW, 2) void bwd_kv_kernel(BwdKVParams p) {
         }
       }
     }
-    if (i + 1 < nitems) store_rowdata(slot ^ 1);
     wait_lds_copies();
     __syncthreads();
   }

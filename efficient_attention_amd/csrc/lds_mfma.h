@@ -39,7 +39,25 @@ __device__ __forceinline__ void copy_to_lds(const void* base, uint32_t off, uint
       : "s"(lds), "v"(off), "s"(base)
       : "memory");
 }
+// The same with 4 bytes per lane: active lane i fills bytes 4 i .. 4 i + 3 from `lds`.
+__device__ __forceinline__ void copy_to_lds_b32(const void* base, uint32_t off, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(off), "s"(base)
+      : "memory");
+}
 __device__ __forceinline__ void wait_lds_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Waits until at most N of this wavefront's copies (and other vector memory loads) are in flight.
+template <int N>
+__device__ __forceinline__ void wait_lds_copies_but() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 // Scheduling hint for one region: NPRE LDS reads first, then NM times {1 MFMA, NDS LDS reads,
 // NV vector instructions}, so the vector work issues in the shadow of the matrix cores.
