@@ -53,11 +53,6 @@ __device__ __forceinline__ void copy_to_lds_b32(const void* base, uint32_t off, 
       : "memory");
 }
 __device__ __forceinline__ void wait_lds_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-// Waits until at most N of this wavefront's copies (and other vector memory loads) are in flight.
-template <int N>
-__device__ __forceinline__ void wait_lds_copies_but() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
 
 // Scheduling hint for one region: NPRE LDS reads first, then NM times {1 MFMA, NDS LDS reads,
 // NV vector instructions}, so the vector work issues in the shadow of the matrix cores.
