@@ -396,7 +396,7 @@ def main():
                     choices=["prefill_8b_128k", "prefill_8b_32k"])
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
