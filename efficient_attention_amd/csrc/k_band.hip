@@ -204,7 +204,11 @@ __global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
   // requested in order 0, 1, 2, ...; the entry of the next one is read a request ahead.
   auto page_of = [&](int e) -> int32_t {
     const int tb = tile_hi_s - kTK * (e < ntiles_s ? e : ntiles_s - 1);
-    return p.pg.table[(idx_t)b * p.pg.tbl_sb + (tb >> p.pg.ps_log2)];
+    // read through the scalar cache (the table is constant while the kernel runs): a vector
+    // load here would make the wave wait for it, and for every copy in flight, on the spot
+    const __attribute__((address_space(4))) int32_t* tbl =
+        (const __attribute__((address_space(4))) int32_t*)p.pg.table;
+    return tbl[(idx_t)b * p.pg.tbl_sb + (tb >> p.pg.ps_log2)];
   };
   int32_t next_page = p.pg.table ? page_of(0) : 0;
   auto load_tile = [&](int e) {
