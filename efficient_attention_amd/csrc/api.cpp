@@ -106,11 +106,11 @@ hipError_t run_stage(int stage, hipStream_t st, F&& f) {
 
 int launch_rc(hipError_t e) { return e == hipSuccess ? ORTHROS_OK : ORTHROS_E_LAUNCH; }
 
-// Split count for the few-row kernel. Two of its work-groups are resident per compute unit
-// (LDS-bound), so a launch runs in waves of kResident groups: pick the split count that
-// minimises (waves x keys per split), preferring splits of ~kSplitKeys keys on ties.
-constexpr int64_t kResident = 2 * 256;
-int nsplit_for(int64_t n, int64_t groups) {
+// Split count for the few-row kernel. Its LDS ring leaves room for one work-group per compute
+// unit at head_dim 128 and two at 64, so a launch runs in waves of that many groups per unit:
+// pick the split count that minimises (waves x keys per split) plus the merge work per split.
+int nsplit_for(int64_t n, int64_t groups, int d) {
+  const int64_t kResident = (d == 128 ? 1 : 2) * 256;
   const int64_t tiles = (n + 63) / 64;
   int best = 1;
   double best_cost = 1e300;
@@ -208,7 +208,7 @@ int decode_common(const orthros_shape* s, const void* q_base, const void* q_out,
     sp.HC = heads_per_chunk(G, true);
     sp.nchunks = (G + sp.HC - 1) / sp.HC;
     sp.window = s->window; sp.with_base = 1;
-    sp.nsplit = nsplit_for(hint + 1, (int64_t)B * Hkv * sp.nchunks);
+    sp.nsplit = nsplit_for(hint + 1, (int64_t)B * Hkv * sp.nchunks, d);
     sp.scale_log2 = scale * kLog2e;
     sp.pm = reinterpret_cast<float*>(wsc + L.pm);
     sp.pl = reinterpret_cast<float*>(wsc + L.pl);
@@ -507,7 +507,7 @@ int forward_sft_impl(const orthros_shape* s, int64_t T, const void* q_base, cons
   sp.HC = 16;
   sp.nchunks = (int)((R * G + 15) / 16);
   sp.window = s->window; sp.with_base = 0;
-  sp.nsplit = nsplit_for(T, (int64_t)B * Hkv * sp.nchunks);
+  sp.nsplit = nsplit_for(T, (int64_t)B * Hkv * sp.nchunks, d);
   sp.scale_log2 = scale * kLog2e;
   sp.pm = reinterpret_cast<float*>(wsc + L.pm);
   sp.pl = reinterpret_cast<float*>(wsc + L.pl);
@@ -609,7 +609,7 @@ int prefill_chunk_impl(const orthros_shape* s, int64_t past_len, int64_t C, cons
   sp.HC = heads_per_chunk(G, false);
   sp.nchunks = (G + sp.HC - 1) / sp.HC;
   sp.window = s->window; sp.with_base = 0;
-  sp.nsplit = nsplit_for(n, (int64_t)B * Hkv * sp.nchunks);
+  sp.nsplit = nsplit_for(n, (int64_t)B * Hkv * sp.nchunks, d);
   sp.scale_log2 = scale * kLog2e;
   sp.pm = reinterpret_cast<float*>(wsc + L.pm);
   sp.pl = reinterpret_cast<float*>(wsc + L.pl);
@@ -718,7 +718,7 @@ int orthros_prefill(const orthros_shape* s, int64_t P, const void* q_base, const
   sp.HC = heads_per_chunk(G, false);
   sp.nchunks = (G + sp.HC - 1) / sp.HC;
   sp.window = s->window; sp.with_base = 0;
-  sp.nsplit = nsplit_for(P, (int64_t)B * Hkv * sp.nchunks);
+  sp.nsplit = nsplit_for(P, (int64_t)B * Hkv * sp.nchunks, d);
   sp.scale_log2 = scale * kLog2e;
   sp.pm = reinterpret_cast<float*>(wsc + L.pm);
   sp.pl = reinterpret_cast<float*>(wsc + L.pl);

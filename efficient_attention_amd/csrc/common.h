@@ -34,6 +34,14 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // Elements are addressed with 64-bit offsets: the largest tensors here exceed 2^31 elements.
 typedef int64_t idx_t;
 
+// A value every lane of the wavefront holds alike, read back as a scalar (values computed by
+// vector instructions, such as 64-bit divisions, otherwise stay in vector registers).
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // Physical block index -> logical block index so that consecutive logical blocks run on the
 // same XCD (blocks are dealt to the 8 XCDs round-robin by physical index), sharing its L2.
 __device__ __forceinline__ uint32_t xcd_swizzle(uint32_t phys, uint32_t total) {

@@ -7,21 +7,25 @@
 // one pass over the key/value stream, so every cached byte is read once per step.
 //
 // Layout: one work-group (4 wavefronts) per (split, kv head x head chunk, sequence). The group
-// stages 64-key tiles of K (row-major) and V (transposed, key-contiguous) through LDS with a
-// double buffer; wavefront w owns keys 16w .. 16w+15 of each tile:
+// copies 64-key tiles of K and V from global memory straight into a kSS-slot LDS ring (row-major,
+// 16-byte slots XOR-swizzled by row), kSS - 1 tiles ahead of their use, so a group keeps two
+// or three tiles of the stream in flight; wavefront w owns keys 16w .. 16w+15 of each tile:
 //   S^T[16 keys x 16 rows] = K . Q^T    4 x mfma_f32_16x16x32_bf16 (d = 128)
 //   online softmax over the 16 keys     (exp2 domain; the query carries scale * log2 e)
-//   O^T[d x 16 rows]     += V^T . P^T   8 x mfma_f32_16x16x16_bf16 (P^T straight from S^T)
+//   O^T[d x 16 rows]     += V^T . P^T   8 x mfma_f32_16x16x16_bf16 (P^T straight from S^T;
+//                                       V^T through the LDS transpose read)
 // The four wavefronts' (max, sum, O) are merged in LDS and written as one fp32 partial per
 // row and split; merge_kernel combines the splits in a fixed order (deterministic).
 #include "common.h"
 #include "launch.h"
+#include "lds_mfma.h"
 
 namespace orthros {
 
 namespace {
 constexpr int kTK = 64;      // keys per tile
 constexpr int kRows = 16;    // query rows per work-group (MFMA N)
+constexpr int kSS = 4;       // LDS ring slots
 // Probabilities are exp2(score - m) with a per-row reference m that moves only when it must
 // (fp32 and bf16 share their exponent range, so values up to 2^64 lose nothing): when a lane's
 // probabilities could exceed 2^64, or at the row's first keys if their maximum lies outside
@@ -31,28 +35,34 @@ constexpr float kSafeScore = 64.f;
 
 template <int D>
 struct SplitSmem {
-  static constexpr int KSTR = D + 8;    // K tile row stride (elements), pads LDS banks
-  static constexpr int VSTR = kTK + 8;  // V^T tile row stride (elements)
-  static constexpr int KBUF = kTK * KSTR;
-  static constexpr int VBUF = D * VSTR;
-  static constexpr int TILE_BYTES = 2 * (KBUF + VBUF) * 2;
+  static constexpr int ROWB = D * 2;           // bytes per K/V row
+  static constexpr int TILEB = kTK * ROWB;     // one K (or V) tile
+  static constexpr int STAGEB = 2 * TILEB;     // K + V
+  static constexpr int RING_BYTES = kSS * STAGEB;
   static constexpr int RED_BYTES = 4 * kRows * (D + 2) * 4;
-  static constexpr int BYTES = TILE_BYTES > RED_BYTES ? TILE_BYTES : RED_BYTES;
+  static constexpr int BYTES = RING_BYTES > RED_BYTES ? RING_BYTES : RED_BYTES;
 };
+// 16-byte slot of channel chunk c in row r: K rows XOR c with r mod (chunks per row), so the
+// 16 rows of a score read hit distinct banks; V rows XOR with an even value (chunk pairs stay
+// together) that differs for 8 consecutive rows (row pairs for d = 64), so the 16 rows of a
+// transposed read cover the banks twice, the least its 512 bytes need.
+template <int D>
+__device__ __forceinline__ int k_swz(int r) { return r % (D / 8); }
+template <int D>
+__device__ __forceinline__ int v_swz(int r) { return D == 128 ? 2 * (r % 8) : 2 * ((r >> 1) % 4); }
 }  // namespace
 
 template <int D, bool PAGED>
 __global__ __launch_bounds__(256) void split_rows_kernel(SplitParams p) {
   using SM = SplitSmem<D>;
-  constexpr int KSTR = SM::KSTR, VSTR = SM::VSTR;
+  constexpr int ROWB = SM::ROWB, TILEB = SM::TILEB, STAGEB = SM::STAGEB;
   constexpr int NST = D / 32;   // QK k-steps (32 channels each)
   constexpr int NMT = D / 16;   // PV output tiles (16 channels each)
   constexpr int CPR = D / 8;    // 16-byte chunks per row
-  constexpr int KCH = kTK * CPR / 256;       // K chunks per thread
-  constexpr int VIT = (kTK / 2) * CPR / 256; // V (key pair, chunk) items per thread
+  constexpr int LROWS = 1024 / ROWB;         // rows per copy instruction (64 lanes x 16 bytes)
+  constexpr int NCOPY = kTK / LROWS / 4;     // copy instructions per wavefront per tensor
+  static_assert(NCOPY >= 1 && NCOPY * LROWS * 4 == kTK, "copies cover a tile");
   __shared__ __attribute__((aligned(16))) unsigned char smem[SM::BYTES];
-  uint16_t* Ks = reinterpret_cast<uint16_t*>(smem);
-  uint16_t* Vt = Ks + 2 * SM::KBUF;
 
   const int s = blockIdx.x;
   const int g = blockIdx.y / p.nchunks;
@@ -65,7 +75,7 @@ __global__ __launch_bounds__(256) void split_rows_kernel(SplitParams p) {
   if (p.len) {
     // keys 0..L-1 come from the cache, key L from this step's input; a length outside
     // [0, capacity] is clamped so no read leaves the cache
-    const int64_t L = p.len[b];
+    const int64_t L = __builtin_amdgcn_readfirstlane(p.len[b]);  // one sequence per group
     Lnew = L < 0 ? 0 : (L > p.cap ? p.cap : L);
     n = Lnew + 1;
   } else {
@@ -73,8 +83,8 @@ __global__ __launch_bounds__(256) void split_rows_kernel(SplitParams p) {
   }
   int64_t per = (n + p.nsplit - 1) / p.nsplit;
   per = (per + kTK - 1) / kTK * kTK;
-  const int64_t kb = (int64_t)s * per;
-  const int64_t ke = kb + per < n ? kb + per : n;
+  const int64_t kb = uniform64((int64_t)s * per);  // this split's keys kb .. ke-1
+  const int64_t ke = uniform64(kb + per < n ? kb + per : n);
 
   const int h0 = g * p.G + chunk * p.HC;
   int nr;  // occupied row slots of this chunk (output stream)
@@ -170,78 +180,98 @@ __global__ __launch_bounds__(256) void split_rows_kernel(SplitParams p) {
   bool seen = false;  // the row met a key of its range in this wavefront's share
 
   if (kb < ke) {
-    u32x4 kreg[KCH], vreg[VIT][2];
-    auto load_tile = [&](int64_t t0) {
-      // Offset of row `key` of this tile (keys past the range re-read its last key; key Lnew
-      // comes from this step's input instead).
+    const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) unsigned char*)smem);
+    // Copy lanes: instruction i of wavefront wv fills rows (wv NCOPY + i) LROWS .. of a tile,
+    // lane l writing slot l % CPR of row l / CPR; it fetches the channel chunk that lands there.
+    int crow[NCOPY];
+    uint32_t kcb[NCOPY], vcb[NCOPY];  // byte offsets of the fetched chunks within a row
+#pragma unroll
+    for (int i = 0; i < NCOPY; ++i) {
+      crow[i] = (wv * NCOPY + i) * LROWS + lane / CPR;
+      kcb[i] = 16u * (uint32_t)((lane % CPR) ^ k_swz<D>(crow[i]));
+      vcb[i] = 16u * (uint32_t)((lane % CPR) ^ v_swz<D>(crow[i]));
+    }
+    const int wv_s = __builtin_amdgcn_readfirstlane(wv);
+    // Pages of >= 64 rows: one table entry per tile, read through the scalar cache (the table is
+    // constant while the kernel runs) one tile request ahead of its use, as tiles are requested
+    // in order.
+    auto read_page = [&](int64_t key) -> int32_t {
+      const int64_t tc = key < 0 ? 0 : (key > p.cap - 1 ? p.cap - 1 : key);
+      const __attribute__((address_space(4))) int32_t* ct =
+          (const __attribute__((address_space(4))) int32_t*)(uintptr_t)uniform64((int64_t)(uintptr_t)tbl);
+      return ct[tc >> p.pg.ps_log2];
+    };
+    int32_t next_page = 0;
+    if constexpr (PAGED) {
+      if (page_per_tile) next_page = read_page(kb);
+    }
+    // Tile starting at key t0 -> ring slot `slot`. Keys past the split's range re-read its last
+    // key; key Lnew comes from this step's input. Every lane carries its own 64-bit address.
+    auto load_tile = [&](int64_t t0, int slot) {
       idx_t tile_off = 0;
-      if (page_per_tile) tile_off = paged_offset(p.pg, tbl, t0, p.cap, p.k_st) - t0 * p.k_st;
-      auto row_off = [&](int64_t key) -> idx_t {
+      if constexpr (PAGED) {
+        if (page_per_tile) {
+          int32_t page = next_page;
+          next_page = read_page(t0 + kTK);
+          if (page < 0 || (int64_t)page >= p.pg.num_pages) {
+            __hip_atomic_fetch_or(p.pg.status, kStatusBadPage, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            page = 0;
+          }
+          // as paged_offset for key t0 (clamped into [0, cap)), minus t0's own rows
+          const int64_t tc = t0 > p.cap - 1 ? p.cap - 1 : t0;
+          tile_off = (idx_t)page * p.pg.k_sp + (tc & (((int64_t)1 << p.pg.ps_log2) - 1)) * p.k_st - t0 * p.k_st;
+        }
+      }
+      const uint32_t sb = lds0 + (uint32_t)(slot * STAGEB);
+#pragma unroll
+      for (int i = 0; i < NCOPY; ++i) {
+        int64_t key = t0 + crow[i];
+        if (key >= ke) key = ke - 1;
+        idx_t roff;
         if constexpr (PAGED) {
-          if (page_per_tile) return tile_off + key * p.k_st;
-          return paged_offset(p.pg, tbl, key, p.cap, p.k_st);
+          roff = page_per_tile ? tile_off + key * p.k_st : paged_offset(p.pg, tbl, key, p.cap, p.k_st);
         } else {
-          return key * p.k_st;
+          roff = key * p.k_st;
         }
-      };
-      auto krow = [&](int64_t key) -> const uint16_t* {
-        if (key >= ke) key = ke - 1;
-        return key == Lnew ? knew : kbase + row_off(key);
-      };
-      auto vrow = [&](int64_t key) -> const uint16_t* {
-        if (key >= ke) key = ke - 1;
-        return key == Lnew ? vnew : vbase + row_off(key);
-      };
-#pragma unroll
-      for (int i = 0; i < KCH; ++i) {
-        const int ci = tid + 256 * i;
-        const int r = ci / CPR, c = ci % CPR;
-        kreg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(krow(t0 + r) + 8 * c));
-      }
-#pragma unroll
-      for (int i = 0; i < VIT; ++i) {
-        const int it = tid + 256 * i;
-        const int c = it % CPR, kp = it / CPR;
-        vreg[i][0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vrow(t0 + 2 * kp) + 8 * c));
-        vreg[i][1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vrow(t0 + 2 * kp + 1) + 8 * c));
+        const unsigned char* ka = key == Lnew ? reinterpret_cast<const unsigned char*>(knew)
+                                              : reinterpret_cast<const unsigned char*>(kbase + roff);
+        const unsigned char* va = key == Lnew ? reinterpret_cast<const unsigned char*>(vnew)
+                                              : reinterpret_cast<const unsigned char*>(vbase + roff);
+        const uint32_t dst = sb + (uint32_t)(wv_s * NCOPY + i) * 1024u;
+        copy_to_lds_at(ka + kcb[i], dst);
+        copy_to_lds_at(va + vcb[i], dst + TILEB);
       }
     };
-    auto store_tile = [&](int buf) {
-      uint16_t* ks = Ks + buf * SM::KBUF;
-      uint16_t* vt = Vt + buf * SM::VBUF;
-#pragma unroll
-      for (int i = 0; i < KCH; ++i) {
-        const int ci = tid + 256 * i;
-        const int r = ci / CPR, c = ci % CPR;
-        *reinterpret_cast<u32x4*>(ks + r * KSTR + 8 * c) = kreg[i];
-      }
-#pragma unroll
-      for (int i = 0; i < VIT; ++i) {
-        const int it = tid + 256 * i;
-        const int c = it % CPR, kp = it / CPR;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t a = vreg[i][0][e >> 1], bb = vreg[i][1][e >> 1];
-          const uint32_t w = (e & 1) ? ((a >> 16) | (bb & 0xffff0000u)) : ((a & 0xffffu) | (bb << 16));
-          *reinterpret_cast<uint32_t*>(vt + (8 * c + e) * VSTR + 2 * kp) = w;
-        }
-      }
+    // Waits until at most `ahead` tiles' copies of this wavefront are still in flight (2 NCOPY
+    // per tile; the loop issues no other vector memory load whose wait is still pending).
+    auto wait_tiles = [&](int ahead) {
+      if (ahead >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * NCOPY) : "memory");
+      else if (ahead == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NCOPY) : "memory");
+      else wait_lds_copies();
     };
+    static_assert(kSS - 2 <= 2, "wait_tiles covers up to two tiles beyond the next");
 
-    load_tile(kb);
-    int buf = 0;
-    for (int64_t t0 = kb; t0 < ke; t0 += kTK) {
-      store_tile(buf);
-      __syncthreads();
-      if (t0 + kTK < ke) load_tile(t0 + kTK);
+    const int ntl = __builtin_amdgcn_readfirstlane((int)((ke - kb + kTK - 1) / kTK));
+    for (int t = 0; t < kSS - 1 && t < ntl; ++t) load_tile(kb + (int64_t)kTK * t, t);
+    wait_tiles(ntl - 1 < kSS - 2 ? ntl - 1 : kSS - 2);  // tile 0 has landed
+    __syncthreads();
+    // LDS read offsets within a slot: score operand (row 16 wv + j, channel chunk 4 st + kg),
+    // transposed value operand (lane j of group kg: row 16 wv + 4 kg + j / 4, channels
+    // 16 mt + 4 (j % 4) .. + 3, i.e. chunk 2 mt + (j % 4) / 2, half j % 2).
+    const int qrow = 16 * wv + j;
+    const int vr = 16 * wv + 4 * kg + (j >> 2);
+    for (int t = 0; t < ntl; ++t) {
+      // tile t + kSS - 1 goes into the slot tile t - 1 left (free since the last barrier)
+      if (t + kSS - 1 < ntl) load_tile(kb + (int64_t)kTK * (t + kSS - 1), (t + kSS - 1) % kSS);
+      const int64_t t0 = kb + (int64_t)kTK * t;
       const int64_t wk0 = t0 + 16 * wv;  // this wavefront's first key
       if (wk0 < ke) {
-        const uint16_t* ks = Ks + buf * SM::KBUF;
-        const uint16_t* vt = Vt + buf * SM::VBUF;
+        const unsigned char* sk = smem + (t % kSS) * STAGEB;
+        const unsigned char* sv = sk + TILEB;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int st = 0; st < NST; ++st) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + (16 * wv + j) * KSTR + 32 * st + 8 * kg);
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(sk + qrow * ROWB + 16 * ((4 * st + kg) ^ k_swz<D>(qrow)));
           acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[st], acc, 0, 0, 0);
           acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf_lo[st], acc, 0, 0, 0);
         }
@@ -290,12 +320,17 @@ __global__ __launch_bounds__(256) void split_rows_kernel(SplitParams p) {
         l += ps;
 #pragma unroll
         for (int mt = 0; mt < NMT; ++mt) {
-          const s16x4 a = *reinterpret_cast<const s16x4*>(vt + (16 * mt + j) * VSTR + 16 * wv + 4 * kg);
+          const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4*)(sv + vr * ROWB + 16 * ((2 * mt + ((j & 3) >> 1)) ^ v_swz<D>(vr)) + 8 * (j & 1)));
           O[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb, O[mt], 0, 0, 0);
           O[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb_lo, O[mt], 0, 0, 0);
         }
       }
-      buf ^= 1;
+      {  // tile t + 1 has landed before the barrier publishes it
+        const int later = ntl - 2 - t;
+        wait_tiles(later < kSS - 2 ? later : kSS - 2);
+      }
+      __syncthreads();
     }
   }
 

@@ -39,6 +39,19 @@ __device__ __forceinline__ void copy_to_lds(const void* base, uint32_t off, uint
       : "s"(lds), "v"(off), "s"(base)
       : "memory");
 }
+// The same with a 64-bit global address per lane (each lane's source may lie anywhere).
+__device__ __forceinline__ void copy_to_lds_at(const void* addr, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(addr)
+      : "memory");
+}
 // The same with 4 bytes per lane: active lane i fills bytes 4 i .. 4 i + 3 from `lds`.
 __device__ __forceinline__ void copy_to_lds_b32(const void* base, uint32_t off, uint32_t lds) {
   uint32_t saved;
