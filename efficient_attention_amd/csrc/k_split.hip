@@ -25,7 +25,7 @@ namespace orthros {
 namespace {
 constexpr int kTK = 64;      // keys per tile
 constexpr int kRows = 16;    // query rows per work-group (MFMA N)
-constexpr int kSS = 4;       // LDS ring slots
+constexpr int kSS = 5;       // LDS ring slots
 // Probabilities are exp2(score - m) with a per-row reference m that moves only when it must
 // (fp32 and bf16 share their exponent range, so values up to 2^64 lose nothing): when a lane's
 // probabilities could exceed 2^64, or at the row's first keys if their maximum lies outside
@@ -245,11 +245,12 @@ __global__ __launch_bounds__(256) void split_rows_kernel(SplitParams p) {
     // Waits until at most `ahead` tiles' copies of this wavefront are still in flight (2 NCOPY
     // per tile; the loop issues no other vector memory load whose wait is still pending).
     auto wait_tiles = [&](int ahead) {
-      if (ahead >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * NCOPY) : "memory");
+      if (ahead >= 3) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(6 * NCOPY) : "memory");
+      else if (ahead == 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * NCOPY) : "memory");
       else if (ahead == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NCOPY) : "memory");
       else wait_lds_copies();
     };
-    static_assert(kSS - 2 <= 2, "wait_tiles covers up to two tiles beyond the next");
+    static_assert(kSS - 2 <= 3, "wait_tiles covers up to three tiles beyond the next");
 
     const int ntl = __builtin_amdgcn_readfirstlane((int)((ke - kb + kTK - 1) / kTK));
     for (int t = 0; t < kSS - 1 && t < ntl; ++t) load_tile(kb + (int64_t)kTK * t, t);
