@@ -8,8 +8,9 @@
 //
 // Layout: one work-group (4 wavefronts) per (split, kv head x head chunk, sequence). The group
 // copies 64-key tiles of K and V from global memory straight into a kSS-slot LDS ring (row-major,
-// 16-byte slots XOR-swizzled by row), kSS - 1 tiles ahead of their use, so a group keeps two
-// or three tiles of the stream in flight; wavefront w owns keys 16w .. 16w+15 of each tile:
+// 16-byte slots XOR-swizzled by row), kSS - 1 tiles ahead of their use, so a group keeps up to
+// four tiles (128 KB at d = 128) of the stream in flight; wavefront w owns keys 16w .. 16w+15
+// of each tile:
 //   S^T[16 keys x 16 rows] = K . Q^T    4 x mfma_f32_16x16x32_bf16 (d = 128)
 //   online softmax over the 16 keys     (exp2 domain; the query carries scale * log2 e)
 //   O^T[d x 16 rows]     += V^T . P^T   8 x mfma_f32_16x16x16_bf16 (P^T straight from S^T;
