@@ -206,6 +206,7 @@ def _decode_run(wl, steps, lengths, tdt, capacity):
 
 @pytest.mark.parametrize("Hq,Hkv,d,w,lengths,dt", [
     (8, 2, 128, 64, [300, 5, 64, 1000], "bf16"),
+    (8, 2, 128, 50, [0, 63, 127, 128], "bf16"),  # empty history; new key at a tile's end / start
     (4, 4, 128, 1, [77, 200], "bf16"),
     (32, 8, 128, 4096, [5000, 9000], "bf16"),
     (16, 1, 64, 100, [150], "bf16"),
