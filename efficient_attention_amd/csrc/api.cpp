@@ -240,7 +240,7 @@ BwdLayout bwd_layout(const orthros_shape* s, int64_t T, int64_t R) {
   const size_t rows[2] = {(size_t)s->batch * (size_t)T, (size_t)s->batch * (size_t)R};
   const size_t n = (size_t)s->num_q_heads * s->head_dim;
   BwdLayout L;
-  L.chunk_rows = 32;
+  L.chunk_rows = 16;  // rows per partial-sum chunk: enough work-groups to keep HBM busy
   const size_t rmax = rows[0] > rows[1] ? rows[0] : rows[1];
   L.nchunk = (int)((rmax + L.chunk_rows - 1) / L.chunk_rows);
   size_t off = kStatusBytes;
