@@ -59,8 +59,8 @@ TRAFFIC = {
 def kernel_sources_sha(kernel: str) -> str:
     import hashlib
     files = {"band_kernel": ["k_band.hip", "lds_mfma.h"],
-             "split_rows_kernel": ["k_split.hip"],
-             "split_rows_kernel_paged": ["k_split.hip"]}[kernel]
+             "split_rows_kernel": ["k_split.hip", "lds_mfma.h"],
+             "split_rows_kernel_paged": ["k_split.hip", "lds_mfma.h"]}[kernel]
     h = hashlib.sha256()
     for f in files + ["common.h", "launch.h"]:
         with open(os.path.join(CSRC, f), "rb") as fh:

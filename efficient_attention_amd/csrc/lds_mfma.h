@@ -28,6 +28,10 @@ __device__ __forceinline__ float lane_pair_sum(float x) {
 // destination slot from the slots being read); the kernel waits for these copies itself before
 // the barrier that publishes them. M0, which carries the LDS address, is restored afterwards.
 __device__ __forceinline__ void copy_to_lds(const void* base, uint32_t off, uint32_t lds) {
+  // (base and lds are the same in every lane; read them as scalars so the operands below are
+  // scalar registers whatever the compiler kept them in)
+  base = reinterpret_cast<const void*>(uniform64(reinterpret_cast<int64_t>(base)));
+  lds = __builtin_amdgcn_readfirstlane(lds);
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
@@ -41,6 +45,7 @@ __device__ __forceinline__ void copy_to_lds(const void* base, uint32_t off, uint
 }
 // The same with a 64-bit global address per lane (each lane's source may lie anywhere).
 __device__ __forceinline__ void copy_to_lds_at(const void* addr, uint32_t lds) {
+  lds = __builtin_amdgcn_readfirstlane(lds);
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
@@ -54,6 +59,8 @@ __device__ __forceinline__ void copy_to_lds_at(const void* addr, uint32_t lds) {
 }
 // The same with 4 bytes per lane: active lane i fills bytes 4 i .. 4 i + 3 from `lds`.
 __device__ __forceinline__ void copy_to_lds_b32(const void* base, uint32_t off, uint32_t lds) {
+  base = reinterpret_cast<const void*>(uniform64(reinterpret_cast<int64_t>(base)));
+  lds = __builtin_amdgcn_readfirstlane(lds);
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
