@@ -50,9 +50,9 @@ CSRC = os.path.join(ROOT, "efficient_attention_amd", "csrc")
 # in the same run. Recorded with the sha256 of the kernel's sources: when they change, the
 # figure no longer describes the kernel and `traffic` is reported as null.
 TRAFFIC = {
-    "band_kernel": {"sha": "3675f5c7c3dfa6ab", "bytes_per_launch": 2.7770e+09},
-    "split_rows_kernel": {"sha": "13eb99cdc8a2ee9c", "bytes_per_launch": 8.5957e+09},
-    "split_rows_kernel_paged": {"sha": "13eb99cdc8a2ee9c", "bytes_per_launch": 8.5968e+09},
+    "band_kernel": {"sha": "1947070995ee175c", "bytes_per_launch": 2.7648e+09},
+    "split_rows_kernel": {"sha": "65d5bc9a0b8873c6", "bytes_per_launch": 8.5957e+09},
+    "split_rows_kernel_paged": {"sha": "65d5bc9a0b8873c6", "bytes_per_launch": 8.5968e+09},
 }
 
 
