@@ -105,6 +105,27 @@ def prefill_flops(wl) -> float:
     return base, out
 
 
+def timed(step, steps, reset=None):
+    """`steps` calls of step(i) timed with nothing else on the stream (ms per call), then, after
+    reset(), the same calls again with the library's per-kernel HIP events on: the stage times
+    (the roofline's launch durations) come from that second pass, so the event records never
+    sit inside the timed region."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    if reset is not None:
+        reset()
+        torch.cuda.synchronize()
+    ox.timing_begin()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    return ms, ox.timing_end()
+
+
 def bench_prefill(wl, steps, warmup, dev):
     log(f"prefill {wl.name}: generating inputs on {dev}")
     inp = syn.make_prefill(wl, device=dev)
@@ -126,15 +147,7 @@ def bench_prefill(wl, steps, warmup, dev):
         step()
     torch.cuda.synchronize()
     log(f"prefill warmup {warmup} done; timing {steps} steps")
-    ox.timing_begin()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    stages = ox.timing_end()
-    ms = (t1 - t0) * 1e3 / steps
+    ms, stages = timed(lambda i: step(), steps)
     log(f"prefill {ms:.3f} ms/step; stages {stages}")
     return dict(ms=ms, stages=stages, inp=inp, planted=inp["planted_pos"])
 
@@ -192,16 +205,10 @@ def bench_decode(wl, warmup, dev, page_size=0):
     cl.fill_(L0)
     torch.cuda.synchronize()
     log(f"decode warmup {warmup} done; timing {S} steps")
-    ox.timing_begin()
-    t0 = time.perf_counter()
-    for s in range(S):
-        step(s, L0 + s)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    stages = ox.timing_end()
+    ms, stages = timed(lambda s: step(s, L0 + s), S, reset=lambda: cl.fill_(L0))
     assert cl.cpu().tolist() == [L0 + S] * B
     assert ox.read_device_status(ws) == 0
-    us = (t1 - t0) * 1e6 / S
+    us = ms * 1e3
     # algorithmic bytes: every cached key/value row read once, new k/v read + appended,
     # queries read, outputs written (both streams)
     kv_row = Hkv * d * 2 * 2
@@ -234,14 +241,7 @@ def bench_sft(wl, R, steps, warmup, dev):
 
     for _ in range(warmup):
         step()
-    torch.cuda.synchronize()
-    ox.timing_begin()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        step()
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / steps
-    stages = ox.timing_end()
+    ms, stages = timed(lambda i: step(), steps)
     flops = 4.0 * d * Hq * B * (swa_pairs(T, wl.window) + sum(t + 1 for t in range(T - R, T)))
     band_ms, band_n = stages["band"]
     log(f"sft {wl.name} R={R}: {ms:.3f} ms/step; stages {stages}")
@@ -277,14 +277,7 @@ def bench_training(wl, steps, warmup, dev):
 
     for _ in range(warmup):
         step()
-    torch.cuda.synchronize()
-    ox.timing_begin()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        step()
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / steps
-    stages = ox.timing_end()
+    ms, stages = timed(lambda i: step(), steps)
     pairs = B * Hq * (swa_pairs(T, wl.window) + T * (T + 1) // 2)
     fwd_flops = 4.0 * d * pairs
     bwd_flops = 10.0 * d * pairs  # five products per (query, key) pair
@@ -334,14 +327,7 @@ def bench_prefill_chunked(wl, chunk, steps, warmup, dev, inp, page_size=0):
 
     for _ in range(warmup):
         step()
-    torch.cuda.synchronize()
-    ox.timing_begin()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        step()
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / steps
-    stages = ox.timing_end()
+    ms, stages = timed(lambda i: step(), steps)
     log(f"prefill in {len(starts)} chunks of {chunk}" + (f" into {page_size}-token pages" if page_size else "")
         + f": {ms:.3f} ms/step; stages {stages}")
     return dict(ms=ms, chunks=len(starts), band_ms=stages["band"][0] / max(steps, 1))
