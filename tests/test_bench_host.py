@@ -30,3 +30,24 @@ def test_gpus_other_than_one_exit_with_message():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_timed_keeps_events_out_of_the_timed_steps(monkeypatch):
+    """bench.timed: `steps` calls with the library's per-kernel events off (the timed pass),
+    then reset, then the same calls with the events on (the stage times)."""
+    log = []
+    state = {"events": False}
+    monkeypatch.setattr(bench.torch.cuda, "synchronize", lambda: None)
+    monkeypatch.setattr(bench.ox, "timing_begin", lambda: state.update(events=True) or log.append("begin"))
+
+    def end():
+        state["events"] = False
+        log.append("end")
+        return {"band": (1.0, 3)}
+
+    monkeypatch.setattr(bench.ox, "timing_end", end)
+    ms, stages = bench.timed(lambda i: log.append(("step", i, state["events"])), 3,
+                             reset=lambda: log.append("reset"))
+    assert log == [("step", 0, False), ("step", 1, False), ("step", 2, False), "reset", "begin",
+                   ("step", 0, True), ("step", 1, True), ("step", 2, True), "end"]
+    assert stages == {"band": (1.0, 3)} and ms >= 0.0
