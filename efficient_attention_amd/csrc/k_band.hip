@@ -330,10 +330,9 @@ __global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
   };
   // After the tentative probabilities of a half: the reference moves only if a probability of
   // the query could exceed 2^8 (their sum over both lane halves does) or the query meets its
-  // first key. Then O and l are rescaled, this half's probabilities redone from its shifted
-  // scores (S itself is dead afterwards and is not rewritten), and the next half's scores,
-  // already accumulated against the old reference, recomputed by `redo_next`. The new
-  // reference is the exact maximum, so the probabilities end up <= 1.
+  // first key. Then O and l are rescaled and this half's probabilities recomputed against the
+  // new reference (the scores are kept unshifted, so the other half's need no correction). The
+  // new reference is the exact maximum, so the probabilities end up <= 1.
   auto settle = [&](const f32x16& S, bf16x8* Ph, float ps) {
     const float tot = lane_pair_sum(ps);
     const bool need = !(tot <= kLazyBound) || !started;
