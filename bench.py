@@ -52,8 +52,8 @@ CSRC = os.path.join(ROOT, "efficient_attention_amd", "csrc")
 # and `traffic` is reported as null.
 TRAFFIC = {
     "band_kernel": {"sha": "19eb1f63f662a4f0", "bytes_per_launch": 2.7648e+09},
-    "split_rows_kernel": {"sha": "d5e65bc6a81c810d", "bytes_per_launch": 8.5957e+09},
-    "split_rows_kernel_paged": {"sha": "d5e65bc6a81c810d", "bytes_per_launch": 8.5968e+09},
+    "split_rows_kernel": {"sha": "f41c3c9fc2cddc90", "bytes_per_launch": 8.5958e+09},
+    "split_rows_kernel_paged": {"sha": "f41c3c9fc2cddc90", "bytes_per_launch": 8.5969e+09},
 }
 
 
