@@ -388,12 +388,32 @@ __global__ __launch_bounds__(64 * kKNW, 2) void bwd_kv_kernel(BwdKVParams p) {
   }
   const int n0 = p.G * nqt[0];
   const int nitems = n0 + p.G * nqt[1];
-  auto item = [&](int i, int& st, int& hd, int& qt) {
-    st = i < n0 ? 0 : 1;
-    const int k = i < n0 ? i : i - n0;
-    hd = g * p.G + k / nqt[st];
-    qt = qt0[st] + k % nqt[st];
+  // Items in order: stream 0's row tiles head by head, then stream 1's, stepped by counters
+  // (no division). The streams' arguments are read once here, so picking one per item is a
+  // select, not a load.
+  struct Item {
+    int st, hd, qt;
   };
+  const Item first{n0 > 0 ? 0 : 1, g * p.G, n0 > 0 ? qt0[0] : qt0[1]};
+  auto next_item = [&](Item it) {
+    ++it.qt;
+    if (it.qt == (it.st ? qt0[1] + nqt[1] : qt0[0] + nqt[0])) {
+      ++it.hd;
+      it.qt = it.st ? qt0[1] : qt0[0];
+      if (it.hd == (g + 1) * p.G) {
+        it.st = 1;
+        it.hd = g * p.G;
+        it.qt = qt0[1];
+      }
+    }
+    return it;
+  };
+  const uint16_t* qs[2] = {static_cast<const uint16_t*>(p.q[0]), static_cast<const uint16_t*>(p.q[1])};
+  const uint16_t* ds[2] = {static_cast<const uint16_t*>(p.dout[0]), static_cast<const uint16_t*>(p.dout[1])};
+  const float* ls[2] = {p.lse[0], p.lse[1]};
+  const float* dd[2] = {p.D[0], p.D[1]};
+  const int* ps2[2] = {p.pos[0], p.pos[1]};
+  const int nr2[2] = {p.nrows[0], p.nrows[1]};
 
   // Per-item copies: q' and dO tiles of 32 rows (rows past the end re-read the last row).
   constexpr int LROWS = 1024 / ROWB;
@@ -412,14 +432,12 @@ __global__ __launch_bounds__(64 * kKNW, 2) void bwd_kv_kernel(BwdKVParams p) {
   // The rows' lse, D and raw positions go straight to LDS as well (4 bytes per lane, lanes
   // 0..31 of wavefront 0; rows past the end re-read the last row; a stream without a row list
   // copies its lse into the unused position slot), so no register ever waits for them.
-  auto load_item = [&](int i, int slot) {
-    int st, hd, qt;
-    item(i, st, hd, qt);
-    const int t0 = qt * kQW;
-    const int NR = p.nrows[st];
+  auto load_item = [&](const Item& it, int slot) {
+    const int st = it.st, hd = it.hd, t0 = it.qt * kQW;
+    const int NR = st ? nr2[1] : nr2[0];
     const idx_t off0 = ((idx_t)b * NR + t0) * p.Hq * D + (idx_t)hd * D;
-    const unsigned char* qg = reinterpret_cast<const unsigned char*>(static_cast<const uint16_t*>(p.q[st]) + off0);
-    const unsigned char* dg = reinterpret_cast<const unsigned char*>(static_cast<const uint16_t*>(p.dout[st]) + off0);
+    const unsigned char* qg = reinterpret_cast<const unsigned char*>((st ? qs[1] : qs[0]) + off0);
+    const unsigned char* dg = reinterpret_cast<const unsigned char*>((st ? ds[1] : ds[0]) + off0);
     const uint32_t sb = lds0 + VBYTES + (uint32_t)(slot * STG);
 #pragma unroll
     for (int k = 0; k < NQI; ++k) {
@@ -432,11 +450,12 @@ __global__ __launch_bounds__(64 * kKNW, 2) void bwd_kv_kernel(BwdKVParams p) {
     if (tid < kQW) {
       const int r = t0 + tid < NR ? t0 + tid : NR - 1;
       const idx_t lr0 = ((idx_t)b * p.Hq + hd) * NR;
-      const float* lb = p.lse[st] + lr0;
+      const float* lb = (st ? ls[1] : ls[0]) + lr0;
+      const int* pl = st ? ps2[1] : ps2[0];
       copy_to_lds_b32(lb, (uint32_t)r * 4u, sb + 2 * QTB);
-      copy_to_lds_b32(p.D[st] + lr0, (uint32_t)r * 4u, sb + 2 * QTB + kQW * 4);
-      if (p.pos[st])
-        copy_to_lds_b32(p.pos[st], (uint32_t)r * 4u, sb + 2 * QTB + 2 * kQW * 4);
+      copy_to_lds_b32((st ? dd[1] : dd[0]) + lr0, (uint32_t)r * 4u, sb + 2 * QTB + kQW * 4);
+      if (pl)
+        copy_to_lds_b32(pl, (uint32_t)r * 4u, sb + 2 * QTB + 2 * kQW * 4);
       else
         copy_to_lds_b32(lb, (uint32_t)r * 4u, sb + 2 * QTB + 2 * kQW * 4);
     }
@@ -466,19 +485,19 @@ __global__ __launch_bounds__(64 * kKNW, 2) void bwd_kv_kernel(BwdKVParams p) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) zero16[r] = 0.f;
 
-  if (nitems > 0) load_item(0, 0);
+  if (nitems > 0) load_item(first, 0);
   wait_lds_copies();
   __syncthreads();
+  Item cur = first;
   for (int i = 0; i < nitems; ++i) {
     const int slot = i & 1;
-    if (i + 1 < nitems) load_item(i + 1, slot ^ 1);
-    int st, hd, qt;
-    item(i, st, hd, qt);
-    (void)hd;
-    const int t0 = qt * kQW;
-    const int w = wst[st];
-    const int NR = p.nrows[st];
-    const bool listed = p.pos[st] != nullptr;
+    const Item nxt = next_item(cur);
+    if (i + 1 < nitems) load_item(nxt, slot ^ 1);
+    const int st = cur.st;
+    const int t0 = cur.qt * kQW;
+    const int w = st ? wst[1] : wst[0];
+    const int NR = st ? nr2[1] : nr2[0];
+    const bool listed = (st ? ps2[1] : ps2[0]) != nullptr;
     const unsigned char* sq = smem + VBYTES + slot * STG;
     const float* rowf = reinterpret_cast<const float*>(sq + 2 * QTB);
     const int* rowp = reinterpret_cast<const int*>(rowf + 2 * kQW);
@@ -565,6 +584,7 @@ __global__ __launch_bounds__(64 * kKNW, 2) void bwd_kv_kernel(BwdKVParams p) {
     }
     wait_lds_copies();
     __syncthreads();
+    cur = nxt;
   }
 
   if (kvalid) {
