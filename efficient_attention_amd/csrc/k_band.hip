@@ -178,8 +178,12 @@ __global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
   // Staging straight from global memory into LDS: one wave instruction fills 64 x 16 B, i.e.
   // LROWS consecutive rows, lane i writing slot i % NCH of row i / NCH (the LDS address of a
   // lane is fixed by its index). The swizzle is therefore applied on the global side: the lane
-  // that fills K slot c of row r fetches channel chunk c ^ (r % NCH), and for V chunk
-  // c ^ 4((r >> 1) % (NCH/4)). Wave wv fills rows (wv NINST + i) LROWS .. of every tile.
+  // that fills K slot c of row r fetches channel chunk c ^ (r % NCH), and for V chunk c ^ f(r),
+  // f(r) = 4 (r % 4) at d = 128 (4 ((r >> 1) % 2) at d = 64). A transposed read serves 32 lanes
+  // per LDS cycle: 64 bytes from each of 4 consecutive rows, which f places in four different
+  // 16-bank groups (with f = 4 ((r >> 1) % 4), rows r and r + 1 shared one: 2-way conflicts, 155
+  // against 239 bytes per clock and CU measured). Wave wv fills rows (wv NINST + i) LROWS ..
+  // of every tile.
   constexpr int LROWS = 1024 / ROWB;
   constexpr int NINST = kTK / LROWS / kNW;
   static_assert(NINST >= 1 && NINST * LROWS * kNW == kTK, "staging covers a tile exactly");
@@ -195,7 +199,7 @@ __global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
     const int c = lane % NCH;
     srow[i] = r;
     skoff[i] = (uint32_t)r * rowb + 16u * (uint32_t)(c ^ (r % NCH));
-    svoff[i] = (uint32_t)r * rowb + 16u * (uint32_t)(c ^ (4 * ((r >> 1) % (NCH / 4))));
+    svoff[i] = (uint32_t)r * rowb + 16u * (uint32_t)(c ^ (NCH == 16 ? 4 * (r % 4) : 4 * ((r >> 1) % 2)));
   }
   const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) unsigned char*)smem);
   const int wv_s = __builtin_amdgcn_readfirstlane(wv);
@@ -256,8 +260,8 @@ __global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
   int pv_off[NDT];
   {
     const int G = lane >> 4, L = lane & 15;
-    const int row = 4 * (G >> 1) + (L >> 2);  // + 16 ks + 8 h2 (row-independent swizzle)
-    const int fv = 4 * ((row >> 1) % (NCH / 4));
+    const int row = 4 * (G >> 1) + (L >> 2);  // + 16 ks + 8 h2, which leave f unchanged
+    const int fv = NCH == 16 ? 4 * (row % 4) : 4 * ((row >> 1) % 2);
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
       const int chunk = 4 * dt + 2 * (G & 1) + ((L & 3) >> 1);

@@ -35,11 +35,18 @@ constexpr int kKNW = 4;     // wavefronts per work-group, key side, 32 keys each
 constexpr float kLn2 = 0.69314718055994531f;
 
 // Byte offset of 16-byte slot `chunk` of row `row` of a row-major LDS tile with NCH slots per
-// row, the slot index XOR-swizzled by the row (row reads of 16 consecutive rows hit distinct
-// banks; so do the transposed 8-byte reads).
+// row, the slot index XOR-swizzled by the row. Any 16 consecutive rows place a given slot in
+// 16 different 4-bank groups, so a 16-byte row read (16 lanes per LDS cycle, one row each) hits
+// all 64 banks; and 4 consecutive rows place a 64-byte run of slots in four different 16-bank
+// groups, so a transposed 8-byte read (32 lanes per LDS cycle, 64 bytes from each of 4 rows)
+// does too. Rows 16 apart share the swizzle; rows 8 apart differ in its bit 1.
+template <int NCH>
+__device__ __forceinline__ int swz(int row) {
+  return NCH == 16 ? 4 * (row % 4) + (row >> 2) % 4 : 4 * ((row >> 1) % 2) + (row >> 2) % 4;
+}
 template <int NCH>
 __device__ __forceinline__ uint32_t slot_off(int row, int chunk) {
-  return (uint32_t)(row * NCH * 16 + 16 * (chunk ^ (row % NCH)));
+  return (uint32_t)(row * NCH * 16 + 16 * (chunk ^ swz<NCH>(row)));
 }
 
 // Transposed-read offsets (bytes, within a tile) for the A operand V^T-style product: lane
@@ -213,7 +220,7 @@ __global__ __launch_bounds__(64 * kQNW) void bwd_q_kernel(BwdQParams p) {
     const int r = (wv * NINST + i) * LROWS + lane / NCH;
     const int c = lane % NCH;
     crow[i] = r;
-    coff[i] = (uint32_t)r * rowb + 16u * (uint32_t)(c ^ (r % NCH));
+    coff[i] = (uint32_t)r * rowb + 16u * (uint32_t)(c ^ swz<NCH>(r));
   }
   const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) unsigned char*)smem);
   const int wv_s = __builtin_amdgcn_readfirstlane(wv);
@@ -366,7 +373,7 @@ __global__ __launch_bounds__(64 * kKNW, 2) void bwd_kv_kernel(BwdKVParams p) {
       const int r = (wv * NV + i) * LROWS + lane / NCH;
       const int c = lane % NCH;
       const int kr = k0 + r < T ? r : T - 1 - k0;  // rows past the end re-read the last key
-      copy_to_lds(vg, (uint32_t)kr * (uint32_t)(kst * 2) + 16u * (uint32_t)(c ^ (r % NCH)),
+      copy_to_lds(vg, (uint32_t)kr * (uint32_t)(kst * 2) + 16u * (uint32_t)(c ^ swz<NCH>(r)),
                   lds0 + (uint32_t)(wk_s * NV + i) * 1024u);
     }
   }
@@ -426,7 +433,7 @@ __global__ __launch_bounds__(64 * kKNW, 2) void bwd_kv_kernel(BwdKVParams p) {
     const int r = (wv * NQI + i) * LROWS + lane / NCH;
     const int c = lane % NCH;
     crow[i] = r;
-    coff[i] = (uint32_t)r * (uint32_t)(p.Hq * D * 2) + 16u * (uint32_t)(c ^ (r % NCH));
+    coff[i] = (uint32_t)r * (uint32_t)(p.Hq * D * 2) + 16u * (uint32_t)(c ^ swz<NCH>(r));
   }
   const uint32_t rowq = (uint32_t)p.Hq * D * 2;
   // The rows' lse, D and raw positions go straight to LDS as well (4 bytes per lane, lanes
@@ -470,7 +477,7 @@ __global__ __launch_bounds__(64 * kKNW, 2) void bwd_kv_kernel(BwdKVParams p) {
   uint32_t tr_init[2][NDT];
   tr_offsets<D>(lane, tr_init);
   const uint32_t tr0_init = tr_init[0][0];
-  constexpr uint32_t kTrHi = NCH == 16 ? 128u : 0u;  // the swizzle bit that 8 rows flip
+  constexpr uint32_t kTrHi = 32u;  // the swizzle bit that 8 rows flip
   const uint32_t vrow = (uint32_t)(32 * wv * ROWB);
 
   f32x16 dK[NDT], dV[NDT];
