@@ -250,9 +250,15 @@ __global__ __launch_bounds__(64 * kQNW) void bwd_q_kernel(BwdQParams p) {
   for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) dQ[dt][r] = 0.f;
-  f32x16 zero16;
+  // Each lane holds one query row, so its -lse and -D are the same for all 16 registers of a
+  // score tile: they seed the accumulators of S and dP, which then come out as s - lse and
+  // dP - D with no per-element subtraction.
+  f32x16 seedS, seedD;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) zero16[r] = 0.f;
+  for (int r = 0; r < 16; ++r) {
+    seedS[r] = -lse2;
+    seedD[r] = -Dt;
+  }
 
   load_tile(0);
   wait_lds_copies();
@@ -265,7 +271,7 @@ __global__ __launch_bounds__(64 * kQNW) void bwd_q_kernel(BwdQParams p) {
       const unsigned char* st = smem + (e & 1) * STAGEB;
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
-        f32x16 S = zero16, dP = zero16;
+        f32x16 S = seedS, dP = seedD;
 #pragma unroll
         for (int s = 0; s < NKS; ++s) {
           const bf16x8 ka = *reinterpret_cast<const bf16x8*>(st + 32 * m * ROWB + rd_off[s]);
@@ -288,8 +294,8 @@ __global__ __launch_bounds__(64 * kQNW) void bwd_q_kernel(BwdQParams p) {
         bf16x8 Z[2];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float pr = fast_exp2(S[r] - lse2);
-          Z[r >> 3][r & 7] = (__bf16)(pr * (dP[r] - Dt));
+          const float pr = fast_exp2(S[r]);
+          Z[r >> 3][r & 7] = (__bf16)(pr * dP[r]);
         }
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
