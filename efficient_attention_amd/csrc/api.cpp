@@ -231,7 +231,7 @@ int decode_common(const orthros_shape* s, const void* q_base, const void* q_out,
 // Backward workspace: status word | q' per stream (bf16) | D per stream | fp32 dq per stream |
 // scale-offset gradient partials.
 struct BwdLayout {
-  size_t qp[2], D[2], dq[2], part, total;
+  size_t qp[2], D[2], L2[2], dq[2], part, total;
   int chunk_rows, nchunk;
 };
 // R: rows of the output stream (T for pre-training, the response rows for fine-tuning).
@@ -249,6 +249,10 @@ BwdLayout bwd_layout(const orthros_shape* s, int64_t T, int64_t R) {
     off += s->dtype == ORTHROS_BF16 ? up(rows[i] * n * 2) : 0;
   }
   for (int i = 0; i < 2; ++i) { L.D[i] = off; off += up(rows[i] * s->num_q_heads * 4); }
+  for (int i = 0; i < 2; ++i) {  // -lse in log2 units, the bf16 key side's score seed
+    L.L2[i] = off;
+    off += s->dtype == ORTHROS_BF16 ? up(rows[i] * s->num_q_heads * 4) : 0;
+  }
   for (int i = 0; i < 2; ++i) { L.dq[i] = off; off += up(rows[i] * n * 4); }
   L.part = off;
   off += up((size_t)L.nchunk * 2 * n * 4);
@@ -358,6 +362,7 @@ int backward_impl(const orthros_shape* s, int64_t T, const void* q_base, const v
   const void* dos[2] = {do_base, do_out};
   const float* lses[2] = {lse_base, lse_out};
   float* Ds[2] = {reinterpret_cast<float*>(w + L.D[0]), reinterpret_cast<float*>(w + L.D[1])};
+  float* l2s[2] = {reinterpret_cast<float*>(w + L.L2[0]), reinterpret_cast<float*>(w + L.L2[1])};
   float* dqs[2] = {reinterpret_cast<float*>(w + L.dq[0]), reinterpret_cast<float*>(w + L.dq[1])};
   void* qps[2] = {w + L.qp[0], w + L.qp[1]};
   const int wins[2] = {wb, (int)T};
@@ -377,7 +382,7 @@ int backward_impl(const orthros_shape* s, int64_t T, const void* q_base, const v
     q.q = bf ? qps[i] : qs[i];
     q.alpha = al[i]; q.beta = be[i];
     q.k = k; q.v = v; q.o = os[i]; q.dout = dos[i]; q.lse = lses[i];
-    q.D = Ds[i]; q.dq = dqs[i];
+    q.D = Ds[i]; q.lse2n = bf ? l2s[i] : nullptr; q.dq = dqs[i];
     q.pos = poss[i]; q.nrows = nrows[i];
     q.B = B; q.T = (int)T; q.Hq = Hq; q.Hkv = Hkv; q.G = G; q.window = wins[i]; q.scale = scale;
     rc = launch_rc(run_stage(ORTHROS_STAGE_BWD_Q, st, [&] {
@@ -389,7 +394,7 @@ int backward_impl(const orthros_shape* s, int64_t T, const void* q_base, const v
   for (int i = 0; i < 2; ++i) {
     kv.q[i] = bf ? qps[i] : qs[i];
     kv.alpha[i] = al[i]; kv.beta[i] = be[i];
-    kv.dout[i] = dos[i]; kv.lse[i] = lses[i]; kv.D[i] = Ds[i]; kv.window[i] = wins[i];
+    kv.dout[i] = dos[i]; kv.lse[i] = bf ? l2s[i] : lses[i]; kv.D[i] = Ds[i]; kv.window[i] = wins[i];
     kv.pos[i] = poss[i]; kv.nrows[i] = nrows[i];
   }
   kv.k = k; kv.v = v; kv.dk = dk; kv.dv = dv;

@@ -159,7 +159,11 @@ __global__ __launch_bounds__(64 * kQNW) void bwd_q_kernel(BwdQParams p) {
   const float Dt = lane_pair_sum(dsum);
   const idx_t lrow = ((idx_t)b * p.Hq + h) * NR + qrow;
   const float lse2 = p.lse[lrow] * kLog2e;
-  if (rvalid && hh == 0) p.D[lrow] = Dt;
+  // for the key side, the seeds of its score and dP accumulators: -lse (log2 units) and -D
+  if (rvalid && hh == 0) {
+    p.D[lrow] = -Dt;
+    p.lse2n[lrow] = -lse2;
+  }
 
   // Row positions: the lowest and highest of this wavefront's rows and of the work-group's.
   int qmin_w, qmax_w, qmin_b, qmax_b, tq;
@@ -545,7 +549,20 @@ __global__ __launch_bounds__(64 * kKNW, 2) void bwd_kv_kernel(BwdKVParams p) {
       const unsigned char* sd = sq + QTB;
       uint32_t rd0 = rd0_init, tr0 = tr0_init;
       asm volatile("" : "+v"(rd0), "+v"(tr0));  // derive the offsets here, not before the loop
-      f32x16 S = zero16, dP = zero16;
+      // Register r holds row i(r) = 8 (r / 4) + 4 hh + r % 4 of the tile, column key j. The
+      // rows' -lse (log2 units) and -D seed the accumulators, so S and dP come out as s - lse
+      // and dP - D.
+      f32x16 S, dP;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(rowf + 8 * q4 + 4 * hh);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(rowf + kQW + 8 * q4 + 4 * hh);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          S[4 * q4 + k] = l4[k];
+          dP[4 * q4 + k] = d4[k];
+        }
+      }
 #pragma unroll
       for (int s = 0; s < NKS; ++s) {
         const bf16x8 qa = *reinterpret_cast<const bf16x8*>(sq + (rd0 ^ (32u * s)));
@@ -557,12 +574,9 @@ __global__ __launch_bounds__(64 * kKNW, 2) void bwd_kv_kernel(BwdKVParams p) {
         const bf16x8 vbv = *reinterpret_cast<const bf16x8*>(smem + vrow + (rd0 ^ (32u * s)));
         dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vbv, dP, 0, 0, 0);
       }
-      // Register r holds row i(r) = 8 (r / 4) + 4 hh + r % 4 of the tile, column key j.
       bf16x8 Pb[2], Zb[2];
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(rowf + 8 * q4 + 4 * hh);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(rowf + kQW + 8 * q4 + 4 * hh);
         int4 p4 = {0, 0, 0, 0};
         if (!fl && listed) p4 = *reinterpret_cast<const int4*>(rowp + 8 * q4 + 4 * hh);
         const int pv[4] = {p4.x, p4.y, p4.z, p4.w};
@@ -575,10 +589,9 @@ __global__ __launch_bounds__(64 * kKNW, 2) void bwd_kv_kernel(BwdKVParams p) {
             const bool ok = key <= t && key > t - w && kvalid;
             s = ok ? s : kNegInf;
           }
-          // scores are in log2 units, lse in natural log
-          const float pr = fast_exp2(fmaf(l4[k], -kLog2e, s));
+          const float pr = fast_exp2(s);
           Pb[r >> 3][r & 7] = (__bf16)pr;
-          Zb[r >> 3][r & 7] = (__bf16)(pr * (dP[r] - d4[k]));
+          Zb[r >> 3][r & 7] = (__bf16)(pr * dP[r]);
         }
       }
 #pragma unroll

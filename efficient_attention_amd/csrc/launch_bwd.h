@@ -16,7 +16,8 @@ struct BwdQParams {
   const void* o;           // forward output of the stream
   const void* dout;        // its gradient
   const float* lse;        // [B, Hq, nrows] natural-log log-sum-exp of the forward rows
-  float* D;                // out: [B, Hq, nrows] rowsum(dout * o)
+  float* D;                // out: [B, Hq, nrows] rowsum(dout * o); the bf16 kernel stores -D
+  float* lse2n;            // out (bf16 kernel): [B, Hq, nrows] -lse in log2 units
   float* dq;               // out: [B, nrows, Hq, d] fp32 gradient of the post-affine query
   const int32_t* pos;      // optional: row r sits at position pos[r] (clamped into [0, T));
                            // without it, rows are positions (nrows = T)
@@ -34,8 +35,8 @@ struct BwdKVParams {
   const float* alpha[2];
   const float* beta[2];
   const void* dout[2];
-  const float* lse[2];
-  const float* D[2];
+  const float* lse[2];     // fp32 kernel: the forward's lse; bf16 kernel: -lse in log2 units
+  const float* D[2];       // fp32 kernel: rowsum(dout * o); bf16 kernel: its negation
   int window[2];
   const void* k;
   const void* v;
