@@ -185,16 +185,16 @@ __global__ __launch_bounds__(256) void affine_grad_partial_kernel(AffineGradPara
   *reinterpret_cast<f32x4*>(p.part + ((idx_t)blockIdx.x * 2 + 1) * p.n + c) = sb;
 }
 
-// Sum of the chunk partials, per column: 4 slices of 64 threads each add every fourth chunk
+// Sum of the chunk partials, per column: 16 slices of 16 threads each add every 16th chunk
 // (loads unrolled so several are in flight), then the slices combine in a fixed order.
 __global__ __launch_bounds__(256) void affine_grad_final_kernel(AffineGradParams p) {
-  __shared__ float red[2][4][64];
-  const int cl = threadIdx.x & 63, sl = threadIdx.x >> 6;
-  const int c = blockIdx.x * 64 + cl;
+  __shared__ float red[2][16][16];
+  const int cl = threadIdx.x & 15, sl = threadIdx.x >> 4;
+  const int c = blockIdx.x * 16 + cl;
   float sa = 0.f, sb = 0.f;
   if (c < p.n) {
 #pragma unroll 8
-    for (int k = sl; k < p.nchunk; k += 4) {
+    for (int k = sl; k < p.nchunk; k += 16) {
       sa += p.part[((idx_t)k * 2 + 0) * p.n + c];
       sb += p.part[((idx_t)k * 2 + 1) * p.n + c];
     }
@@ -203,8 +203,14 @@ __global__ __launch_bounds__(256) void affine_grad_final_kernel(AffineGradParams
   red[1][sl][cl] = sb;
   __syncthreads();
   if (sl == 0 && c < p.n) {
-    p.dalpha[c] = (red[0][0][cl] + red[0][1][cl]) + (red[0][2][cl] + red[0][3][cl]);
-    p.dbeta[c] = (red[1][0][cl] + red[1][1][cl]) + (red[1][2][cl] + red[1][3][cl]);
+    float a = 0.f, b = 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      a += red[0][k][cl];
+      b += red[1][k][cl];
+    }
+    p.dalpha[c] = a;
+    p.dbeta[c] = b;
   }
 }
 
@@ -231,7 +237,7 @@ hipError_t launch_affine_grad(const AffineGradParams& p, hipStream_t s) {
   hipLaunchKernelGGL(affine_grad_partial_kernel, dim3((unsigned)p.nchunk, cb4), dim3(256), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(affine_grad_final_kernel, dim3((unsigned)((p.n + 63) / 64)), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(affine_grad_final_kernel, dim3((unsigned)((p.n + 15) / 16)), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
