@@ -208,6 +208,7 @@ __global__ __launch_bounds__(256) void split_rows_kernel(SplitParams p) {
     }
     // Tile starting at key t0 -> ring slot `slot`. Keys past the split's range re-read its last
     // key; key Lnew comes from this step's input. Every lane carries its own 64-bit address.
+    // Each cached byte is read once per call, so the copies carry the non-temporal hint.
     auto load_tile = [&](int64_t t0, int slot) {
       idx_t tile_off = 0;
       if constexpr (PAGED) {
@@ -239,8 +240,8 @@ __global__ __launch_bounds__(256) void split_rows_kernel(SplitParams p) {
         const unsigned char* va = key == Lnew ? reinterpret_cast<const unsigned char*>(vnew)
                                               : reinterpret_cast<const unsigned char*>(vbase + roff);
         const uint32_t dst = sb + (uint32_t)(wv_s * NCOPY + i) * 1024u;
-        copy_to_lds_at(ka + kcb[i], dst);
-        copy_to_lds_at(va + vcb[i], dst + TILEB);
+        stream_to_lds_at(ka + kcb[i], dst);
+        stream_to_lds_at(va + vcb[i], dst + TILEB);
       }
     };
     // Waits until at most `ahead` tiles' copies of this wavefront are still in flight (2 NCOPY
