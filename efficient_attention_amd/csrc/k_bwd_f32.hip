@@ -160,15 +160,15 @@ __global__ __launch_bounds__(256) void affine_grad_partial_kernel(AffineGradPara
   const int r0 = blockIdx.x * p.chunk_rows;
   const int r1 = r0 + p.chunk_rows < p.rows ? r0 + p.chunk_rows : p.rows;
   const f32x4 a = *reinterpret_cast<const f32x4*>(p.alpha + c);
-  const float* __restrict__ dq = p.dq;
+  const float* __restrict__ dq = p.dq;  // dq and q are read once: non-temporal loads
   f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
   for (int r = r0; r < r1; ++r) {
     const idx_t i = (idx_t)r * p.n + c;
-    const f32x4 x = *reinterpret_cast<const f32x4*>(dq + i);
+    const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(dq + i));
     f32x4 qr;
     if (p.bf16) {
-      const u32x2 w = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.q) + i);
+      const u32x2 w = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.q) + i));
       qr = f32x4{bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1])};
       u32x2 o;
       o[0] = pack_bf16x2(a[0] * x[0], a[1] * x[1]);
