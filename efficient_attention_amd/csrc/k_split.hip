@@ -333,12 +333,8 @@ __global__ __launch_bounds__(256) void split_rows_kernel(SplitParams p) {
         const int later = ntl - 2 - t;
         wait_tiles(later < kSS - 2 ? later : kSS - 2);
       }
-      // A wavefront copies exactly the rows it reads, so the data needs no barrier. In a paged
-      // pool one is kept anyway: it holds the four wavefronts to the same tile, so a page's four
-      // quarters are fetched together. Measured on the 128K decode step: over a shuffled pool of
-      // 64-row pages, letting the wavefronts drift apart is 5% slower; over the contiguous cache,
-      // where consecutive tiles are adjacent in memory, it is 1% faster.
-      if constexpr (PAGED) __syncthreads();
+      // A wavefront copies exactly the rows it reads, so the tiles need no barrier and the
+      // wavefronts run apart.
     }
   }
 
