@@ -51,9 +51,9 @@ CSRC = os.path.join(ROOT, "efficient_attention_amd", "csrc")
 # blank lines are left out): when the code changes, the figure no longer describes the kernel
 # and `traffic` is reported as null.
 TRAFFIC = {
-    "band_kernel": {"sha": "bd86874654fd889e", "bytes_per_launch": 2.8011e+09},
-    "split_rows_kernel": {"sha": "8b5d4ae5a67b0151", "bytes_per_launch": 8.5958e+09},
-    "split_rows_kernel_paged": {"sha": "8b5d4ae5a67b0151", "bytes_per_launch": 8.5969e+09},
+    "band_kernel": {"sha": "bd86874654fd889e", "bytes_per_launch": 2.7881e+09},
+    "split_rows_kernel": {"sha": "40ae932194d2dd3c", "bytes_per_launch": 8.5958e+09},
+    "split_rows_kernel_paged": {"sha": "40ae932194d2dd3c", "bytes_per_launch": 8.5969e+09},
 }
 
 
