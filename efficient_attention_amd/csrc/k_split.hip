@@ -264,7 +264,7 @@ __global__ __launch_bounds__(256) void split_rows_kernel(SplitParams p) {
     const int qrow = 16 * wv + j;
     const int vr = 16 * wv + 4 * kg + (j >> 2);
     for (int t = 0; t < ntl; ++t) {
-      // tile t + kSS - 1 goes into the slot tile t - 1 left (free since the last barrier)
+      // tile t + kSS - 1 goes into the slot tile t - 1 left (this wavefront has read its rows)
       if (t + kSS - 1 < ntl) load_tile(kb + (int64_t)kTK * (t + kSS - 1), (t + kSS - 1) % kSS);
       const int64_t t0 = kb + (int64_t)kTK * t;
       const int64_t wk0 = t0 + 16 * wv;  // this wavefront's first key
