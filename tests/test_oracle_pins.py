@@ -556,3 +556,89 @@ def test_sft_backward_with_every_position_is_pt_backward():
     lb = oracle.lse_pt(x["q_base"], x["q_out"], x["k"], x["alpha_b"], x["beta_b"], x["alpha_o"],
                        x["beta_o"], window=5)
     np.testing.assert_array_equal(la[1], lb[1])
+    np.testing.assert_array_equal(la[0], lb[0])
+
+
+def test_lse_sft_rows_match_library_logsumexp():
+    """Output rows at unsorted and repeated response positions (Eq. 5 ranges, keys 0 .. pos)
+    and every base row (Eq. 4 ranges) against torch.logsumexp over explicitly masked scores."""
+    B, T, Hq, Hkv, d, w = 2, 14, 4, 2, 8, 4
+    x, _ = _train_case(B=B, T=T, Hq=Hq, Hkv=Hkv, d=d, seed=12)
+    pos = [9, 0, 13, 9, 3, 13, 6]
+    R = len(pos)
+    r = np.random.default_rng(13)
+    x["q_out"] = r.standard_normal((B, R, Hq, d))
+    lb, lo = oracle.lse_sft(x["q_base"], x["q_out"], x["k"], pos, x["alpha_b"], x["beta_b"],
+                            x["alpha_o"], x["beta_o"], window=w)
+    assert lb.shape == (B, Hq, T) and lo.shape == (B, Hq, R)
+    s = 1 / math.sqrt(d)
+    i = torch.arange(T)
+    band = (i[None, :] <= i[:, None]) & (i[None, :] > i[:, None] - w)
+    rows = torch.tensor(pos)
+    prefix = i[None, :] <= rows[:, None]  # [R, T]
+    for b in range(B):
+        qb = torch.tensor(x["alpha_b"].reshape(Hq, d) * x["q_base"][b] + x["beta_b"].reshape(Hq, d))
+        qo = torch.tensor(x["alpha_o"].reshape(Hq, d) * x["q_out"][b] + x["beta_o"].reshape(Hq, d))
+        for h in range(Hq):
+            kk = torch.tensor(x["k"][b, :, h // (Hq // Hkv)])
+            zb = (s * qb[:, h] @ kk.T).masked_fill(~band, float("-inf"))
+            np.testing.assert_allclose(lb[b, h], torch.logsumexp(zb, dim=1).numpy(), rtol=1e-12)
+            zo = (s * qo[:, h] @ kk.T).masked_fill(~prefix, float("-inf"))
+            np.testing.assert_allclose(lo[b, h], torch.logsumexp(zo, dim=1).numpy(), rtol=1e-12)
+    # repeated positions with the same query give the same value; row 1 (position 0) is its score
+    np.testing.assert_allclose(lo[:, :, 1],
+                               s * np.einsum("bhd,bhd->bh",
+                                             x["alpha_o"].reshape(Hq, d) * x["q_out"][:, 1]
+                                             + x["beta_o"].reshape(Hq, d),
+                                             np.repeat(x["k"][:, 0], Hq // Hkv, axis=1)),
+                               rtol=1e-12)
+
+
+@pytest.mark.parametrize("ps,T", [(1, 3), (4, 6), (8, 5), (16, 17)])
+def test_paged_write_appends_tokens_across_pages(ps, T):
+    """A T-token append per sequence, read back through the table, equals history + tokens
+    (a write that crosses page boundaries included); a sequence without room for all T tokens
+    is left untouched and flagged; no page outside a sequence's written blocks changes."""
+    B, Hkv, d = 4, 2, 4
+    max_pages = 24 // ps + 2
+    cap = max_pages * ps
+    lengths = [ps - 1, 0, cap - T + 1, cap - T]  # crosses a page; empty; one short; exact fit
+    num_pages = B * max_pages + 3
+    table = RNG.permutation(num_pages)[:B * max_pages].reshape(B, max_pages)
+    kp = RNG.standard_normal((num_pages, Hkv, ps, d))
+    vp = RNG.standard_normal((num_pages, Hkv, ps, d))
+    hk = [RNG.standard_normal((L, Hkv, d)) for L in lengths]
+    hv = [RNG.standard_normal((L, Hkv, d)) for L in lengths]
+    for b in range(B):
+        kp = _scatter_blocks(hk[b], table[b], kp, ps)
+        vp = _scatter_blocks(hv[b], table[b], vp, ps)
+    k = RNG.standard_normal((B, T, Hkv, d))
+    v = RNG.standard_normal((B, T, Hkv, d))
+    kp2, vp2, lens, full = oracle.paged_write(kp, vp, table, np.array(lengths), k, v)
+    assert full.tolist() == [False, False, True, False]
+    assert lens.tolist() == [lengths[0] + T, T, lengths[2], cap]
+    for b in (0, 1, 3):
+        L = lengths[b]
+        # the expected pool: the whole new history scattered block by block by the test
+        exp_k = _scatter_blocks(np.concatenate([hk[b], k[b]]), table[b], kp, ps)
+        exp_v = _scatter_blocks(np.concatenate([hv[b], v[b]]), table[b], vp, ps)
+        blocks = table[b][:(L + T + ps - 1) // ps]
+        np.testing.assert_array_equal(kp2[blocks], exp_k[blocks])
+        np.testing.assert_array_equal(vp2[blocks], exp_v[blocks])
+        np.testing.assert_array_equal(oracle.gather_pages(kp2, table[b], L + T),
+                                      np.concatenate([hk[b], k[b]]))
+        np.testing.assert_array_equal(oracle.gather_pages(vp2, table[b], L + T),
+                                      np.concatenate([hv[b], v[b]]))
+    written = set()
+    for b in (0, 1, 3):
+        L = lengths[b]
+        written |= {int(table[b][t // ps]) for t in range(L, L + T)}
+    for pg in range(num_pages):
+        if pg not in written:
+            np.testing.assert_array_equal(kp2[pg], kp[pg])
+            np.testing.assert_array_equal(vp2[pg], vp[pg])
+    # the slots written are exactly positions L .. L + T - 1 of the written sequences
+    changed = {(int(c[0]), int(c[1])) for c in np.argwhere((kp2 != kp).any(axis=(1, 3)))}
+    expect = {(int(table[b][t // ps]), t % ps) for b in (0, 1, 3)
+              for t in range(lengths[b], lengths[b] + T)}
+    assert changed == expect
