@@ -81,6 +81,45 @@ float scale_of(const orthros_shape* s) {
 
 int esize(const orthros_shape* s) { return s->dtype == ORTHROS_BF16 ? 2 : 4; }
 
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+// How T tokens of keys/values [B, T, H_kv, d] reach cache rows t_first .. t_first + T - 1 of
+// the head-major cache: copied (*copy = true), or already there, when k and v are the cache's
+// own rows. The two layouts describe the same bytes only with one kv head and with B == 1 or
+// capacity == T; any other overlap with the cache is an error.
+int kv_source(const orthros_shape* s, int64_t T, int64_t t_first, const void* k, const void* v,
+              const void* ck, const void* cv, bool* copy) {
+  const size_t es = (size_t)esize(s), d = (size_t)s->head_dim;
+  const size_t kvb = (size_t)s->batch * (size_t)T * s->num_kv_heads * d * es;
+  const size_t cb = (size_t)s->batch * s->num_kv_heads * (size_t)s->capacity * d * es;
+  const char* kd = static_cast<const char*>(ck) + (size_t)t_first * d * es;
+  const char* vd = static_cast<const char*>(cv) + (size_t)t_first * d * es;
+  if (k == kd && v == vd && s->num_kv_heads == 1 && (s->batch == 1 || s->capacity == T)) {
+    *copy = false;
+    return ORTHROS_OK;
+  }
+  for (const void* src : {k, v})
+    for (const void* dst : {ck, cv})
+      if (overlap(src, kvb, dst, cb)) return ORTHROS_E_INVALID;
+  *copy = true;
+  return ORTHROS_OK;
+}
+
+// Keys/values [B, T, H_kv, d] must not overlap a paged pool they are written into.
+int kv_outside_pool(const orthros_shape* s, int64_t T, const void* k, const void* v,
+                    const orthros_paged_kv* c) {
+  const size_t es = (size_t)esize(s), d = (size_t)s->head_dim;
+  const size_t kvb = (size_t)s->batch * (size_t)T * s->num_kv_heads * d * es;
+  const size_t pb = (size_t)c->num_pages * s->num_kv_heads * (size_t)c->page_size * d * es;
+  for (const void* src : {k, v})
+    for (const void* dst : {(const void*)c->k_pages, (const void*)c->v_pages})
+      if (overlap(src, kvb, dst, pb)) return ORTHROS_E_INVALID;
+  return ORTHROS_OK;
+}
+
 // ---------------------------------------------------------------------------------------------
 // Optional timing: event pairs around every launch while enabled.
 struct TimingRec {
@@ -272,14 +311,17 @@ int forward_pt_impl(const orthros_shape* s, int64_t T, const void* q_base, const
   const bool any_cache = cache_k || cache_v || cache_len;
   if (any_cache && (rc = check_ptrs({cache_k, cache_v, cache_len}))) return rc;
   if ((rc = check_ws(s, ws, ws_bytes))) return rc;
-  if (any_cache && T > s->capacity) return ORTHROS_E_CAPACITY;
+  if (any_cache && T > s->capacity) return ORTHROS_E_INVALID;
+  bool copy = true;
+  if (any_cache && (rc = kv_source(s, T, 0, k, v, cache_k, cache_v, &copy))) return rc;
 
   const int B = s->batch, Hq = s->num_q_heads, Hkv = s->num_kv_heads, d = s->head_dim;
   const int G = Hq / Hkv;
   const float scale = scale_of(s);
 
   if (any_cache) {
-    CacheWriteParams cw{k, v, cache_k, cache_v, cache_len, B, (int)T, Hkv, d, esize(s), s->capacity};
+    CacheWriteParams cw{k, v, cache_k, cache_v, cache_len, B, (int)T, Hkv, d, esize(s), s->capacity,
+                        0, copy ? 0 : 1};
     rc = launch_rc(run_stage(ORTHROS_STAGE_CACHE_WRITE, st, [&] { return launch_cache_write(cw, st); }));
     if (rc) return rc;
   }
@@ -434,7 +476,9 @@ int forward_sft_impl(const orthros_shape* s, int64_t T, const void* q_base, cons
   const bool any_cache = cache_k || cache_v || cache_len;
   if (any_cache && (rc = check_ptrs({cache_k, cache_v, cache_len}))) return rc;
   if ((rc = check_ws(s, ws, ws_bytes, sft_rows_per_head(R)))) return rc;
-  if (any_cache && T > s->capacity) return ORTHROS_E_CAPACITY;
+  if (any_cache && T > s->capacity) return ORTHROS_E_INVALID;
+  bool copy = true;
+  if (any_cache && (rc = kv_source(s, T, 0, k, v, cache_k, cache_v, &copy))) return rc;
 
   const int B = s->batch, Hq = s->num_q_heads, Hkv = s->num_kv_heads, d = s->head_dim;
   const int G = Hq / Hkv;
@@ -443,7 +487,8 @@ int forward_sft_impl(const orthros_shape* s, int64_t T, const void* q_base, cons
   char* wsc = static_cast<char*>(ws);
 
   if (any_cache) {
-    CacheWriteParams cw{k, v, cache_k, cache_v, cache_len, B, (int)T, Hkv, d, esize(s), s->capacity};
+    CacheWriteParams cw{k, v, cache_k, cache_v, cache_len, B, (int)T, Hkv, d, esize(s), s->capacity,
+                        0, copy ? 0 : 1};
     rc = launch_rc(run_stage(ORTHROS_STAGE_CACHE_WRITE, st, [&] { return launch_cache_write(cw, st); }));
     if (rc) return rc;
   }
@@ -538,8 +583,10 @@ int prefill_chunk_impl(const orthros_shape* s, int64_t past_len, int64_t C, cons
   if ((rc = check_affine(aff))) return rc;
   if ((rc = check_ptrs({q_base, q_out, k, v, cache_k, cache_v, cache_len, o_base, o_out}))) return rc;
   if ((rc = check_ws(s, ws, ws_bytes))) return rc;
-  if (past_len + C > s->capacity) return ORTHROS_E_CAPACITY;
+  if (past_len + C > s->capacity) return ORTHROS_E_INVALID;
   const bool paged = pg.table != nullptr;
+  bool copy = true;  // (the paged callers have checked k, v against the pool)
+  if (!paged && (rc = kv_source(s, C, past_len, k, v, cache_k, cache_v, &copy))) return rc;
 
   const int B = s->batch, Hq = s->num_q_heads, Hkv = s->num_kv_heads, d = s->head_dim;
   const int G = Hq / Hkv;
@@ -557,7 +604,7 @@ int prefill_chunk_impl(const orthros_shape* s, int64_t past_len, int64_t C, cons
     rc = launch_rc(run_stage(ORTHROS_STAGE_CACHE_WRITE, st, [&] { return launch_paged_write(wp, st); }));
   } else {
     CacheWriteParams cw{k, v, cache_k, cache_v, cache_len, B, (int)C, Hkv, d, esize(s),
-                        s->capacity, past_len};
+                        s->capacity, past_len, copy ? 0 : 1};
     rc = launch_rc(run_stage(ORTHROS_STAGE_CACHE_WRITE, st, [&] { return launch_cache_write(cw, st); }));
   }
   if (rc) return rc;
@@ -632,14 +679,9 @@ int prefill_chunk_impl(const orthros_shape* s, int64_t past_len, int64_t C, cons
 
 extern "C" {
 
-size_t orthros_workspace_bytes(const orthros_shape* shape) {
-  if (check_shape(shape) != ORTHROS_OK) return 0;
-  return ws_layout(shape).total;
-}
-
-size_t orthros_sft_workspace_bytes(const orthros_shape* shape, int64_t R) {
-  if (check_shape(shape) != ORTHROS_OK || R < 1) return 0;
-  return ws_layout(shape, sft_rows_per_head(R)).total;
+size_t orthros_workspace_bytes(const orthros_shape* shape, int64_t max_rows_T) {
+  if (check_shape(shape) != ORTHROS_OK || max_rows_T < 1) return 0;
+  return ws_layout(shape, sft_rows_per_head(max_rows_T)).total;
 }
 
 const char* orthros_status_string(int code) {
@@ -648,7 +690,6 @@ const char* orthros_status_string(int code) {
     case ORTHROS_E_INVALID: return "invalid argument";
     case ORTHROS_E_UNSUPPORTED: return "unsupported dtype or shape";
     case ORTHROS_E_WORKSPACE: return "workspace missing or too small";
-    case ORTHROS_E_CAPACITY: return "sequence longer than the cache capacity";
     case ORTHROS_E_LAUNCH: return "HIP launch or runtime failure";
     default: return "unknown status";
   }
@@ -664,7 +705,9 @@ int orthros_prefill(const orthros_shape* s, int64_t P, const void* q_base, const
   if ((rc = check_affine(aff))) return rc;
   if ((rc = check_ptrs({q_base, q_out, k, v, cache_k, cache_v, cache_len, o_base, o_out}))) return rc;
   if ((rc = check_ws(s, ws, ws_bytes))) return rc;
-  if (P > s->capacity) return ORTHROS_E_CAPACITY;
+  if (P > s->capacity) return ORTHROS_E_INVALID;
+  bool copy = true;
+  if ((rc = kv_source(s, P, 0, k, v, cache_k, cache_v, &copy))) return rc;
 
   const int B = s->batch, Hq = s->num_q_heads, Hkv = s->num_kv_heads, d = s->head_dim;
   const int G = Hq / Hkv;
@@ -672,7 +715,8 @@ int orthros_prefill(const orthros_shape* s, int64_t P, const void* q_base, const
   const WsLayout L = ws_layout(s);
   char* wsc = static_cast<char*>(ws);
 
-  CacheWriteParams cw{k, v, cache_k, cache_v, cache_len, B, (int)P, Hkv, d, esize(s), s->capacity};
+  CacheWriteParams cw{k, v, cache_k, cache_v, cache_len, B, (int)P, Hkv, d, esize(s), s->capacity,
+                      0, copy ? 0 : 1};
   rc = launch_rc(run_stage(ORTHROS_STAGE_CACHE_WRITE, st, [&] { return launch_cache_write(cw, st); }));
   if (rc) return rc;
 
@@ -773,6 +817,7 @@ int orthros_paged_write(const orthros_shape* s, int64_t T, const void* k, const 
   if ((rc = check_ws(s, ws, ws_bytes))) return rc;
   PagedKV pg{};
   if ((rc = check_paged(s, cache, ws, &pg))) return rc;
+  if ((rc = kv_outside_pool(s, T, k, v, cache))) return rc;
   PagedWriteParams wp{k, v, cache->k_pages, cache->v_pages, cache_len, s->batch, (int)T,
                       s->num_kv_heads, s->head_dim, esize(s), s->capacity, pg};
   return launch_rc(run_stage(ORTHROS_STAGE_CACHE_WRITE, st, [&] { return launch_paged_write(wp, st); }));
@@ -852,6 +897,7 @@ int orthros_prefill_chunk_paged(const orthros_shape* s, int64_t past_len, int64_
   if ((rc = check_paged(s, cache, ws, &pg))) return rc;
   // the banded kernel reads one table entry per 64-key tile
   if (s->dtype == ORTHROS_BF16 && cache->page_size < 64) return ORTHROS_E_UNSUPPORTED;
+  if (C >= 1 && C <= INT_MAX / 2 && k && v && (rc = kv_outside_pool(s, C, k, v, cache))) return rc;
   return prefill_chunk_impl(s, past_len, C, q_base, q_out, k, v, aff, cache->k_pages,
                             cache->v_pages, pg, cache_len, o_base, o_out, ws, ws_bytes, st);
 }

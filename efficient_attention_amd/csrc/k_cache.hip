@@ -10,7 +10,7 @@ namespace orthros {
 // One 16-byte chunk per thread-iteration; rows are d*esize bytes (a multiple of 16).
 __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteParams p) {
   const int cpr = p.d * p.esize / 16;  // chunks per row
-  const idx_t total = (idx_t)p.B * p.T * p.Hkv * cpr;
+  const idx_t total = p.in_place ? 0 : (idx_t)p.B * p.T * p.Hkv * cpr;
   const idx_t stride = (idx_t)gridDim.x * blockDim.x;
   const u32x4* ksrc = reinterpret_cast<const u32x4*>(p.k);
   const u32x4* vsrc = reinterpret_cast<const u32x4*>(p.v);
@@ -103,19 +103,38 @@ __global__ __launch_bounds__(256) void paged_write_kernel(PagedWriteParams p) {
   }
 }
 
+// One block per sequence: len[b] += T if the write had room and every table entry it went
+// through was a valid page (the write kernel skipped rows of a bad entry, so a length that
+// counted them would make later steps read rows that were never written).
 __global__ __launch_bounds__(256) void paged_advance_kernel(PagedWriteParams p) {
-  for (int b = blockIdx.x * blockDim.x + threadIdx.x; b < p.B; b += gridDim.x * blockDim.x) {
-    const int64_t L = p.len[b];
-    if (L >= 0 && L + p.T <= p.cap) {
-      p.len[b] = (int32_t)(L + p.T);
-    } else {
+  __shared__ int any_bad;
+  const int b = blockIdx.x;
+  const int64_t L = p.len[b];
+  const bool room = L >= 0 && L + p.T <= p.cap;
+  if (threadIdx.x == 0) any_bad = 0;
+  __syncthreads();
+  if (room) {
+    const int32_t* tbl = p.pg.table + (idx_t)b * p.pg.tbl_sb;
+    const int64_t first = L >> p.pg.ps_log2, last = (L + p.T - 1) >> p.pg.ps_log2;
+    bool bad = false;
+    for (int64_t i = first + threadIdx.x; i <= last; i += blockDim.x) {
+      const int32_t page = tbl[i];
+      bad = bad || page < 0 || (int64_t)page >= p.pg.num_pages;
+    }
+    if (bad) any_bad = 1;  // (the write kernel has set the status bit)
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    if (!room) {
       __hip_atomic_fetch_or(p.pg.status, kStatusCacheFull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else if (!any_bad) {
+      p.len[b] = (int32_t)(L + p.T);
     }
   }
 }
 
 hipError_t launch_cache_write(const CacheWriteParams& p, hipStream_t s) {
-  const idx_t total = (idx_t)p.B * p.T * p.Hkv * (p.d * p.esize / 16);
+  const idx_t total = p.in_place ? 0 : (idx_t)p.B * p.T * p.Hkv * (p.d * p.esize / 16);
   idx_t blocks = (total + 255) / 256;
   if (blocks > 8192) blocks = 8192;
   if (blocks < 1) blocks = 1;
@@ -131,7 +150,7 @@ hipError_t launch_paged_write(const PagedWriteParams& p, hipStream_t s) {
   hipLaunchKernelGGL(paged_write_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(paged_advance_kernel, dim3((unsigned)((p.B + 255) / 256)), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(paged_advance_kernel, dim3((unsigned)p.B), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

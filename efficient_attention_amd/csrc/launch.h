@@ -53,6 +53,7 @@ struct CacheWriteParams {
   int B, T, Hkv, d, esize;
   int64_t cap;
   int64_t t_first;
+  int in_place;  // k, v are the cache rows themselves: only len is set
 };
 
 // Decode append: cache row len[b] <- (k_new, v_new)[b]; len[b]++ unless the cache is full.
@@ -69,7 +70,8 @@ struct AppendParams {
 };
 
 // Paged bulk write: token t of k, v [B, T, Hkv, d] goes to position len[b] + t of the paged
-// cache (a sequence without room for all T tokens is skipped); paged_advance then moves len.
+// cache (a sequence without room for all T tokens is skipped); paged_advance then moves len,
+// except for sequences with no room or with a bad table entry among those positions.
 struct PagedWriteParams {
   const void* k;
   const void* v;

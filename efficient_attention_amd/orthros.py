@@ -14,9 +14,9 @@ from dataclasses import dataclass
 import torch
 
 __all__ = [
-    "OK", "E_INVALID", "E_UNSUPPORTED", "E_WORKSPACE", "E_CAPACITY", "E_LAUNCH",
+    "OK", "E_INVALID", "E_UNSUPPORTED", "E_WORKSPACE", "E_LAUNCH",
     "STATUS_CACHE_FULL", "STATUS_BAD_PAGE", "STAGES", "OrthrosError", "Shape", "Affine",
-    "PagedKV", "lib", "library_path", "workspace_bytes", "sft_workspace_bytes",
+    "PagedKV", "lib", "library_path", "workspace_bytes",
     "make_workspace", "prefill", "prefill_chunk", "prefill_chunk_paged", "decode_step",
     "decode_step_paged",
     "paged_write", "forward_pt", "forward_sft", "forward_pt_lse", "backward_workspace_bytes",
@@ -25,14 +25,14 @@ __all__ = [
     "timing_begin", "timing_end", "EXPORTED_SYMBOLS",
 ]
 
-OK, E_INVALID, E_UNSUPPORTED, E_WORKSPACE, E_CAPACITY, E_LAUNCH = 0, -1, -2, -3, -4, -5
+OK, E_INVALID, E_UNSUPPORTED, E_WORKSPACE, E_LAUNCH = 0, -1, -2, -3, -4
 STATUS_CACHE_FULL = 1
 STATUS_BAD_PAGE = 2
 F32, BF16 = 0, 1
 STAGES = ("cache_write", "band", "split_rows", "merge", "append", "rows_f32", "bwd_q", "bwd_kv",
           "bwd_affine")
 EXPORTED_SYMBOLS = (
-    "orthros_workspace_bytes", "orthros_sft_workspace_bytes", "orthros_prefill",
+    "orthros_workspace_bytes", "orthros_prefill",
     "orthros_prefill_chunk", "orthros_prefill_chunk_paged", "orthros_decode_step",
     "orthros_decode_step_paged",
     "orthros_paged_write", "orthros_forward_pt", "orthros_forward_sft",
@@ -91,7 +91,7 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(path)
         vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
         sp, ap = ctypes.POINTER(_CShape), ctypes.POINTER(_CAffine)
-        L.orthros_workspace_bytes.argtypes = [sp]
+        L.orthros_workspace_bytes.argtypes = [sp, i64]
         L.orthros_workspace_bytes.restype = sz
         L.orthros_prefill.argtypes = [sp, i64, vp, vp, vp, vp, ap, vp, vp, vp, vp, vp, vp, sz, vp]
         L.orthros_prefill.restype = ctypes.c_int
@@ -99,8 +99,6 @@ def lib() -> ctypes.CDLL:
         L.orthros_decode_step.restype = ctypes.c_int
         L.orthros_forward_pt.argtypes = [sp, i64, vp, vp, vp, vp, ap, vp, vp, vp, vp, vp, vp, sz, vp]
         L.orthros_forward_pt.restype = ctypes.c_int
-        L.orthros_sft_workspace_bytes.argtypes = [sp, i64]
-        L.orthros_sft_workspace_bytes.restype = sz
         L.orthros_forward_sft.argtypes = [sp, i64, vp, vp, vp, i64, vp, vp, ap, vp, vp, vp, vp,
                                           vp, vp, sz, vp]
         L.orthros_forward_sft.restype = ctypes.c_int
@@ -234,18 +232,16 @@ def _rc(code: int, what: str):
         raise OrthrosError(code, what)
 
 
-def workspace_bytes(shape: Shape) -> int:
-    return int(lib().orthros_workspace_bytes(ctypes.byref(shape.c())))
-
-
-def sft_workspace_bytes(shape: Shape, R: int) -> int:
-    return int(lib().orthros_sft_workspace_bytes(ctypes.byref(shape.c()), int(R)))
+def workspace_bytes(shape: Shape, max_rows: int = 1) -> int:
+    """orthros_workspace_bytes: max_rows is the most output-stream rows per sequence of one
+    call (R for fine-tuning with R response rows, 1 otherwise)."""
+    return int(lib().orthros_workspace_bytes(ctypes.byref(shape.c()), int(max_rows)))
 
 
 def make_workspace(shape: Shape, device, sft_rows: int = 0) -> torch.Tensor:
     """A zero-filled workspace (the status word must start at 0); sft_rows > 0 sizes it for
     orthros_forward_sft with that many response rows."""
-    n = sft_workspace_bytes(shape, sft_rows) if sft_rows > 0 else workspace_bytes(shape)
+    n = workspace_bytes(shape, max(1, sft_rows))
     if n == 0:
         raise OrthrosError(E_INVALID, "workspace_bytes")
     return torch.zeros(n, dtype=torch.uint8, device=device)

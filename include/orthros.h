@@ -62,11 +62,12 @@ typedef enum {
 
 enum {
   ORTHROS_OK = 0,
-  ORTHROS_E_INVALID = -1,      /* null pointer, non-positive size, misaligned pointer, ... */
+  ORTHROS_E_INVALID = -1,      /* null pointer, non-positive size, misaligned pointer, a prompt
+                                  longer than the cache capacity, keys/values overlapping the
+                                  cache they are copied into, ... */
   ORTHROS_E_UNSUPPORTED = -2,  /* dtype / head_dim / head-group combination not built */
   ORTHROS_E_WORKSPACE = -3,    /* workspace missing or smaller than orthros_workspace_bytes */
-  ORTHROS_E_CAPACITY = -4,     /* prompt longer than the cache capacity */
-  ORTHROS_E_LAUNCH = -5        /* a HIP launch or runtime call failed */
+  ORTHROS_E_LAUNCH = -4        /* a HIP launch or runtime call failed */
 };
 
 /* Sticky device status bits, read with orthros_read_device_status. */
@@ -100,11 +101,14 @@ typedef struct {
   const float* beta_out;
 } orthros_affine;
 
-/* Bytes of workspace every call on this shape needs (0 if the shape is invalid). The
- * workspace holds split partials and the sticky status word; zero-fill it once when it is
- * allocated (the status word must start at 0), and never share it between calls that may run
- * concurrently. */
-size_t orthros_workspace_bytes(const orthros_shape* shape);
+/* Bytes of workspace the forward calls on this shape need (0 if the shape is invalid or
+ * max_rows_T < 1). max_rows_T is the largest number of output-stream rows per sequence that a
+ * call using this workspace computes at once: 1 for prefill, decode and pre-training (whose
+ * output rows do not use the workspace), R for orthros_forward_sft with R response rows. The
+ * workspace holds the split partials of the few-row kernel and the sticky status word;
+ * zero-fill it once when it is allocated (the status word must start at 0), and never share
+ * it between calls that may run concurrently. */
+size_t orthros_workspace_bytes(const orthros_shape* shape, int64_t max_rows_T);
 
 /* Prefilling regime (§3.2, T_in = P-1, T_out = 1).
  *   q_base  [B, P, H_q, d]   base-stream raw queries (before the scale-offset)
@@ -114,7 +118,13 @@ size_t orthros_workspace_bytes(const orthros_shape* shape);
  *   cache_len [B]            set to P
  *   o_base  [B, P, H_q, d]   Eq. 4 for every prompt position
  *   o_out   [B, 1, H_q, d]   Eq. 5 at position P-1 (keys 0..P-1)
- * Requires 1 <= P <= capacity. */
+ * Requires 1 <= P <= capacity (ORTHROS_E_INVALID otherwise).
+ * Keys and values already in the cache: k and v may be the cache's own rows (k == cache_k and
+ * v == cache_v here, cache_k + past_len * d elements for orthros_prefill_chunk), which the
+ * two layouts allow only with one kv head and with B == 1 or capacity == P; the copy is then
+ * skipped. Any other overlap of k or v with cache_k or cache_v is ORTHROS_E_INVALID. The same
+ * holds for orthros_forward_pt / orthros_forward_sft with a cache and orthros_prefill_chunk;
+ * the paged calls reject any overlap of k or v with the page pool. */
 int orthros_prefill(const orthros_shape* shape, int64_t P,
                     const void* q_base, const void* q_out, const void* k, const void* v,
                     const orthros_affine* affine,
@@ -153,10 +163,6 @@ int orthros_forward_pt(const orthros_shape* shape, int64_t T,
                        void* o_base, void* o_out,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Bytes of workspace orthros_forward_sft needs for R response rows per sequence (0 if the
- * shape is invalid or R < 1); at least orthros_workspace_bytes(shape). */
-size_t orthros_sft_workspace_bytes(const orthros_shape* shape, int64_t R);
-
 /* Supervised fine-tuning regime (§3.2, T_in = T - T_out, T_out = R >= 1): base rows at every
  * position, output rows only at the R response positions.
  *   q_base   [B, T, H_q, d]   base-stream raw queries
@@ -169,7 +175,7 @@ size_t orthros_sft_workspace_bytes(const orthros_shape* shape, int64_t R);
  *   o_base   [B, T, H_q, d]   Eq. 4 at every position
  *   o_out    [B, R, H_q, d]   Eq. 5 at position out_pos[r] (keys 0 .. out_pos[r])
  *   cache_k/cache_v/cache_len: optional, as for orthros_forward_pt.
- *   workspace: at least orthros_sft_workspace_bytes(shape, R) bytes. */
+ *   workspace: at least orthros_workspace_bytes(shape, R) bytes. */
 int orthros_forward_sft(const orthros_shape* shape, int64_t T,
                         const void* q_base, const void* q_out,
                         const int32_t* out_pos, int64_t R,
@@ -319,13 +325,19 @@ int orthros_prefill_chunk_paged(const orthros_shape* shape, int64_t past_len, in
 /* Appends T tokens per sequence to a paged cache: k, v [B, T, H_kv, d] go to positions
  * cache_len[b] .. cache_len[b] + T - 1 through the table, then cache_len[b] += T (prefilling a
  * prompt into pages, §3.2: the base tokens write the cache). A sequence without room for all T
- * tokens is left unchanged and ORTHROS_STATUS_CACHE_FULL is set. Requires T >= 1. */
+ * tokens is left unchanged and ORTHROS_STATUS_CACHE_FULL is set. A sequence whose table
+ * entries for those positions include one outside [0, num_pages) sets
+ * ORTHROS_STATUS_BAD_PAGE: nothing is written through the bad entry and its cache_len is left
+ * unchanged (rows written through its good entries lie past cache_len and count as unused).
+ * orthros_prefill_chunk_paged writes the chunk the same way. Requires T >= 1. */
 int orthros_paged_write(const orthros_shape* shape, int64_t T, const void* k, const void* v,
                         const orthros_paged_kv* cache, int32_t* cache_len,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Copies the workspace's sticky status word to *host_status (host pointer) after draining
- * `stream`; clears it on the device afterwards when `clear` is non-zero. Synchronous. */
+ * `stream`; clears it on the device afterwards when `clear` is non-zero (the bits are sticky,
+ * so a caller that has handled them resets them here). workspace_bytes is the workspace's
+ * size, checked to hold the status word (ORTHROS_E_INVALID otherwise). Synchronous. */
 int orthros_read_device_status(void* workspace, size_t workspace_bytes, int32_t* host_status,
                                int clear, hipStream_t stream);
 

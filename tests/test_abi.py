@@ -71,7 +71,7 @@ def _prefill(shape, P=64, aff=None, ws_bytes=None, **ptrs):
              o_base=FAKE, o_out=FAKE, ws=FAKE)
     p.update(ptrs)
     L = ox.lib()
-    wsb = L.orthros_workspace_bytes(ctypes.byref(shape)) if ws_bytes is None else ws_bytes
+    wsb = L.orthros_workspace_bytes(ctypes.byref(shape), 1) if ws_bytes is None else ws_bytes
     return L.orthros_prefill(ctypes.byref(shape), P, p["q_base"], p["q_out"], p["k"], p["v"],
                              ctypes.byref(aff or _aff()), p["cache_k"], p["cache_v"],
                              p["cache_len"], p["o_base"], p["o_out"], p["ws"], wsb, None)
@@ -79,11 +79,11 @@ def _prefill(shape, P=64, aff=None, ws_bytes=None, **ptrs):
 
 def test_workspace_bytes():
     L = ox.lib()
-    n = L.orthros_workspace_bytes(ctypes.byref(_shape()))
+    n = L.orthros_workspace_bytes(ctypes.byref(_shape()), 1)
     # status + (max, sum) + d partials for B * Hq * 2 rows * 64 splits
     assert n >= 2 * 8 * 2 * 64 * (128 + 2) * 4
-    assert L.orthros_workspace_bytes(ctypes.byref(_shape(head_dim=96))) == 0
-    assert L.orthros_workspace_bytes(None) == 0
+    assert L.orthros_workspace_bytes(ctypes.byref(_shape(head_dim=96)), 1) == 0
+    assert L.orthros_workspace_bytes(None, 1) == 0
 
 
 @pytest.mark.parametrize("field,value,code", [
@@ -107,14 +107,14 @@ def test_prefill_rejects_bad_affine_workspace_capacity_and_length():
     assert _prefill(_shape(), aff=_aff(beta_out=None)) == ox.E_INVALID
     assert _prefill(_shape(), ws=None) == ox.E_WORKSPACE
     assert _prefill(_shape(), ws_bytes=100) == ox.E_WORKSPACE
-    assert _prefill(_shape(capacity=63), P=64) == ox.E_CAPACITY
+    assert _prefill(_shape(capacity=63), P=64) == ox.E_INVALID
     assert _prefill(_shape(), P=0) == ox.E_INVALID
 
 
 def test_decode_and_pt_reject_bad_arguments():
     L = ox.lib()
     s = _shape()
-    wsb = L.orthros_workspace_bytes(ctypes.byref(s))
+    wsb = L.orthros_workspace_bytes(ctypes.byref(s), 1)
     F = FAKE
     rc = L.orthros_decode_step(ctypes.byref(s), F, F, None, F, ctypes.byref(_aff()), F, F, F, 10,
                                F, F, F, wsb, None)
@@ -131,14 +131,14 @@ def test_decode_and_pt_reject_bad_arguments():
     assert rc == ox.E_INVALID
     rc = L.orthros_forward_pt(ctypes.byref(_shape(capacity=32)), 64, F, F, F, F,
                               ctypes.byref(_aff()), F, F, F, F, F, F, wsb, None)
-    assert rc == ox.E_CAPACITY
+    assert rc == ox.E_INVALID
     rc = L.orthros_forward_pt(ctypes.byref(_shape(head_dim=32)), 64, F, F, F, F,
                               ctypes.byref(_aff()), None, None, None, F, F, F, wsb, None)
     assert rc == ox.E_UNSUPPORTED
 
 
 def test_status_strings():
-    for code in (ox.OK, ox.E_INVALID, ox.E_UNSUPPORTED, ox.E_WORKSPACE, ox.E_CAPACITY,
+    for code in (ox.OK, ox.E_INVALID, ox.E_UNSUPPORTED, ox.E_WORKSPACE, 
                  ox.E_LAUNCH):
         assert ox.status_string(code) not in ("", "unknown status")
     assert ox.status_string(12345) == "unknown status"
@@ -152,13 +152,13 @@ def test_read_status_rejects_null():
 def test_sft_workspace_bytes():
     L = ox.lib()
     s = _shape()
-    base = L.orthros_workspace_bytes(ctypes.byref(s))
-    assert L.orthros_sft_workspace_bytes(ctypes.byref(s), 1) == base
+    base = L.orthros_workspace_bytes(ctypes.byref(s), 1)
+    assert L.orthros_workspace_bytes(ctypes.byref(s), 1) == base
     # up to 16 response rows use split-key rows: one partial row per (head, response row)
-    assert L.orthros_sft_workspace_bytes(ctypes.byref(s), 16) > base
-    assert L.orthros_sft_workspace_bytes(ctypes.byref(s), 17) == base  # banded path: no partials
-    assert L.orthros_sft_workspace_bytes(ctypes.byref(s), 0) == 0
-    assert L.orthros_sft_workspace_bytes(ctypes.byref(_shape(head_dim=96)), 4) == 0
+    assert L.orthros_workspace_bytes(ctypes.byref(s), 16) > base
+    assert L.orthros_workspace_bytes(ctypes.byref(s), 17) == base  # banded path: no partials
+    assert L.orthros_workspace_bytes(ctypes.byref(s), 0) == 0
+    assert L.orthros_workspace_bytes(ctypes.byref(_shape(head_dim=96)), 4) == 0
 
 
 def _sft(shape, T=64, R=4, ws_bytes=None, aff=None, **ptrs):
@@ -166,7 +166,7 @@ def _sft(shape, T=64, R=4, ws_bytes=None, aff=None, **ptrs):
              cache_len=None, o_base=FAKE, o_out=FAKE, ws=FAKE)
     p.update(ptrs)
     L = ox.lib()
-    wsb = L.orthros_sft_workspace_bytes(ctypes.byref(shape), max(R, 1)) if ws_bytes is None else ws_bytes
+    wsb = L.orthros_workspace_bytes(ctypes.byref(shape), max(R, 1)) if ws_bytes is None else ws_bytes
     return L.orthros_forward_sft(ctypes.byref(shape), T, p["q_base"], p["q_out"], p["pos"], R,
                                  p["k"], p["v"], ctypes.byref(aff or _aff()), p["cache_k"],
                                  p["cache_v"], p["cache_len"], p["o_base"], p["o_out"], p["ws"],
@@ -182,10 +182,10 @@ def test_sft_rejects_bad_arguments():
     assert _sft(_shape(), pos=FAKE + 2) == ox.E_INVALID        # positions must be int32-aligned
     assert _sft(_shape(), R=0) == ox.E_INVALID
     assert _sft(_shape(), T=0) == ox.E_INVALID
-    assert _sft(_shape(), R=8, ws_bytes=ox.lib().orthros_workspace_bytes(ctypes.byref(_shape()))) \
+    assert _sft(_shape(), R=8, ws_bytes=ox.lib().orthros_workspace_bytes(ctypes.byref(_shape()), 1)) \
         == ox.E_WORKSPACE                                        # 8 rows need the larger workspace
     assert _sft(_shape(), cache_k=FAKE) == ox.E_INVALID          # cache is all-or-nothing
-    assert _sft(_shape(capacity=32), cache_k=FAKE, cache_v=FAKE, cache_len=FAKE) == ox.E_CAPACITY
+    assert _sft(_shape(capacity=32), cache_k=FAKE, cache_v=FAKE, cache_len=FAKE) == ox.E_INVALID
     assert _sft(_shape(head_dim=48)) == ox.E_UNSUPPORTED
     assert _sft(_shape(), aff=_aff(alpha_out=None)) == ox.E_INVALID
 
@@ -195,7 +195,7 @@ def _chunk(shape, past=100, C=64, ws_bytes=None, **ptrs):
              o_base=FAKE, o_out=FAKE, ws=FAKE)
     p.update(ptrs)
     L = ox.lib()
-    wsb = L.orthros_workspace_bytes(ctypes.byref(shape)) if ws_bytes is None else ws_bytes
+    wsb = L.orthros_workspace_bytes(ctypes.byref(shape), 1) if ws_bytes is None else ws_bytes
     return L.orthros_prefill_chunk(ctypes.byref(shape), past, C, p["q_base"], p["q_out"], p["k"],
                                    p["v"], ctypes.byref(_aff()), p["cache_k"], p["cache_v"],
                                    p["cache_len"], p["o_base"], p["o_out"], p["ws"], wsb, None)
@@ -211,7 +211,7 @@ def test_prefill_chunk_rejects_null_and_misaligned(name):
 def test_prefill_chunk_rejects_bad_lengths_and_workspace():
     assert _chunk(_shape(), past=-1) == ox.E_INVALID
     assert _chunk(_shape(), C=0) == ox.E_INVALID
-    assert _chunk(_shape(capacity=163), past=100, C=64) == ox.E_CAPACITY
+    assert _chunk(_shape(capacity=163), past=100, C=64) == ox.E_INVALID
     assert _chunk(_shape(capacity=164), past=100, C=64, ws=None) == ox.E_WORKSPACE
     assert _chunk(_shape(), ws_bytes=64) == ox.E_WORKSPACE
 
@@ -228,7 +228,7 @@ def _decode_paged(shape, cache=None, hint=100, ws_bytes=None, **ptrs):
              o_out=FAKE, ws=FAKE)
     p.update(ptrs)
     L = ox.lib()
-    wsb = L.orthros_workspace_bytes(ctypes.byref(shape)) if ws_bytes is None else ws_bytes
+    wsb = L.orthros_workspace_bytes(ctypes.byref(shape), 1) if ws_bytes is None else ws_bytes
     c = cache if cache is not None else _paged()
     return L.orthros_decode_step_paged(ctypes.byref(shape), p["q_base"], p["q_out"], p["k_new"],
                                        p["v_new"], ctypes.byref(_aff()), ctypes.byref(c),
@@ -240,7 +240,7 @@ def _paged_write(shape, T=8, cache=None, ws_bytes=None, **ptrs):
     p = dict(k=FAKE, v=FAKE, cache_len=FAKE, ws=FAKE)
     p.update(ptrs)
     L = ox.lib()
-    wsb = L.orthros_workspace_bytes(ctypes.byref(shape)) if ws_bytes is None else ws_bytes
+    wsb = L.orthros_workspace_bytes(ctypes.byref(shape), 1) if ws_bytes is None else ws_bytes
     c = cache if cache is not None else _paged()
     return L.orthros_paged_write(ctypes.byref(shape), T, p["k"], p["v"], ctypes.byref(c),
                                  p["cache_len"], p["ws"], wsb, None)
@@ -287,9 +287,68 @@ def test_paged_prefill_chunk_validation():
         return L.orthros_prefill_chunk_paged(
             ctypes.byref(shape), past, C, FAKE, FAKE, FAKE, FAKE, ctypes.byref(_aff()),
             ctypes.byref(cache), FAKE, FAKE, FAKE, FAKE,
-            L.orthros_workspace_bytes(ctypes.byref(shape)), None)
+            L.orthros_workspace_bytes(ctypes.byref(shape), 1), None)
     # the banded kernel reads one table entry per 64-key tile: bf16 needs pages of >= 64 rows
     assert call(_paged(page_size=32, max_pages=32)) == ox.E_UNSUPPORTED
     assert call(_paged(page_size=48)) == ox.E_INVALID
     assert call(_paged(), past=-1) == ox.E_INVALID
-    assert call(_paged(), past=1020, C=8) == ox.E_CAPACITY
+    assert call(_paged(), past=1020, C=8) == ox.E_INVALID
+
+
+def test_error_codes_match_the_header():
+    text = open(HEADER).read()
+    codes = dict(re.findall(r"ORTHROS_(OK|E_[A-Z]+)\s*=\s*(-?\d+)", text))
+    assert {k: int(v) for k, v in codes.items()} == dict(
+        OK=ox.OK, E_INVALID=ox.E_INVALID, E_UNSUPPORTED=ox.E_UNSUPPORTED,
+        E_WORKSPACE=ox.E_WORKSPACE, E_LAUNCH=ox.E_LAUNCH)
+    assert ox.E_LAUNCH == -4 and ox.E_INVALID == -1
+
+
+def test_read_status_checks_its_arguments():
+    L = ox.lib()
+    out = ctypes.c_int32(0)
+    # the workspace must hold the 256-byte status block; the host pointer must be set
+    assert L.orthros_read_device_status(FAKE, 100, ctypes.byref(out), 0, None) == ox.E_INVALID
+    assert L.orthros_read_device_status(FAKE, 4096, None, 1, None) == ox.E_INVALID
+
+
+# Distinct, far-apart fake addresses so that only the overlaps a test plants exist.
+def _addr(i):
+    return (1 << 36) + (i << 30)
+
+
+def _prefill_at(shape, P, k, v, cache_k, cache_v):
+    L = ox.lib()
+    return L.orthros_prefill(ctypes.byref(shape), P, _addr(1), _addr(2), k, v,
+                             ctypes.byref(_aff()), cache_k, cache_v, _addr(3), _addr(4),
+                             _addr(5), _addr(6), L.orthros_workspace_bytes(ctypes.byref(shape), 1),
+                             None)
+
+
+def test_keys_overlapping_the_cache_are_rejected():
+    ck, cv = _addr(10), _addr(20)
+    one = _shape(batch=1, num_q_heads=4, num_kv_heads=1, capacity=1024)
+    # k inside the cache but not at its rows 0 .. P-1, or v inside the key cache
+    assert _prefill_at(one, 64, ck + 256, cv, ck, cv) == ox.E_INVALID
+    assert _prefill_at(one, 64, _addr(30), ck + 4096, ck, cv) == ox.E_INVALID
+    # with two kv heads the layouts differ: k == cache_k is an overlap, not the cache rows
+    two = _shape(batch=1, num_q_heads=4, num_kv_heads=2, capacity=1024)
+    assert _prefill_at(two, 64, ck, cv, ck, cv) == ox.E_INVALID
+    # two sequences in one kv head coincide only when capacity == P
+    assert _prefill_at(_shape(batch=2, num_q_heads=4, num_kv_heads=1, capacity=1024), 64,
+                       ck, cv, ck, cv) == ox.E_INVALID
+    L = ox.lib()
+    # a chunk's rows start at past_len: k == cache_k (row 0) overlaps rows 0 .. past_len - 1
+    assert L.orthros_prefill_chunk(ctypes.byref(one), 100, 64, _addr(1), _addr(2), ck, cv,
+                                   ctypes.byref(_aff()), ck, cv, _addr(3), _addr(4), _addr(5),
+                                   _addr(6), L.orthros_workspace_bytes(ctypes.byref(one), 1),
+                                   None) == ox.E_INVALID
+
+
+def test_keys_overlapping_a_page_pool_are_rejected():
+    pool = _paged(k_pages=_addr(10), v_pages=_addr(20))
+    shape = _shape()
+    assert _paged_write(shape, cache=pool, k=_addr(10) + 1024, v=_addr(30), cache_len=_addr(31),
+                        ws=_addr(32)) == ox.E_INVALID
+    assert _paged_write(shape, cache=pool, k=_addr(30), v=_addr(20), cache_len=_addr(31),
+                        ws=_addr(32)) == ox.E_INVALID

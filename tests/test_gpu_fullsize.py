@@ -3,8 +3,10 @@
 The four bf16 workloads run whole on the GPU exactly as the benchmark runs them (same shapes,
 capacity, workspace and inputs drawn on the device from the same seeds). The float64 oracle
 then evaluates a seeded sample of rows, one at a time, on host copies of the same bf16 values:
-edge positions (first keys, the window boundary, the last rows) plus random ones, every query
-head. Cache contents are compared bit for bit in full.
+edge positions (first keys, the window boundary, the last rows), one row in every block of 64
+positions (the prompts) and random ones, every query head. Cache contents are compared bit for
+bit in full. The decode workload runs all of its 128 steps; its first and last steps are
+compared in full.
 
 Tolerances: max-abs 1.5e-2 and mean relative error 3e-3 over the sampled outputs.
 """
@@ -25,11 +27,16 @@ def _say(*a):
     print("[gpu case]", *a, flush=True)
 
 
-def _positions(T, w, n_random, seed):
-    """Edge rows (start, window boundary, tile boundaries, end) plus seeded random rows."""
+def _positions(T, w, n_random, seed, per_block=False):
+    """Edge rows (start, window boundary, tile boundaries, end) plus seeded random rows; with
+    per_block, also one seeded row in every block of 64 positions (each block of rows is one
+    work-group's share of the banded kernel, so a wrong block-to-rows mapping shows up)."""
     edges = {0, 1, 2, 63, 64, 65, w - 2, w - 1, w, w + 1, T - 65, T - 64, T - 2, T - 1}
     rng = np.random.default_rng(seed)
     pos = edges | set(rng.integers(0, T, size=n_random).tolist())
+    if per_block:
+        nb = (T + 63) // 64
+        pos |= set((64 * np.arange(nb) + rng.integers(0, 64, size=nb)).tolist())
     return sorted(p for p in pos if 0 <= p < T)
 
 
@@ -63,7 +70,7 @@ def _run_prefill_fullsize(name, n_random):
     assert not torch.isnan(ob).any().item(), "unwritten base row"
 
     a_b, b_b, a_o, b_o = H.affine64(inp["affine"])
-    pos = _positions(P, wl.window, n_random, wl.seed)
+    pos = _positions(P, wl.window, n_random, wl.seed, per_block=True)
     idx = torch.as_tensor(pos, device=DEV)
     K = H.to64(inp["k"][0])
     V = H.to64(inp["v"][0])
@@ -133,12 +140,26 @@ def test_pt_1p3b_2k_fullsize():
     _say(f"pt_1p3b_2k: max-abs {worst[0]:.2e} mean-rel {worst[1]:.2e}")
 
 
+def _host64(t: torch.Tensor) -> np.ndarray:
+    """Device bf16 -> host float64 (widened to fp32 on the device: exact, and the host side
+    only converts fp32 to fp64)."""
+    return t.float().cpu().numpy().astype(np.float64)
+
+
 def test_decode_8b_128k_fullsize():
-    """Two consecutive steps of the 16 x 131072 decode workload; three sequences checked."""
+    """All 128 consecutive steps of the 16 x 131072 decode workload, as the benchmark runs them.
+
+    Every appended cache row of all 16 sequences is compared bit for bit; the first step
+    (L = 131072) and the last (L = 131199) are compared, for all 16 sequences, every query head
+    and both streams, against the oracle's decode step on that history. Each step draws fresh
+    inputs, so one oracle step per checked step is the whole check of that step. The oracle is
+    called per kv head (its query heads h = g G .. g G + G - 1 with that kv head's history):
+    the same equations, with contiguous host arrays."""
     wl = syn.WORKLOADS["decode_8b_128k"]
-    _say("full-size decode", wl)
-    steps = 2
+    _say("full-size decode, 128 steps", wl)
+    S = wl.steps
     B, L0, Hq, Hkv, d = wl.batch, wl.length, wl.q_heads, wl.kv_heads, wl.head_dim
+    G = Hq // Hkv
     cap = L0 + wl.steps + 4  # as the benchmark sizes it
     inp = syn.make_decode_resident(wl, DEV, cap)
     ck, cv = inp["cache_k"], inp["cache_v"]
@@ -146,33 +167,46 @@ def test_decode_8b_128k_fullsize():
     cl = torch.full((B,), L0, dtype=torch.int32, device=DEV)
     ws = ox.make_workspace(shape, DEV)
     aff = ox.Affine(*inp["affine"])
-    check = [0, 7, 15]
-    hist = {b: (H.to64(ck[b, :, :L0].permute(1, 0, 2)), H.to64(cv[b, :, :L0].permute(1, 0, 2)))
-            for b in check}
-    a64 = H.affine64(inp["affine"])
-    for s in range(steps):
+    checked = {0: None, S - 1: None}
+    for s in range(S):
         ob = H.nan_like((B, Hq, d), torch.bfloat16, DEV)
         oo = H.nan_like((B, Hq, d), torch.bfloat16, DEV)
         ox.decode_step(shape, inp["q_base"][s], inp["q_out"][s], inp["k_new"][s], inp["v_new"][s],
                        aff, ck, cv, cl, L0 + s, ob, oo, ws)
-        torch.cuda.synchronize()
-        assert not torch.isnan(ob).any().item() and not torch.isnan(oo).any().item()
-        for b in check:
-            hk, hv = hist[b]
-            rb, ro, nk, nv, _ = oracle.decode_step(
-                [hk], [hv], np.array([L0 + s]), H.to64(inp["q_base"][s, b:b + 1]),
-                H.to64(inp["q_out"][s, b:b + 1]), H.to64(inp["k_new"][s, b:b + 1]),
-                H.to64(inp["v_new"][s, b:b + 1]), *a64, window=wl.window)
-            mb = H.assert_close(H.to64(ob[b:b + 1]), rb, torch.bfloat16, f"o_base step {s} seq {b}")
-            mo = H.assert_close(H.to64(oo[b:b + 1]), ro, torch.bfloat16, f"o_out step {s} seq {b}")
-            hist[b] = (nk[0], nv[0])
-            _say(f"decode step {s} seq {b}: base max-abs {mb[0]:.2e} rel {mb[1]:.2e}; "
-                 f"out max-abs {mo[0]:.2e} rel {mo[1]:.2e}")
-    assert cl.cpu().tolist() == [L0 + steps] * B
+        if s in checked:
+            checked[s] = (ob, oo)
+    torch.cuda.synchronize()
+    _say("128 steps done")
+    assert cl.cpu().tolist() == [L0 + S] * B
     assert ox.read_device_status(ws) == 0
-    for s in range(steps):  # appended rows, bit for bit
-        assert torch.equal(ck[:, :, L0 + s], inp["k_new"][s])
-        assert torch.equal(cv[:, :, L0 + s], inp["v_new"][s])
+    # every appended row of every sequence, bit for bit
+    assert torch.equal(ck[:, :, L0:L0 + S], inp["k_new"].permute(1, 2, 0, 3))
+    assert torch.equal(cv[:, :, L0:L0 + S], inp["v_new"].permute(1, 2, 0, 3))
+    a64 = H.affine64(inp["affine"])
+    ref = {s: (np.empty((B, Hq, d)), np.empty((B, Hq, d))) for s in checked}
+    for b in range(B):
+        for g in range(Hkv):
+            hs = slice(g * G, (g + 1) * G)
+            cs = slice(g * G * d, (g + 1) * G * d)
+            # this kv head's history through the last checked step (keys 0 .. L0 + S - 2);
+            # the oracle reads its first L rows for a step at length L
+            Kg = _host64(ck[b, g, :L0 + S - 1])[:, None, :]
+            Vg = _host64(cv[b, g, :L0 + S - 1])[:, None, :]
+            for s in checked:
+                r = oracle.decode_step(
+                    [Kg], [Vg], np.array([L0 + s]), H.to64(inp["q_base"][s, b:b + 1, hs]),
+                    H.to64(inp["q_out"][s, b:b + 1, hs]),
+                    H.to64(inp["k_new"][s, b:b + 1, g:g + 1]),
+                    H.to64(inp["v_new"][s, b:b + 1, g:g + 1]), a64[0][cs], a64[1][cs],
+                    a64[2][cs], a64[3][cs], window=wl.window)
+                ref[s][0][b, hs], ref[s][1][b, hs] = r[0][0], r[1][0]
+        _say(f"oracle: sequence {b} done")
+    for s, (ob, oo) in checked.items():
+        assert not torch.isnan(ob).any().item() and not torch.isnan(oo).any().item()
+        mb = H.assert_close(H.to64(ob), ref[s][0], torch.bfloat16, f"o_base step {s}")
+        mo = H.assert_close(H.to64(oo), ref[s][1], torch.bfloat16, f"o_out step {s}")
+        _say(f"decode step {s} (L = {L0 + s}), 16 sequences x 32 heads: base max-abs "
+             f"{mb[0]:.2e} rel {mb[1]:.2e}; out max-abs {mo[0]:.2e} rel {mo[1]:.2e}")
 
 
 def test_decode_8b_128k_paged_equals_contiguous():
