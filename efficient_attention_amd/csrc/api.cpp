@@ -6,6 +6,7 @@
 
 #include <climits>
 #include <cmath>
+#include <mutex>
 #include <vector>
 
 #include "launch.h"
@@ -132,8 +133,8 @@ struct Timing {
 } g_timing;
 
 template <class F>
-hipError_t run_stage(int stage, hipStream_t st, F&& f) {
-  if (!g_timing.on) return f();
+hipError_t run_stage(int stage, hipStream_t st, F&& f, bool timed = true) {
+  if (!g_timing.on || !timed) return f();
   TimingRec r{stage, nullptr, nullptr};
   if (hipEventCreate(&r.a) != hipSuccess || hipEventCreate(&r.b) != hipSuccess) return hipErrorUnknown;
   (void)hipEventRecord(r.a, st);
@@ -191,24 +192,35 @@ int check_paged(const orthros_shape* s, const orthros_paged_kv* c, void* ws, Pag
   return ORTHROS_OK;
 }
 
-// One decode step over a contiguous cache (pg.table == nullptr) or a paged pool.
+// Split count of a decode step: the split grid is sized by the host bound on the lengths.
+int decode_nsplit(const orthros_shape* s, int64_t max_len_hint) {
+  const int64_t hint = max_len_hint < s->capacity ? max_len_hint : s->capacity;
+  const int G = s->num_q_heads / s->num_kv_heads;
+  const int nchunks = (G + heads_per_chunk(G, true) - 1) / heads_per_chunk(G, true);
+  return nsplit_for(hint + 1, (int64_t)s->batch * s->num_kv_heads * nchunks, s->head_dim);
+}
+
+// Where a decode step keeps its split partials ([rows][nsplit] maxima and sums, [rows][nsplit][d]
+// partial outputs, rows = 2 B H_q) and its sticky status word.
+struct DecodeScratch {
+  float* pm;
+  float* pl;
+  float* po;
+  int32_t* status;
+};
+
+// One decode step over a contiguous cache (pg.table == nullptr) or a paged pool. Arguments
+// are validated by the callers; `timed` lets the per-stage timing record events around its
+// launches.
 int decode_common(const orthros_shape* s, const void* q_base, const void* q_out,
                   const void* k_new, const void* v_new, const orthros_affine* aff,
                   void* cache_k, void* cache_v, const PagedKV& pg, int32_t* cache_len,
-                  int64_t max_len_hint, void* o_base, void* o_out, void* ws, size_t ws_bytes,
-                  hipStream_t st) {
+                  int64_t max_len_hint, void* o_base, void* o_out, const DecodeScratch& sc,
+                  bool timed, hipStream_t st) {
   int rc;
-  if (max_len_hint < 0) return ORTHROS_E_INVALID;
-  if ((rc = check_affine(aff))) return rc;
-  if ((rc = check_ptrs({q_base, q_out, k_new, v_new, cache_len, o_base, o_out}))) return rc;
-  if ((rc = check_ws(s, ws, ws_bytes))) return rc;
-
   const int B = s->batch, Hq = s->num_q_heads, Hkv = s->num_kv_heads, d = s->head_dim;
   const int G = Hq / Hkv;
   const float scale = scale_of(s);
-  const WsLayout L = ws_layout(s);
-  char* wsc = static_cast<char*>(ws);
-  int64_t hint = max_len_hint < s->capacity ? max_len_hint : s->capacity;
 
   if (s->dtype == ORTHROS_F32) {
     RowsF32Params r{};
@@ -224,14 +236,14 @@ int decode_common(const orthros_shape* s, const void* q_base, const void* q_out,
     r.o = static_cast<float*>(o_base); r.o_sb = (idx_t)Hq * d; r.o_st = 0; r.o_sh = d;
     r.B = B; r.Hq = Hq; r.Hkv = Hkv; r.G = G; r.d = d; r.nrows = 1; r.t0 = 0;
     r.window = s->window; r.scale = scale;
-    rc = launch_rc(run_stage(ORTHROS_STAGE_ROWS_F32, st, [&] { return launch_rows_f32(r, st); }));
+    rc = launch_rc(run_stage(ORTHROS_STAGE_ROWS_F32, st, [&] { return launch_rows_f32(r, st); }, timed));
     if (rc) return rc;
     RowsF32Params o = r;
     o.q = static_cast<const float*>(q_out);
     o.alpha = aff->alpha_out; o.beta = aff->beta_out;
     o.o = static_cast<float*>(o_out);
     o.window = INT_MAX;
-    rc = launch_rc(run_stage(ORTHROS_STAGE_ROWS_F32, st, [&] { return launch_rows_f32(o, st); }));
+    rc = launch_rc(run_stage(ORTHROS_STAGE_ROWS_F32, st, [&] { return launch_rows_f32(o, st); }, timed));
     if (rc) return rc;
   } else {
     SplitParams sp{};
@@ -247,24 +259,83 @@ int decode_common(const orthros_shape* s, const void* q_base, const void* q_out,
     sp.HC = heads_per_chunk(G, true);
     sp.nchunks = (G + sp.HC - 1) / sp.HC;
     sp.window = s->window; sp.with_base = 1;
-    sp.nsplit = nsplit_for(hint + 1, (int64_t)B * Hkv * sp.nchunks, d);
+    sp.nsplit = decode_nsplit(s, max_len_hint);
     sp.scale_log2 = scale * kLog2e;
-    sp.pm = reinterpret_cast<float*>(wsc + L.pm);
-    sp.pl = reinterpret_cast<float*>(wsc + L.pl);
-    sp.po = reinterpret_cast<float*>(wsc + L.po);
-    rc = launch_rc(run_stage(ORTHROS_STAGE_SPLIT_ROWS, st, [&] { return launch_split_rows(sp, d, st); }));
+    sp.pm = sc.pm;
+    sp.pl = sc.pl;
+    sp.po = sc.po;
+    rc = launch_rc(run_stage(ORTHROS_STAGE_SPLIT_ROWS, st, [&] { return launch_split_rows(sp, d, st); }, timed));
     if (rc) return rc;
     MergeParams mp{};
     mp.pm = sp.pm; mp.pl = sp.pl; mp.po = sp.po;
     mp.out0 = o_out; mp.o_sb0 = (idx_t)Hq * d; mp.o_sh0 = d;
     mp.out1 = o_base; mp.o_sb1 = (idx_t)Hq * d; mp.o_sh1 = d;
     mp.rows = B * Hq * 2; mp.nsplit = sp.nsplit; mp.d = d; mp.Hq = Hq; mp.nstreams = 2; mp.bf16 = 1;
-    rc = launch_rc(run_stage(ORTHROS_STAGE_MERGE, st, [&] { return launch_merge(mp, st); }));
+    rc = launch_rc(run_stage(ORTHROS_STAGE_MERGE, st, [&] { return launch_merge(mp, st); }, timed));
     if (rc) return rc;
   }
-  AppendParams ap{k_new, v_new, cache_k, cache_v, cache_len,
-                  reinterpret_cast<int32_t*>(wsc), B, Hkv, d, esize(s), s->capacity, pg};
-  return launch_rc(run_stage(ORTHROS_STAGE_APPEND, st, [&] { return launch_append(ap, st); }));
+  AppendParams ap{k_new, v_new, cache_k, cache_v, cache_len, sc.status, B, Hkv, d, esize(s),
+                  s->capacity, pg};
+  return launch_rc(run_stage(ORTHROS_STAGE_APPEND, st, [&] { return launch_append(ap, st); }, timed));
+}
+
+// Checks shared by the decode entry points (the cache pointers are checked by each).
+int check_decode_args(const void* q_base, const void* q_out, const void* k_new,
+                      const void* v_new, const orthros_affine* aff, int32_t* cache_len,
+                      int64_t max_len_hint, void* o_base, void* o_out) {
+  int rc;
+  if (max_len_hint < 0) return ORTHROS_E_INVALID;
+  if ((rc = check_affine(aff))) return rc;
+  return check_ptrs({q_base, q_out, k_new, v_new, cache_len, o_base, o_out});
+}
+
+DecodeScratch workspace_scratch(const orthros_shape* s, void* ws) {
+  const WsLayout L = ws_layout(s);
+  char* w = static_cast<char*>(ws);
+  return DecodeScratch{reinterpret_cast<float*>(w + L.pm), reinterpret_cast<float*>(w + L.pl),
+                       reinterpret_cast<float*>(w + L.po), reinterpret_cast<int32_t*>(w)};
+}
+
+// ---------------------------------------------------------------------------------------------
+// The split partials of orthros_decode_step_noalloc live in this array, not in a caller's
+// workspace. Each device holds its own copy from the moment the library's code is loaded
+// onto it until the process ends. In host code the name stands for a host-side shadow, not
+// for device memory: every use goes through the device address looked up below.
+static __device__ __align__(256) unsigned char scratch[ORTHROS_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per device (the first
+// call with that device current) and kept.
+int scratch_on_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return ORTHROS_E_LAUNCH;
+  if (dev < 0 || dev >= kMaxDevices) return ORTHROS_E_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return ORTHROS_E_LAUNCH;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ORTHROS_OK;
+}
+
+// Split partials packed for the step's own split count, each array 256-byte aligned.
+struct NoAllocLayout {
+  size_t pm, pl, po, total;
+};
+NoAllocLayout noalloc_layout(const orthros_shape* s, int nsplit) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  const size_t rows = 2 * (size_t)s->batch * s->num_q_heads;
+  NoAllocLayout L;
+  L.pm = 0;
+  L.pl = up(rows * nsplit * sizeof(float));
+  L.po = L.pl + up(rows * nsplit * sizeof(float));
+  L.total = L.po + up(rows * nsplit * (size_t)s->head_dim * sizeof(float));
+  return L;
 }
 
 // Backward workspace: status word | q' per stream (bf16) | D per stream | fp32 dq per stream |
@@ -789,8 +860,37 @@ int orthros_decode_step(const orthros_shape* s, const void* q_base, const void* 
   int rc = check_shape(s);
   if (rc) return rc;
   if ((rc = check_ptrs({cache_k, cache_v}))) return rc;
+  if ((rc = check_decode_args(q_base, q_out, k_new, v_new, aff, cache_len, max_len_hint, o_base,
+                              o_out))) return rc;
+  if ((rc = check_ws(s, ws, ws_bytes))) return rc;
   return decode_common(s, q_base, q_out, k_new, v_new, aff, cache_k, cache_v, PagedKV{},
-                       cache_len, max_len_hint, o_base, o_out, ws, ws_bytes, st);
+                       cache_len, max_len_hint, o_base, o_out, workspace_scratch(s, ws), true, st);
+}
+
+int orthros_decode_step_noalloc(const orthros_shape* s, const void* q_base, const void* q_out,
+                                const void* k_new, const void* v_new, const orthros_affine* aff,
+                                void* cache_k, void* cache_v, int32_t* cache_len,
+                                int64_t max_len_hint, void* o_base, void* o_out,
+                                int32_t* device_status, hipStream_t st) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if ((rc = check_ptrs({cache_k, cache_v}))) return rc;
+  if ((rc = check_decode_args(q_base, q_out, k_new, v_new, aff, cache_len, max_len_hint, o_base,
+                              o_out))) return rc;
+  if (!device_status || ((uintptr_t)device_status & 3u)) return ORTHROS_E_INVALID;
+  DecodeScratch sc{nullptr, nullptr, nullptr, device_status};
+  if (s->dtype == ORTHROS_BF16) {  // (the fp32 rows use no partials)
+    const NoAllocLayout L = noalloc_layout(s, decode_nsplit(s, max_len_hint));
+    if (L.total > ORTHROS_NOALLOC_SCRATCH_BYTES) return ORTHROS_E_WORKSPACE;
+    void* base = nullptr;
+    if ((rc = scratch_on_current_device(&base))) return rc;
+    char* b = static_cast<char*>(base);
+    sc.pm = reinterpret_cast<float*>(b + L.pm);
+    sc.pl = reinterpret_cast<float*>(b + L.pl);
+    sc.po = reinterpret_cast<float*>(b + L.po);
+  }
+  return decode_common(s, q_base, q_out, k_new, v_new, aff, cache_k, cache_v, PagedKV{},
+                       cache_len, max_len_hint, o_base, o_out, sc, false, st);
 }
 
 int orthros_decode_step_paged(const orthros_shape* s, const void* q_base, const void* q_out,
@@ -803,8 +903,10 @@ int orthros_decode_step_paged(const orthros_shape* s, const void* q_base, const 
   if ((rc = check_ws(s, ws, ws_bytes))) return rc;
   PagedKV pg{};
   if ((rc = check_paged(s, cache, ws, &pg))) return rc;
+  if ((rc = check_decode_args(q_base, q_out, k_new, v_new, aff, cache_len, max_len_hint, o_base,
+                              o_out))) return rc;
   return decode_common(s, q_base, q_out, k_new, v_new, aff, cache->k_pages, cache->v_pages, pg,
-                       cache_len, max_len_hint, o_base, o_out, ws, ws_bytes, st);
+                       cache_len, max_len_hint, o_base, o_out, workspace_scratch(s, ws), true, st);
 }
 
 int orthros_paged_write(const orthros_shape* s, int64_t T, const void* k, const void* v,

@@ -18,7 +18,7 @@ __all__ = [
     "STATUS_CACHE_FULL", "STATUS_BAD_PAGE", "STAGES", "OrthrosError", "Shape", "Affine",
     "PagedKV", "lib", "library_path", "workspace_bytes",
     "make_workspace", "prefill", "prefill_chunk", "prefill_chunk_paged", "decode_step",
-    "decode_step_paged",
+    "decode_step_paged", "decode_step_noalloc",
     "paged_write", "forward_pt", "forward_sft", "forward_pt_lse", "backward_workspace_bytes",
     "backward_pt", "forward_sft_lse", "backward_sft_workspace_bytes", "backward_sft",
     "read_device_status", "status_string",
@@ -34,7 +34,7 @@ STAGES = ("cache_write", "band", "split_rows", "merge", "append", "rows_f32", "b
 EXPORTED_SYMBOLS = (
     "orthros_workspace_bytes", "orthros_prefill",
     "orthros_prefill_chunk", "orthros_prefill_chunk_paged", "orthros_decode_step",
-    "orthros_decode_step_paged",
+    "orthros_decode_step_paged", "orthros_decode_step_noalloc",
     "orthros_paged_write", "orthros_forward_pt", "orthros_forward_sft",
     "orthros_forward_pt_lse", "orthros_backward_workspace_bytes", "orthros_backward_pt",
     "orthros_forward_sft_lse", "orthros_backward_sft_workspace_bytes", "orthros_backward_sft",
@@ -97,6 +97,9 @@ def lib() -> ctypes.CDLL:
         L.orthros_prefill.restype = ctypes.c_int
         L.orthros_decode_step.argtypes = [sp, vp, vp, vp, vp, ap, vp, vp, vp, i64, vp, vp, vp, sz, vp]
         L.orthros_decode_step.restype = ctypes.c_int
+        L.orthros_decode_step_noalloc.argtypes = [sp, vp, vp, vp, vp, ap, vp, vp, vp, i64, vp,
+                                                  vp, vp, vp]
+        L.orthros_decode_step_noalloc.restype = ctypes.c_int
         L.orthros_forward_pt.argtypes = [sp, i64, vp, vp, vp, vp, ap, vp, vp, vp, vp, vp, vp, sz, vp]
         L.orthros_forward_pt.restype = ctypes.c_int
         L.orthros_forward_sft.argtypes = [sp, i64, vp, vp, vp, i64, vp, vp, ap, vp, vp, vp, vp,
@@ -316,6 +319,32 @@ def decode_step(shape: Shape, q_base, q_out, k_new, v_new, affine: Affine, cache
         cache_len.data_ptr(), int(max_len_hint), o_base.data_ptr(), o_out.data_ptr(),
         workspace.data_ptr(), workspace.numel(), _stream(stream))
     _rc(rc, "orthros_decode_step")
+
+
+def decode_step_noalloc(shape: Shape, q_base, q_out, k_new, v_new, affine: Affine, cache_k,
+                        cache_v, cache_len, max_len_hint: int, o_base, o_out, device_status,
+                        stream=None):
+    """orthros_decode_step_noalloc: orthros_decode_step without a workspace (the split partials
+    live in the library's own device array); status bits are OR-ed into device_status."""
+    B, Hq, Hkv, d = shape.batch, shape.num_q_heads, shape.num_kv_heads, shape.head_dim
+    dev, dt = q_base.device, shape.dtype
+    _check(q_base, (B, Hq, d), dt, dev, "q_base")
+    _check(q_out, (B, Hq, d), dt, dev, "q_out")
+    _check(k_new, (B, Hkv, d), dt, dev, "k_new")
+    _check(v_new, (B, Hkv, d), dt, dev, "v_new")
+    _check(cache_k, (B, Hkv, shape.capacity, d), dt, dev, "cache_k")
+    _check(cache_v, (B, Hkv, shape.capacity, d), dt, dev, "cache_v")
+    _check(cache_len, (B,), torch.int32, dev, "cache_len")
+    _check(o_base, (B, Hq, d), dt, dev, "o_base")
+    _check(o_out, (B, Hq, d), dt, dev, "o_out")
+    _check(device_status, (1,), torch.int32, dev, "device_status")
+    aff = affine.c(Hq * d, dev)
+    rc = lib().orthros_decode_step_noalloc(
+        ctypes.byref(shape.c()), q_base.data_ptr(), q_out.data_ptr(), k_new.data_ptr(),
+        v_new.data_ptr(), ctypes.byref(aff), cache_k.data_ptr(), cache_v.data_ptr(),
+        cache_len.data_ptr(), int(max_len_hint), o_base.data_ptr(), o_out.data_ptr(),
+        device_status.data_ptr(), _stream(stream))
+    _rc(rc, "orthros_decode_step_noalloc")
 
 
 def decode_step_paged(shape: Shape, q_base, q_out, k_new, v_new, affine: Affine,

@@ -151,6 +151,35 @@ int orthros_decode_step(const orthros_shape* shape,
                         void* o_base, void* o_out,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* orthros_decode_step for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. It takes no workspace and
+ * calls no allocating routine: the split partials live in a fixed array inside the library,
+ * ORTHROS_NOALLOC_SCRATCH_BYTES bytes on each device, held from the moment the library's code
+ * is loaded onto that device until the process ends. The sticky status bits (as in the
+ * workspace's status word: ORTHROS_STATUS_CACHE_FULL) are OR-ed into *device_status, a
+ * caller-owned device int32 that the caller zeroes.
+ *   - Same arguments, outputs and rounding as orthros_decode_step, minus the workspace.
+ *   - A step needs 2 B H_q nsplit (head_dim + 2) fp32 values (each of the three arrays rounded
+ *     up to 256 bytes), where nsplit (1 .. 64) is the split count orthros_decode_step picks for
+ *     max_len_hint; a step that needs more than ORTHROS_NOALLOC_SCRATCH_BYTES returns
+ *     ORTHROS_E_WORKSPACE and enqueues nothing. The 16-sequence, 32-head, d 128 decode of
+ *     131072-token caches needs about 1 MiB. fp32 calls use no partials.
+ *   - Every call on one device shares that device's array: calls that may overlap in time on
+ *     one device (other streams, other threads) race and give wrong results. Calls on one
+ *     stream are ordered and safe.
+ *   - The first call with a device current looks up the array's device address
+ *     (hipGetSymbolAddress) and keeps it; make that first call before any graph capture.
+ *   - The per-stage timing (orthros_timing_begin) does not record this call. */
+#define ORTHROS_NOALLOC_SCRATCH_BYTES (8u << 20)
+int orthros_decode_step_noalloc(const orthros_shape* shape,
+                                const void* q_base, const void* q_out,
+                                const void* k_new, const void* v_new,
+                                const orthros_affine* affine,
+                                void* cache_k, void* cache_v, int32_t* cache_len,
+                                int64_t max_len_hint,
+                                void* o_base, void* o_out,
+                                int32_t* device_status, hipStream_t stream);
+
 /* Pre-training regime (§3.2, T_in = 0, T_out = T): every position duplicated.
  *   q_base, q_out [B, T, H_q, d]; k, v [B, T, H_kv, d]; o_base, o_out [B, T, H_q, d]
  *   o_base[t] is Eq. 4 with q_base[t]; o_out[t] is Eq. 5 with q_out[t].

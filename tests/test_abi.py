@@ -352,3 +352,18 @@ def test_keys_overlapping_a_page_pool_are_rejected():
                         ws=_addr(32)) == ox.E_INVALID
     assert _paged_write(shape, cache=pool, k=_addr(30), v=_addr(20), cache_len=_addr(31),
                         ws=_addr(32)) == ox.E_INVALID
+
+
+def test_noalloc_decode_rejects_steps_beyond_its_scratch():
+    L = ox.lib()
+    F = FAKE
+    dst = _addr(40)
+    # 64 sequences x 128 query heads: 2 x 64 x 128 rows x (128 + 2) floats > 8 MiB at one split
+    big = _shape(batch=64, num_q_heads=128, num_kv_heads=8, capacity=4096)
+    assert L.orthros_decode_step_noalloc(ctypes.byref(big), F, F, F, F, ctypes.byref(_aff()),
+                                         F, F, F, 100, F, F, dst, None) == ox.E_WORKSPACE
+    s = _shape()
+    assert L.orthros_decode_step_noalloc(ctypes.byref(s), F, F, F, F, ctypes.byref(_aff()),
+                                         F, F, F, 100, F, F, None, None) == ox.E_INVALID
+    assert L.orthros_decode_step_noalloc(ctypes.byref(s), F, F, F, F, ctypes.byref(_aff()),
+                                         F, F, F, -1, F, F, dst, None) == ox.E_INVALID
