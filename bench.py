@@ -51,9 +51,9 @@ CSRC = os.path.join(ROOT, "efficient_attention_amd", "csrc")
 # blank lines are left out): when the code changes, the figure no longer describes the kernel
 # and `traffic` is reported as null.
 TRAFFIC = {
-    "band_kernel": {"sha": "bd86874654fd889e", "bytes_per_launch": 2.7881e+09},
-    "split_rows_kernel": {"sha": "40ae932194d2dd3c", "bytes_per_launch": 8.5958e+09},
-    "split_rows_kernel_paged": {"sha": "40ae932194d2dd3c", "bytes_per_launch": 8.5969e+09},
+    "band_kernel": {"sha": "91724eaf331ba1da", "bytes_per_launch": 2.7998e+09},
+    "split_rows_kernel": {"sha": "0733d21749a8c317", "bytes_per_launch": 8.5959e+09},
+    "split_rows_kernel_paged": {"sha": "0733d21749a8c317", "bytes_per_launch": 8.5969e+09},
 }
 
 
@@ -128,6 +128,23 @@ def timed(step, steps, reset=None):
         step(i)
     torch.cuda.synchronize()
     return ms, ox.timing_end()
+
+
+def per_step_us(step, steps, reset=None):
+    """Each of `steps` calls of step(i) bracketed by HIP events on the current stream (the one
+    the library launches on): median and mean microseconds per call. A separate pass, so the
+    event records stay out of the timed region."""
+    if reset is not None:
+        reset()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for i in range(steps):
+        step(i)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    us = sorted(ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(steps))
+    return us[len(us) // 2], sum(us) / len(us)
 
 
 def bench_prefill(wl, steps, warmup, dev):
@@ -212,6 +229,7 @@ def bench_decode(wl, warmup, dev, page_size=0):
     ms, stages = timed(lambda s: step(s, L0 + s), S, reset=lambda: cl.fill_(L0))
     assert cl.cpu().tolist() == [L0 + S] * B
     assert ox.read_device_status(ws) == 0
+    med, mean_ev = per_step_us(lambda s: step(s, L0 + s), S, reset=lambda: cl.fill_(L0))
     us = ms * 1e3
     # algorithmic bytes: every cached key/value row read once, new k/v read + appended,
     # queries read, outputs written (both streams)
@@ -225,7 +243,7 @@ def bench_decode(wl, warmup, dev, page_size=0):
     split_s = split_ms / 1e3 / max(split_n, 1)
     log(f"decode {us:.1f} us/step; stages {stages}")
     return dict(us=us, stages=stages, step_bytes=step_bytes, split_bytes=split_bytes,
-                split_s=split_s)
+                split_s=split_s, us_median=med, us_mean_events=mean_ev)
 
 
 def bench_sft(wl, R, steps, warmup, dev):
@@ -337,14 +355,36 @@ def bench_prefill_chunked(wl, chunk, steps, warmup, dev, inp, page_size=0):
     return dict(ms=ms, chunks=len(starts), band_ms=stages["band"][0] / max(steps, 1))
 
 
+def host_description():
+    """CPUs this process may run on, the machine's CPU count and model, the BLAS thread count."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([x.get("num_threads", 1) for x in threadpool_info()
+                    if x.get("user_api") == "blas"] + [1])
+    except Exception:  # pragma: no cover
+        blas = 1
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        usable = os.cpu_count() or 1
+    return dict(usable_cpus=usable, os_cpu_count=os.cpu_count(), cpu_model=model,
+                blas_threads=blas)
+
+
 def cpu_baseline(inp, wl, budget_s=12.0):
     """The float64 oracle on host cores: base rows at seeded positions (all heads)."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([x.get("num_threads", 1) for x in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        threads = 1
+    host = host_description()
+    threads = host["blas_threads"]
     log("cpu baseline: copying inputs to host")
     K = inp["k"][0].float().cpu().numpy()
     V = inp["v"][0].float().cpu().numpy()
@@ -368,7 +408,9 @@ def cpu_baseline(inp, wl, budget_s=12.0):
     return dict(value=n / dt, unit="tokens/s", cores=threads, kind="oracle",
                 sample=f"{n} base-stream positions (all {wl.q_heads} heads, window {w}) drawn "
                        f"uniformly from [{min(w, P - 1)}, {P}) of the {P}-token prompt, "
-                       f"float64 numpy, {dt:.1f} s")
+                       f"float64 numpy, {dt:.1f} s",
+                cores_note="cores = the BLAS threads the oracle's products ran on",
+                **host)
 
 
 def main():
@@ -439,6 +481,7 @@ def main():
         rec["decode"] = {
             "metric": "decode-step us @128K", "workload": dw.name, "batch": dw.batch,
             "cache_len": dw.length, "steps": dw.steps, "us_per_step": round(dc["us"], 2),
+            "us_per_step_median": round(dc["us_median"], 2),
             "step_GBps": round(dc["step_bytes"] / (dc["us"] / 1e6) / 1e9, 1),
             "roofline": {"bound": "hbm", "achieved": round(ach / 1e9, 1),
                          "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
@@ -457,7 +500,7 @@ def main():
         rec["decode_paged"] = {
             "metric": "decode-step us @128K", "workload": f"{dw.name}, paged",
             "page_size": ps, "pages": "shuffled pool, one block table row per sequence",
-            "us_per_step": round(dp["us"], 2),
+            "us_per_step": round(dp["us"], 2), "us_per_step_median": round(dp["us_median"], 2),
             "roofline": {"bound": "hbm", "achieved": round(ach / 1e9, 1),
                          "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
                          "frac": round(ach / PEAK_HBM_BYTES, 4),
