@@ -413,6 +413,120 @@ def cpu_baseline(inp, wl, budget_s=12.0):
                 **host)
 
 
+def all_configs(dev, budget_s=6.0):
+    """Each of the five workloads on the GPU next to the float64 oracle on the host cores (a
+    bounded sample of each: rows at seeded positions, or whole calls for the tiny one), in the
+    workload's own unit. Not part of the default run (`--all-configs`)."""
+    import oracle
+    out = []
+    host = host_description()
+
+    def sample(fn, n_max):
+        n, t0 = 0, time.perf_counter()
+        while n < n_max:
+            fn(n)
+            n += 1
+            if time.perf_counter() - t0 > budget_s and n >= 2:
+                break
+        return n, time.perf_counter() - t0
+
+    # tiny fp32 prefill: whole calls
+    wl = syn.WORKLOADS["tiny_fp32_prefill"]
+    inp = syn.make_prefill(wl)
+    B, P, Hq, d = inp["q_base"].shape
+    Hkv = inp["k"].shape[2]
+    shape = ox.Shape(B, Hq, Hkv, d, wl.window, torch.float32, P)
+    g = {n: inp[n].to(dev) for n in ("q_base", "q_out", "k", "v")}
+    aff = ox.Affine(*(a.to(dev) for a in inp["affine"]))
+    ck = torch.empty(B, Hkv, P, d, device=dev)
+    cv, cl = torch.empty_like(ck), torch.zeros(B, dtype=torch.int32, device=dev)
+    ob, oo = torch.empty(B, P, Hq, d, device=dev), torch.empty(B, 1, Hq, d, device=dev)
+    ws = ox.make_workspace(shape, dev)
+    step = lambda i: ox.prefill(shape, g["q_base"], g["q_out"], g["k"], g["v"], aff, ck, cv, cl,  # noqa: E731
+                                ob, oo, ws)
+    for _ in range(3):
+        step(0)
+    ms, _ = timed(step, 50)
+    a64 = [a.double().numpy() for a in inp["affine"]]
+    h64 = {n: inp[n].double().numpy() for n in ("q_base", "q_out", "k", "v")}
+    n, dt = sample(lambda i: oracle.prefill(h64["q_base"], h64["q_out"], h64["k"], h64["v"], *a64,
+                                            window=wl.window), 50)
+    out.append(dict(workload=wl.name, unit="us per call", gpu=ms * 1e3, oracle=dt / n * 1e6,
+                    oracle_sample=f"{n} whole calls"))
+
+    # pre-training forward at the 1.3B shape: both streams at every position
+    wl = syn.WORKLOADS["pt_1p3b_2k"]
+    inp = syn.make_pt(wl, device=dev)
+    B, T, Hq, d = inp["q_base"].shape
+    Hkv = inp["k"].shape[2]
+    shape = ox.Shape(B, Hq, Hkv, d, wl.window, torch.bfloat16, T)
+    aff = ox.Affine(*inp["affine"])
+    ob, oo = (torch.empty(B, T, Hq, d, dtype=torch.bfloat16, device=dev) for _ in range(2))
+    ws = ox.make_workspace(shape, dev)
+    step = lambda i: ox.forward_pt(shape, inp["q_base"], inp["q_out"], inp["k"], inp["v"], aff,  # noqa: E731
+                                   ob, oo, ws)
+    for _ in range(3):
+        step(0)
+    ms, _ = timed(step, 10)
+    rng = np.random.default_rng(wl.seed)
+    pos = rng.integers(0, T, size=400)
+    bs = rng.integers(0, B, size=400)
+    K = [inp["k"][b].float().cpu().numpy() for b in range(B)]
+    V = [inp["v"][b].float().cpu().numpy() for b in range(B)]
+    a64 = [x.cpu().numpy() for x in inp["affine"]]
+    qb = inp["q_base"].float().cpu().numpy()
+    qo = inp["q_out"].float().cpu().numpy()
+    s_ = oracle.default_scale(d)
+
+    def pt_row(i):
+        b, t = int(bs[i]), int(pos[i])
+        oracle.base_row(oracle.scale_offset(qb[b, t], a64[0], a64[1]), K[b], V[b], t, wl.window, s_)
+        oracle.output_row(oracle.scale_offset(qo[b, t], a64[2], a64[3]), K[b], V[b], t, s_)
+    n, dt = sample(pt_row, 400)
+    out.append(dict(workload=wl.name, unit="tokens/s (both streams)", gpu=B * T / (ms / 1e3),
+                    oracle=n / dt, oracle_sample=f"{n} positions at seeded (sequence, position), "
+                                                 f"both rows, all {Hq} heads"))
+    del inp, ob, oo
+    torch.cuda.empty_cache()
+
+    # the two 8B-shaped prefills
+    for name in ("prefill_8b_32k", "prefill_8b_128k"):
+        wl = syn.WORKLOADS[name]
+        pf = bench_prefill(wl, 5, 2, dev)
+        cb = cpu_baseline(pf["inp"], wl, budget_s=budget_s)
+        out.append(dict(workload=name, unit="tokens/s", gpu=wl.length / (pf["ms"] / 1e3),
+                        oracle=cb["value"], oracle_sample=cb["sample"]))
+        del pf
+        torch.cuda.empty_cache()
+
+    # decode: the GPU step time, and the oracle's decode step for sampled sequences
+    dw = syn.WORKLOADS["decode_8b_128k"]
+    dc = bench_decode(dw, 4, dev)
+    torch.cuda.empty_cache()
+    L0, Hq, Hkv, d = dw.length, dw.q_heads, dw.kv_heads, dw.head_dim
+    G = Hq // Hkv
+    inp = syn.make_decode_resident(dw, dev, L0 + 1)
+    a64 = [x.cpu().numpy() for x in inp["affine"]]
+
+    def dec_seq(b):
+        for gg in range(Hkv):
+            Kg = inp["cache_k"][b, gg, :L0].float().cpu().numpy()[:, None, :]
+            Vg = inp["cache_v"][b, gg, :L0].float().cpu().numpy()[:, None, :]
+            hs, cs = slice(gg * G, (gg + 1) * G), slice(gg * G * d, (gg + 1) * G * d)
+            oracle.decode_step([Kg], [Vg], np.array([L0]),
+                               inp["q_base"][0, b:b + 1, hs].float().cpu().numpy(),
+                               inp["q_out"][0, b:b + 1, hs].float().cpu().numpy(),
+                               inp["k_new"][0, b:b + 1, gg:gg + 1].float().cpu().numpy(),
+                               inp["v_new"][0, b:b + 1, gg:gg + 1].float().cpu().numpy(),
+                               *(x[cs] for x in a64), window=dw.window)
+    n, dt = sample(dec_seq, dw.batch)
+    out.append(dict(workload=dw.name, unit="us per step (16 sequences)", gpu=dc["us"],
+                    oracle=dt / n * dw.batch * 1e6,
+                    oracle_sample=f"{n} of the 16 sequences' first step (L = {L0}), every head, "
+                                  f"scaled to 16"))
+    return dict(configs=out, host=host)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -424,6 +538,9 @@ def main():
                     help="skip the SFT and chunked-prefill measurements")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--all-configs", action="store_true",
+                    help="only time each of the five workloads on the GPU and the float64 oracle "
+                         "on a bounded sample of it, and print that table")
     ap.add_argument("--workload", default="prefill_8b_128k",
                     choices=["prefill_8b_128k", "prefill_8b_32k"])
     args = ap.parse_args()
@@ -437,6 +554,9 @@ def main():
     dev = torch.device("cuda:0")
     ox.lib()
 
+    if args.all_configs:
+        print(json.dumps(all_configs(dev)), flush=True)
+        return
     if args.copy_calibration:
         copy_calibration(dev)
     wl = syn.WORKLOADS[args.workload]
