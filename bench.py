@@ -676,6 +676,11 @@ def main():
             "kernel_tflops": {
                 "bwd_q": round(6.0 * tr["d"] * tr["pairs"] / (per.get("bwd_q", 1) / 1e3) / 1e12, 1),
                 "bwd_kv": round(8.0 * tr["d"] * tr["pairs"] / (per.get("bwd_kv", 1) / 1e3) / 1e12, 1)},
+            "gradient_tolerance": "per gradient tensor, against the float64 oracle: mean relative "
+                                  "error <= 5e-3 and max-abs <= 1e-2 x the tensor's largest "
+                                  "magnitude; a bf16 gradient passes through up to four bf16 "
+                                  "roundings (post-affine query, probabilities, score gradient, "
+                                  "the forward output inside D), each <= 2^-9 relative",
         }
     if not args.skip_cpu:
         rec["cpu_baseline"] = cpu_baseline(pf["inp"], wl)
