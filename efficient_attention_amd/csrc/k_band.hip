@@ -381,6 +381,10 @@ __global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
     if (e + 2 < ntiles_s) load_tile(e + 2);
     if (wactive && e >= ea && e <= eb) {
       const bool prev = e > ea, next = e < eb, fl = full(e);
+      // Region A runs at raised wavefront priority, region B at the normal one: the wavefront
+      // of a SIMD that is still in region A (the one that lags) gets the issue slots first, so
+      // the pair reaches the barrier closer together (2-3% on the 128K prefill).
+      __builtin_amdgcn_s_setprio(1);
       if (!prev) qk(S0, e, 0);
       float ps;
       if (prev && fl) {
@@ -398,6 +402,7 @@ __global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
         mask(S0, e, 0);
         ps = expo(S0, P0);
       }
+      __builtin_amdgcn_s_setprio(0);
       settle(S0, P0, ps);
       if (next && fl) {
         qk(S0, e + 1, 0);
