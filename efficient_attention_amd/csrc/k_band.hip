@@ -33,6 +33,10 @@ constexpr int kNW = 8;       // wavefronts per work-group (two per SIMD)
 constexpr int kThreads = 64 * kNW;
 constexpr int kStages = 4;   // LDS ring depth
 constexpr float kLazyBound = 256.f;  // largest tolerated sum of a half's probabilities
+// Reference of a query that has met no key yet: any finite score then gives an infinite
+// tentative probability, which sends the query through the rescale path, and the rescale
+// factor exp2(kUnstarted - max) is 0 (nothing has been accumulated).
+constexpr float kUnstarted = -1e30f;
 
 }  // namespace
 
@@ -274,11 +278,10 @@ __global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
   for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) O[dt][r] = 0.f;
-  // This lane's query row r0w + j: reference max (probabilities are exp2(score - mref)), this lane's
-  // part of the row sum (its half of the keys), and whether the query has met a key of its
-  // window.
-  float mref = 0.f, l = 0.f;
-  bool started = false;
+  // This lane's query row r0w + j: reference max (probabilities are exp2(score - mref);
+  // kUnstarted until the query meets a key of its window) and this lane's part of the row sum
+  // (its half of the keys).
+  float mref = kUnstarted, l = 0.f;
   f32x16 zero16;
 #pragma unroll
   for (int r = 0; r < 16; ++r) zero16[r] = 0.f;
@@ -333,26 +336,26 @@ __global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
     return s0 + s1;
   };
   // After the tentative probabilities of a half: the reference moves only if a probability of
-  // the query could exceed 2^8 (their sum over both lane halves does) or the query meets its
-  // first key. Then O and l are rescaled and this half's probabilities recomputed against the
-  // new reference (the scores are kept unshifted, so the other half's need no correction). The
-  // new reference is the exact maximum, so the probabilities end up <= 1.
+  // the query could exceed 2^8 (their sum over both lane halves does; a query meeting its first
+  // key has an infinite sum). Then O and l are rescaled and this half's probabilities
+  // recomputed against the new reference (the scores are kept unshifted, so the other half's
+  // need no correction). The new reference is the exact maximum, so the probabilities end up
+  // <= 1. The common path tests only this lane's own part of the sum against half the bound
+  // (one compare and a branch); the sum over both lane halves is formed only past that test.
   auto settle = [&](const f32x16& S, bf16x8* Ph, float ps) {
-    const float tot = lane_pair_sum(ps);
-    const bool need = !(tot <= kLazyBound) || !started;
-    if (__builtin_amdgcn_ballot_w64(need)) {
+    if (__builtin_amdgcn_ballot_w64(!(ps <= 0.5f * kLazyBound))) {
+      const float tot = lane_pair_sum(ps);
+      const bool need = !(tot <= kLazyBound);
       float a0 = fmaxf(S[0], S[1]), a1 = fmaxf(S[2], S[3]);
 #pragma unroll
       for (int r = 4; r < 16; r += 4) {
         a0 = fmaxf(a0, fmaxf(S[r], S[r + 1]));
         a1 = fmaxf(a1, fmaxf(S[r + 2], S[r + 3]));
       }
-      const float mx = lane_pair_max(fmaxf(a0, a1)) - mref;
+      const float mx = lane_pair_max(fmaxf(a0, a1));
       const bool move = need && mx != kNegInf;
-      const float dlt = move ? mx : 0.f;
-      const float alpha = started ? fast_exp2(-dlt) : 0.f;  // nothing accumulated yet: O, l = 0
-      started = started || move;
-      mref += dlt;
+      const float alpha = move ? fast_exp2(mref - mx) : 1.f;  // 0 when the query starts here
+      mref = move ? mx : mref;
       l *= alpha;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) O[dt] *= alpha;
@@ -367,9 +370,13 @@ __global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
   //   A: MFMA scores of keys 32..63 of e and PV of keys 32..63 of e-1 | softmax of keys 0..31 of e
   //   B: MFMA scores of keys 0..31 of e+1 and PV of keys 0..31 of e  | softmax of keys 32..63 of e
   // PV of tile e-1 in A is why the LDS ring holds four tiles.
-  // Tiles 0 and 1 before the loop; tile e + 2 is requested at the top of iteration e into the
-  // slot tile e - 2 left (free since the previous barrier) and has landed by the barrier that
-  // ends iteration e (the barrier waits for outstanding loads).
+  // Tiles 0 and 1 before the loop; tile e + 2 is requested in iteration e into the slot tile
+  // e - 2 left (free since the previous barrier) and has landed by the barrier that ends
+  // iteration e (the barrier waits for outstanding loads). A copy instruction holds up its
+  // wavefront for ~100 clocks while the address unit works through the queue, so the two
+  // wavefronts of a SIMD take turns: the second (wavefronts 4..7) copies at the top of the tile,
+  // while the first computes region A, and the first copies after its region A (1-2% on the
+  // 128K prefill against both at the top).
   load_tile(0);
   if (ntiles_s > 1) load_tile(1);
   wait_lds_copies();
@@ -378,7 +385,8 @@ __global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
   f32x16 S0 = zero16, S1 = zero16;
   bf16x8 P0[2], P1[2];
   for (int e = 0; e < ntiles_s; ++e) {
-    if (e + 2 < ntiles_s) load_tile(e + 2);
+    const bool copy_late = wv_s < kNW / 2;  // the first wavefront of its SIMD
+    if (!copy_late && e + 2 < ntiles_s) load_tile(e + 2);
     if (wactive && e >= ea && e <= eb) {
       const bool prev = e > ea, next = e < eb, fl = full(e);
       // Region A runs at raised wavefront priority, region B at the normal one: the wavefront
@@ -404,6 +412,7 @@ __global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
       }
       __builtin_amdgcn_s_setprio(0);
       settle(S0, P0, ps);
+      if (copy_late && e + 2 < ntiles_s) load_tile(e + 2);
       if (next && fl) {
         qk(S0, e + 1, 0);
         pv(P0, e, 0);
@@ -421,6 +430,8 @@ __global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
       }
       settle(S1, P1, ps);
       if (!next) pv(P1, e, 1);
+    } else if (copy_late && e + 2 < ntiles_s) {
+      load_tile(e + 2);
     }
     wait_lds_copies();  // tile e + 2 has landed before the barrier publishes it
     __syncthreads();
