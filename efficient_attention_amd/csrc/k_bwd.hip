@@ -157,6 +157,10 @@ __global__ __launch_bounds__(64 * kQNW) void bwd_q_kernel(BwdQParams p) {
     for (int e = 0; e < 4; ++e)
       dsum += bf16_lo(dr[e]) * bf16_lo(orr[e]) + bf16_hi(dr[e]) * bf16_hi(orr[e]);
   }
+  // Wait for the fragments here: a wait the compiler would otherwise leave inside the tile loop
+  // would also wait for the tile copies in flight (the hardware counts them with these loads).
+#pragma unroll
+  for (int s = 0; s < NKS; ++s) asm volatile("" : "+v"(qf[s]));
   const float Dt = lane_pair_sum(dsum);
   const idx_t lrow = ((idx_t)b * p.Hq + h) * NR + qrow;
   const float lse2 = p.lse[lrow] * kLog2e;
@@ -370,6 +374,9 @@ __global__ __launch_bounds__(64 * kKNW, 2) void bwd_kv_kernel(BwdKVParams p) {
     const uint16_t* kr = kg + (idx_t)(kvalid ? key : T - 1) * kst;
 #pragma unroll
     for (int s = 0; s < NKS; ++s) kf[s] = *reinterpret_cast<const bf16x8*>(kr + 16 * s + 8 * hh);
+    // waited for here, not inside the item loop, where the wait would include the item copies
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) asm volatile("" : "+v"(kf[s]));
   }
   const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) unsigned char*)smem);
   // Value block -> LDS (rows past the end re-read the last row).
@@ -575,25 +582,26 @@ __global__ __launch_bounds__(64 * kKNW, 2) void bwd_kv_kernel(BwdKVParams p) {
         const bf16x8 vbv = *reinterpret_cast<const bf16x8*>(smem + vrow + (rd0 ^ (32u * s)));
         dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vbv, dP, 0, 0, 0);
       }
-      bf16x8 Pb[2], Zb[2];
+      if (!fl) {  // keys outside a row's window (or rows past the end) -> -inf
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        int4 p4 = {0, 0, 0, 0};
-        if (!fl && listed) p4 = *reinterpret_cast<const int4*>(rowp + 8 * q4 + 4 * hh);
-        const int pv[4] = {p4.x, p4.y, p4.z, p4.w};
+        for (int q4 = 0; q4 < 4; ++q4) {
+          int4 p4 = {0, 0, 0, 0};
+          if (listed) p4 = *reinterpret_cast<const int4*>(rowp + 8 * q4 + 4 * hh);
+          const int pv[4] = {p4.x, p4.y, p4.z, p4.w};
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int r = 4 * q4 + k;
-          float s = S[r];
-          if (!fl) {
+          for (int k = 0; k < 4; ++k) {
             const int t = row_pos(8 * q4 + 4 * hh + k, pv[k]);  // -1 past the last row: masked
             const bool ok = key <= t && key > t - w && kvalid;
-            s = ok ? s : kNegInf;
+            S[4 * q4 + k] = ok ? S[4 * q4 + k] : kNegInf;
           }
-          const float pr = fast_exp2(s);
-          Pb[r >> 3][r & 7] = (__bf16)pr;
-          Zb[r >> 3][r & 7] = (__bf16)(pr * dP[r]);
         }
+      }
+      bf16x8 Pb[2], Zb[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pr = fast_exp2(S[r]);
+        Pb[r >> 3][r & 7] = (__bf16)pr;
+        Zb[r >> 3][r & 7] = (__bf16)(pr * dP[r]);
       }
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
