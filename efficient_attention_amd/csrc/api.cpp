@@ -338,11 +338,12 @@ NoAllocLayout noalloc_layout(const orthros_shape* s, int nsplit) {
   return L;
 }
 
-// Backward workspace: status word | q' per stream (bf16) | D per stream | fp32 dq per stream |
-// scale-offset gradient partials.
+// Backward workspace: status word | q' per stream (bf16) | D per stream | -lse per stream (bf16) |
+// fp32 dq per stream and the scale-offset partials (fp32) | per-stream partials of 32-row
+// tiles (bf16: the query-side kernel writes them).
 struct BwdLayout {
-  size_t qp[2], D[2], L2[2], dq[2], part, total;
-  int chunk_rows, nchunk;
+  size_t qp[2], D[2], L2[2], dq[2], part, partq[2], total;
+  int chunk_rows, nchunk, nrt[2];
 };
 // R: rows of the output stream (T for pre-training, the response rows for fine-tuning).
 BwdLayout bwd_layout(const orthros_shape* s, int64_t T, int64_t R) {
@@ -363,9 +364,16 @@ BwdLayout bwd_layout(const orthros_shape* s, int64_t T, int64_t R) {
     L.L2[i] = off;
     off += s->dtype == ORTHROS_BF16 ? up(rows[i] * s->num_q_heads * 4) : 0;
   }
-  for (int i = 0; i < 2; ++i) { L.dq[i] = off; off += up(rows[i] * n * 4); }
+  const bool bf = s->dtype == ORTHROS_BF16;
+  for (int i = 0; i < 2; ++i) { L.dq[i] = off; off += bf ? 0 : up(rows[i] * n * 4); }
   L.part = off;
-  off += up((size_t)L.nchunk * 2 * n * 4);
+  off += bf ? 0 : up((size_t)L.nchunk * 2 * n * 4);
+  const int64_t per_seq[2] = {T, R};
+  for (int i = 0; i < 2; ++i) {
+    L.nrt[i] = (int)((per_seq[i] + 31) / 32);
+    L.partq[i] = off;
+    off += bf ? up((size_t)s->batch * L.nrt[i] * 2 * n * 4) : 0;
+  }
   L.total = off;
   return L;
 }
@@ -481,6 +489,7 @@ int backward_impl(const orthros_shape* s, int64_t T, const void* q_base, const v
   const int wins[2] = {wb, (int)T};
   const int nrows[2] = {(int)T, (int)R};
   const int32_t* poss[2] = {nullptr, out_pos};
+  void* dqo[2] = {dq_base, dq_out};
   if (bf) {
     for (int i = 0; i < 2; ++i) {
       rc = launch_rc(run_stage(ORTHROS_STAGE_BWD_Q, st, [&] {
@@ -495,7 +504,11 @@ int backward_impl(const orthros_shape* s, int64_t T, const void* q_base, const v
     q.q = bf ? qps[i] : qs[i];
     q.alpha = al[i]; q.beta = be[i];
     q.k = k; q.v = v; q.o = os[i]; q.dout = dos[i]; q.lse = lses[i];
-    q.D = Ds[i]; q.lse2n = bf ? l2s[i] : nullptr; q.dq = dqs[i];
+    q.D = Ds[i]; q.lse2n = bf ? l2s[i] : nullptr; q.dq = bf ? nullptr : dqs[i];
+    if (bf) {  // the scale-offset step runs in the query-side kernel's epilogue
+      q.qraw = qs[i]; q.dq_raw = dqo[i];
+      q.part = reinterpret_cast<float*>(w + L.partq[i]); q.nrt = L.nrt[i];
+    }
     q.pos = poss[i]; q.nrows = nrows[i];
     q.B = B; q.T = (int)T; q.Hq = Hq; q.Hkv = Hkv; q.G = G; q.window = wins[i]; q.scale = scale;
     rc = launch_rc(run_stage(ORTHROS_STAGE_BWD_Q, st, [&] {
@@ -516,17 +529,19 @@ int backward_impl(const orthros_shape* s, int64_t T, const void* q_base, const v
     return bf ? launch_bwd_kv_bf16(kv, d, st) : launch_bwd_kv_f32(kv, d, st);
   }));
   if (rc) return rc;
-  void* dqo[2] = {dq_base, dq_out};
   float* da[2] = {dg->dalpha_base, dg->dalpha_out};
   float* db[2] = {dg->dbeta_base, dg->dbeta_out};
   for (int i = 0; i < 2; ++i) {
     AffineGradParams ag{};
     ag.dq = dqs[i]; ag.q = qs[i]; ag.alpha = al[i]; ag.dq_raw = dqo[i];
-    ag.part = reinterpret_cast<float*>(w + L.part);
+    ag.part = reinterpret_cast<float*>(w + (bf ? L.partq[i] : L.part));
     ag.dalpha = da[i]; ag.dbeta = db[i];
-    ag.rows = B * nrows[i]; ag.n = Hq * d; ag.chunk_rows = L.chunk_rows; ag.nchunk = L.nchunk;
+    ag.rows = B * nrows[i]; ag.n = Hq * d; ag.chunk_rows = L.chunk_rows;
+    ag.nchunk = bf ? B * L.nrt[i] : L.nchunk;
     ag.bf16 = bf ? 1 : 0;
-    rc = launch_rc(run_stage(ORTHROS_STAGE_BWD_AFFINE, st, [&] { return launch_affine_grad(ag, st); }));
+    rc = launch_rc(run_stage(ORTHROS_STAGE_BWD_AFFINE, st, [&] {
+      return bf ? launch_affine_grad_final(ag, st) : launch_affine_grad(ag, st);
+    }));
     if (rc) return rc;
   }
   return ORTHROS_OK;

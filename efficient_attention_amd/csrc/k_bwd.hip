@@ -108,6 +108,42 @@ __global__ __launch_bounds__(256) void qprep_kernel(QPrepParams p) {
   }
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Sums v[0..N) over the 32 lanes of each lane half (the lanes sharing lane >> 5), N = 32 M:
+// afterwards lane j (= lane & 31) holds in v[0..M) the sums of the original v[M j + i]. Each
+// of five steps halves the values a lane holds: the lane keeps one half and adds its partner's
+// copy of that half, the partner the other half. Partners are lane j ^ 16 (a swizzle), j ^ 15
+// and j ^ 7 (row and half-row mirrors), j ^ 2 and j ^ 1 (quad permutes): the masks span all
+// five lane bits, and the bit that decides the kept half (4, 3, 2, 1, 0) differs between
+// partners, so both hold the same index range at every step.
+template <int N>
+__device__ __forceinline__ void lane_transpose_sum(float (&v)[N], int j) {
+  static_assert(N % 32 == 0, "32 values or a multiple per lane");
+  auto step = [&](auto partner, int n, int bit) {
+    const bool up = (j >> bit) & 1;
+#pragma unroll
+    for (int i = 0; i < n / 2; ++i) {
+      const float send = up ? v[i] : v[i + n / 2];
+      const float keep = up ? v[i + n / 2] : v[i];
+      v[i] = keep + partner(send);
+    }
+  };
+  auto swz16 = [](float x) {  // lane ^ 16 within 32: bit-mode swizzle, xor mask 16
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F));
+  };
+  auto dpp = [](auto ctrl) {
+    return [](float x) {
+      return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), decltype(ctrl)::value, 0xF, 0xF, true));
+    };
+  };
+  step(swz16, N, 4);
+  step(dpp(std::integral_constant<int, 0x140>{}), N / 2, 3);   // row mirror: lane ^ 15
+  step(dpp(std::integral_constant<int, 0x141>{}), N / 4, 2);   // half-row mirror: lane ^ 7
+  step(dpp(std::integral_constant<int, 0x4E>{}), N / 8, 1);    // quad permute [2, 3, 0, 1]
+  step(dpp(std::integral_constant<int, 0xB1>{}), N / 16, 0);   // quad permute [1, 0, 3, 2]
+}
+
 // ---- query side ------------------------------------------------------------------------------
 // Work-group: 8 wavefronts, HPW query heads of one kv head x (8 / HPW) blocks of 32 rows. p.q
 // is q' (prepared); K and V tiles of 64 keys go through a two-slot LDS ring. Rows are positions,
@@ -322,6 +358,56 @@ __global__ __launch_bounds__(64 * kQNW) void bwd_q_kernel(BwdQParams p) {
     __syncthreads();
   }
 
+  if (p.part) {
+    // The scale-offset step (§3.1: q = alpha (.) q_raw + beta) folded in: dq_raw = alpha (.) dq,
+    // and this wavefront's 32 rows summed into dalpha (dq (.) q_raw) and dbeta (dq) partials.
+    if (!wactive) return;
+    constexpr int NV = 16 * NDT, M = NV / 32;  // values per lane; sums per lane after reducing
+    const idx_t roff = ((idx_t)b * NR + qrow) * p.Hq * D + (idx_t)h * D;
+    const uint16_t* qr = static_cast<const uint16_t*>(p.qraw) + roff;
+    uint16_t* dr = static_cast<uint16_t*>(p.dq_raw) + roff;
+    const float* al = p.alpha + (idx_t)h * D;
+    // value k of a lane: channel 32 (k / 16) + 8 ((k % 16) / 4) + 4 hh + k % 4 of its row
+    auto chan = [&](int k) { return 32 * (k / 16) + 8 * ((k % 16) / 4) + 4 * hh + k % 4; };
+    u32x2 qw[NV / 4];
+#pragma unroll
+    for (int t = 0; t < NV / 4; ++t)  // issued first: they land while the dbeta sums reduce
+      qw[t] = *reinterpret_cast<const u32x2*>(qr + chan(4 * t));
+    float x[NV], vs[NV];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      x[k] = rvalid ? dQ[k / 16][k % 16] * p.scale : 0.f;
+      vs[k] = x[k];
+    }
+    const int chunk = b * p.nrt + r0w / kQW;
+    float* prt = p.part + (idx_t)chunk * 2 * p.Hq * D + (idx_t)h * D;
+    // after the reduction lane j holds the sums of values M j .. M j + M - 1 (adjacent channels)
+    auto store_sums = [&](float* dst) {
+      if constexpr (M == 2) {
+        *reinterpret_cast<f32x2*>(dst + chan(2 * j)) = f32x2{vs[0], vs[1]};
+      } else {
+        dst[chan(j)] = vs[0];
+      }
+    };
+    lane_transpose_sum(vs, j);
+    store_sums(prt + (idx_t)p.Hq * D);  // [1]: dbeta
+#pragma unroll
+    for (int t = 0; t < NV / 4; ++t) {
+      const float qv[4] = {bf16_lo(qw[t][0]), bf16_hi(qw[t][0]), bf16_lo(qw[t][1]), bf16_hi(qw[t][1])};
+      if (rvalid) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(al + chan(4 * t));
+        u32x2 o;
+        o[0] = pack_bf16x2(a[0] * x[4 * t], a[1] * x[4 * t + 1]);
+        o[1] = pack_bf16x2(a[2] * x[4 * t + 2], a[3] * x[4 * t + 3]);
+        *reinterpret_cast<u32x2*>(dr + chan(4 * t)) = o;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vs[4 * t + i] = x[4 * t + i] * qv[i];
+    }
+    lane_transpose_sum(vs, j);
+    store_sums(prt);  // [0]: dalpha
+    return;
+  }
   if (rvalid) {
     float* out = p.dq + ((idx_t)b * NR + row) * p.Hq * D + (idx_t)h * D;
 #pragma unroll

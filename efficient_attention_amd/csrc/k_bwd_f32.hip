@@ -232,6 +232,11 @@ hipError_t launch_bwd_kv_f32(const BwdKVParams& p, int d, hipStream_t s) {
   return hipGetLastError();
 }
 
+hipError_t launch_affine_grad_final(const AffineGradParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(affine_grad_final_kernel, dim3((unsigned)((p.n + 15) / 16)), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_affine_grad(const AffineGradParams& p, hipStream_t s) {
   const unsigned cb4 = (unsigned)((p.n / 4 + 255) / 256);
   hipLaunchKernelGGL(affine_grad_partial_kernel, dim3((unsigned)p.nchunk, cb4), dim3(256), 0, s, p);

@@ -19,6 +19,13 @@ struct BwdQParams {
   float* D;                // out: [B, Hq, nrows] rowsum(dout * o); the bf16 kernel stores -D
   float* lse2n;            // out (bf16 kernel): [B, Hq, nrows] -lse in log2 units
   float* dq;               // out: [B, nrows, Hq, d] fp32 gradient of the post-affine query
+  // bf16 kernel with part set: instead of dq, the raw query's gradient dq_raw = alpha (.) dq
+  // (bf16, [B, nrows, Hq, d]) and, per 32-row tile and head, the tile's sums of dq (.) q_raw and
+  // dq into part[(b nrt + tile) 2 + {0, 1}][Hq d] (nrt = row tiles per sequence)
+  const void* qraw;
+  void* dq_raw;
+  float* part;
+  int nrt;
   const int32_t* pos;      // optional: row r sits at position pos[r] (clamped into [0, T));
                            // without it, rows are positions (nrows = T)
   int nrows;
@@ -64,6 +71,8 @@ hipError_t launch_bwd_kv_f32(const BwdKVParams& p, int d, hipStream_t s);
 hipError_t launch_bwd_q_bf16(const BwdQParams& p, int d, hipStream_t s);
 hipError_t launch_bwd_kv_bf16(const BwdKVParams& p, int d, hipStream_t s);
 hipError_t launch_affine_grad(const AffineGradParams& p, hipStream_t s);
+// Only the fixed-order sum of p.nchunk partials (the bf16 query-side kernel writes them).
+hipError_t launch_affine_grad_final(const AffineGradParams& p, hipStream_t s);
 hipError_t launch_qprep(const void* q0, const void* q1, const float* a0, const float* b0,
                         const float* a1, const float* b1, void* o0, void* o1, idx_t n, int hd,
                         float c, hipStream_t s, int nstreams);
