@@ -81,30 +81,35 @@ struct QPrepParams {
   float c;   // s log2 e
 };
 
+// A thread owns 16-byte column chunks of the rows (no index division) and walks the rows of
+// its work-group's share; the chunk's scale-offset stays in registers.
 __global__ __launch_bounds__(256) void qprep_kernel(QPrepParams p) {
   const int st = blockIdx.y;
   const uint16_t* q = static_cast<const uint16_t*>(p.q[st]);
   uint16_t* o = static_cast<uint16_t*>(p.qp[st]);
-  const float* al = p.alpha[st];
-  const float* be = p.beta[st];
-  for (idx_t i = (idx_t)blockIdx.x * 256 + threadIdx.x; i < p.n / 8; i += (idx_t)gridDim.x * 256) {
-    const idx_t e0 = i * 8;
-    const int c0 = (int)(e0 % p.hd);
-    const u32x4 raw = *reinterpret_cast<const u32x4*>(q + e0);
-    const f32x4 a0 = *reinterpret_cast<const f32x4*>(al + c0);
-    const f32x4 a1 = *reinterpret_cast<const f32x4*>(al + c0 + 4);
-    const f32x4 b0 = *reinterpret_cast<const f32x4*>(be + c0);
-    const f32x4 b1 = *reinterpret_cast<const f32x4*>(be + c0 + 4);
-    u32x4 out;
+  const int nch = p.hd / 8;  // 16-byte chunks per row (hd is a multiple of 8)
+  const idx_t rows = p.n / p.hd;
+  for (int ch = threadIdx.x; ch < nch; ch += 256) {
+    const int c0 = 8 * ch;
+    const f32x4 a0 = *reinterpret_cast<const f32x4*>(p.alpha[st] + c0);
+    const f32x4 a1 = *reinterpret_cast<const f32x4*>(p.alpha[st] + c0 + 4);
+    const f32x4 b0 = *reinterpret_cast<const f32x4*>(p.beta[st] + c0);
+    const f32x4 b1 = *reinterpret_cast<const f32x4*>(p.beta[st] + c0 + 4);
+#pragma unroll 4
+    for (idx_t r = blockIdx.x; r < rows; r += gridDim.x) {
+      const idx_t e0 = r * p.hd + c0;
+      const u32x4 raw = *reinterpret_cast<const u32x4*>(q + e0);
+      u32x4 out;
 #pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      const uint32_t w = raw[e >> 1];
-      const float x0 = bf16_lo(w), x1 = bf16_hi(w);
-      const float y0 = ((e < 4 ? a0[e] : a1[e - 4]) * x0 + (e < 4 ? b0[e] : b1[e - 4])) * p.c;
-      const float y1 = ((e < 4 ? a0[e + 1] : a1[e - 3]) * x1 + (e < 4 ? b0[e + 1] : b1[e - 3])) * p.c;
-      out[e >> 1] = pack_bf16x2(y0, y1);
+      for (int e = 0; e < 8; e += 2) {
+        const uint32_t w = raw[e >> 1];
+        const float x0 = bf16_lo(w), x1 = bf16_hi(w);
+        const float y0 = ((e < 4 ? a0[e] : a1[e - 4]) * x0 + (e < 4 ? b0[e] : b1[e - 4])) * p.c;
+        const float y1 = ((e < 4 ? a0[e + 1] : a1[e - 3]) * x1 + (e < 4 ? b0[e + 1] : b1[e - 3])) * p.c;
+        out[e >> 1] = pack_bf16x2(y0, y1);
+      }
+      *reinterpret_cast<u32x4*>(o + e0) = out;
     }
-    *reinterpret_cast<u32x4*>(o + e0) = out;
   }
 }
 
@@ -733,8 +738,8 @@ hipError_t launch_qprep(const void* q0, const void* q1, const float* a0, const f
                         const float* a1, const float* b1, void* o0, void* o1, idx_t n, int hd,
                         float c, hipStream_t s, int nstreams) {
   QPrepParams p{{q0, q1}, {a0, a1}, {b0, b1}, {o0, o1}, n, hd, c};
-  idx_t blocks = (n / 8 + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
+  idx_t blocks = n / hd;  // rows; each work-group walks rows blocks apart
+  if (blocks > 2048) blocks = 2048;
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(qprep_kernel, dim3((unsigned)blocks, (unsigned)nstreams), dim3(256), 0, s, p);
   return hipGetLastError();
