@@ -31,7 +31,6 @@ namespace orthros {
 namespace {
 constexpr int kTK = 64;     // keys per tile, query side
 constexpr int kQW = 32;     // rows per wavefront (query side) / rows per tile (key side)
-constexpr int kQNW = 8;     // wavefronts per work-group, query side
 constexpr int kKNW = 4;     // wavefronts per work-group, key side, 32 keys each
 constexpr float kLn2 = 0.69314718055994531f;
 
@@ -150,13 +149,15 @@ __device__ __forceinline__ void lane_transpose_sum(float (&v)[N], int j) {
 }
 
 // ---- query side ------------------------------------------------------------------------------
-// Work-group: 8 wavefronts, HPW query heads of one kv head x (8 / HPW) blocks of 32 rows. p.q
+// Work-group: NW wavefronts, HPW query heads of one kv head x (NW / HPW) blocks of 32 rows. p.q
 // is q' (prepared); K and V tiles of 64 keys go through a two-slot LDS ring. Rows are positions,
-// or (with p.pos) row r sits at position pos[r].
-template <int D, int HPW>
-__global__ __launch_bounds__(64 * kQNW) void bwd_q_kernel(BwdQParams p) {
+// or (with p.pos) row r sits at position pos[r]. With one or two heads per kv head, NW is 4
+// (two work-groups per CU): the work-group's rows then span 128 positions instead of 256, and
+// its wavefronts idle on fewer of its tiles (a base-stream wavefront uses w / 64 + 1 of them).
+template <int D, int HPW, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_q_kernel(BwdQParams p) {
   constexpr int NCH = D / 8, ROWB = D * 2, TILEB = kTK * ROWB, STAGEB = 2 * TILEB;
-  constexpr int PB = kQNW / HPW, BMP = kQW * PB, NKS = D / 16, NDT = D / 32;
+  constexpr int PB = NW / HPW, BMP = kQW * PB, NKS = D / 16, NDT = D / 32;
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGEB];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -222,7 +223,7 @@ __global__ __launch_bounds__(64 * kQNW) void bwd_q_kernel(BwdQParams p) {
     qmax_b = last_b;
     tq = rvalid ? row : last_w;
   } else {
-    __shared__ int wrange[2 * kQNW];
+    __shared__ int wrange[2 * NW];
     int mine = p.pos[qrow];
     mine = mine < 0 ? 0 : (mine > T - 1 ? T - 1 : mine);  // clamped into [0, T)
     int lo = rvalid ? mine : 0x7fffffff, hi = rvalid ? mine : -1;
@@ -241,7 +242,7 @@ __global__ __launch_bounds__(64 * kQNW) void bwd_q_kernel(BwdQParams p) {
     qmin_b = 0x7fffffff;
     qmax_b = -1;
 #pragma unroll
-    for (int i = 0; i < kQNW; ++i) {
+    for (int i = 0; i < NW; ++i) {
       qmin_b = min(qmin_b, wrange[2 * i]);
       qmax_b = max(qmax_b, wrange[2 * i + 1]);
     }
@@ -258,8 +259,8 @@ __global__ __launch_bounds__(64 * kQNW) void bwd_q_kernel(BwdQParams p) {
 
   // Tile copies (global side swizzled; wave wv fills rows (wv NINST + i) LROWS .. of a tile).
   constexpr int LROWS = 1024 / ROWB;
-  constexpr int NINST = kTK / LROWS / kQNW;
-  static_assert(NINST >= 1 && NINST * LROWS * kQNW == kTK, "copies cover a tile");
+  constexpr int NINST = kTK / LROWS / NW;
+  static_assert(NINST >= 1 && NINST * LROWS * NW == kTK, "copies cover a tile");
   const uint32_t rowb = (uint32_t)p.Hkv * D * 2u;
   const unsigned char* kb = reinterpret_cast<const unsigned char*>(p.k) + ((idx_t)b * T * p.Hkv + g) * D * 2;
   const unsigned char* vb = reinterpret_cast<const unsigned char*>(p.v) + ((idx_t)b * T * p.Hkv + g) * D * 2;
@@ -337,7 +338,7 @@ __global__ __launch_bounds__(64 * kQNW) void bwd_q_kernel(BwdQParams p) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = kk + 8 * (r >> 2) + (r & 3);
-            const bool ok = key <= tq && key > tq - w && key < T;
+            const bool ok = (key <= tq) & (key > tq - w) & (key < T);  // no branches
             S[r] = ok ? S[r] : kNegInf;
           }
         }
@@ -750,10 +751,11 @@ hipError_t launch_bwd_q_bf16(const BwdQParams& p, int d, hipStream_t s) {
   if (p.G % 8 == 0) hpw = 8;
   else if (p.G % 4 == 0) hpw = 4;
   else if (p.G % 2 == 0) hpw = 2;
-  const int bmp = kQW * (kQNW / hpw);
+  const int nw = hpw >= 4 ? 8 : 4;  // wavefronts per work-group
+  const int bmp = kQW * (nw / hpw);
   const int npb = (p.nrows + bmp - 1) / bmp;  // row blocks, as the kernel derives them
-  dim3 grid((unsigned)(p.B * p.Hkv * (p.G / hpw) * npb)), block(64 * kQNW);
-#define ORTHROS_BWDQ(DD, HH) hipLaunchKernelGGL((bwd_q_kernel<DD, HH>), grid, block, 0, s, p)
+  dim3 grid((unsigned)(p.B * p.Hkv * (p.G / hpw) * npb)), block(64 * nw);
+#define ORTHROS_BWDQ(DD, HH) hipLaunchKernelGGL((bwd_q_kernel<DD, HH, (HH >= 4 ? 8 : 4)>), grid, block, 0, s, p)
   if (d == 128) {
     if (hpw == 8) ORTHROS_BWDQ(128, 8);
     else if (hpw == 4) ORTHROS_BWDQ(128, 4);
