@@ -54,4 +54,23 @@ __device__ __forceinline__ uint32_t xcd_swizzle(uint32_t phys, uint32_t total) {
   return start + k;
 }
 
+// Work order for blocks of unequal length (causal rows, or keys with rows only after them):
+// logical block lid -> (pair, block index counted from the longest), grouping the blocks of a
+// few pairs at a time so that they run together and their operands stay in one XCD's L2, and
+// running each group's blocks longest first. `conc` is the number of work-groups one XCD runs
+// at once; a group holds about that many blocks. (Ordering all pairs' longest blocks first
+// spread every pair over every XCD: the 2048-token causal rows read their keys and values
+// from memory 4-5 times over.)
+__device__ __forceinline__ void grouped_order(uint32_t lid, int pairs, int nblk, int conc,
+                                              int& from_longest, int& pair) {
+  const int gp0 = conc / nblk < 1 ? 1 : (conc / nblk > pairs ? pairs : conc / nblk);
+  const uint32_t gsz = (uint32_t)gp0 * (uint32_t)nblk;
+  const int grp = (int)(lid / gsz);
+  const int r = (int)(lid % gsz);
+  const int p0 = grp * gp0;
+  const int gp = gp0 < pairs - p0 ? gp0 : pairs - p0;  // the last group may hold fewer pairs
+  from_longest = r / gp;
+  pair = p0 + r % gp;
+}
+
 }  // namespace orthros

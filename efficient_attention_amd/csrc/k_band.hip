@@ -59,10 +59,10 @@ __global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
   const uint32_t lid = xcd_swizzle(blockIdx.x, total);
   const bool causal = p.window >= p.nkeys;
   int pb, rest;
-  if (causal) {  // longest rows first
-    const int inner = p.B * p.Hkv * nhc;
-    pb = npb - 1 - (int)(lid / inner);
-    rest = (int)(lid % inner);
+  if (causal) {  // a few (sequence, head group) pairs at a time, longest rows first
+    int from_longest;
+    grouped_order(lid, p.B * p.Hkv * nhc, npb, 32, from_longest, rest);
+    pb = npb - 1 - from_longest;
   } else {
     pb = (int)(lid % npb);
     rest = (int)(lid / npb);

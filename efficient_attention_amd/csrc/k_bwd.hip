@@ -166,10 +166,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_q_kernel(BwdQParams p) {
   const int npb = (NR + BMP - 1) / BMP;
   const uint32_t total = (uint32_t)p.B * p.Hkv * nhc * npb;
   const uint32_t lid = xcd_swizzle(blockIdx.x, total);
-  const int inner = p.B * p.Hkv * nhc;
-  const int pb = __builtin_amdgcn_readfirstlane(npb - 1 - (int)(lid / inner));  // longest first
+  int from_longest, rest;  // a few (sequence, head group) pairs at a time, longest rows first
+  grouped_order(lid, p.B * p.Hkv * nhc, npb, 32 * (8 / NW), from_longest, rest);
+  const int pb = __builtin_amdgcn_readfirstlane(npb - 1 - from_longest);
   if (pb < 0) return;  // the grid covers exactly npb row blocks; nothing past them
-  int rest = (int)(lid % inner);
   const int hc = __builtin_amdgcn_readfirstlane(rest % nhc);
   rest /= nhc;
   const int g = __builtin_amdgcn_readfirstlane(rest % p.Hkv);
@@ -448,9 +448,11 @@ __global__ __launch_bounds__(64 * kKNW, 2) void bwd_kv_kernel(BwdKVParams p) {
   const uint32_t total = (uint32_t)p.B * p.Hkv * nkb;
   const uint32_t lid = xcd_swizzle(blockIdx.x, total);
   const int bg = p.B * p.Hkv;
-  const int kbi = __builtin_amdgcn_readfirstlane((int)(lid / bg));  // block 0 (most rows) first
-  const int g = __builtin_amdgcn_readfirstlane((int)(lid % bg) % p.Hkv);
-  const int b = __builtin_amdgcn_readfirstlane((int)(lid % bg) / p.Hkv);
+  int kbo, pr;  // a few (sequence, kv head) pairs at a time, key block 0 (most rows) first
+  grouped_order(lid, bg, nkb, 64, kbo, pr);
+  const int kbi = __builtin_amdgcn_readfirstlane(kbo);
+  const int g = __builtin_amdgcn_readfirstlane(pr % p.Hkv);
+  const int b = __builtin_amdgcn_readfirstlane(pr / p.Hkv);
   const int k0 = kbi * KB;
   const int k0w = k0 + 32 * wv;
   const int j = lane & 31, hh = lane >> 5;
