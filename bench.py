@@ -51,9 +51,9 @@ CSRC = os.path.join(ROOT, "efficient_attention_amd", "csrc")
 # blank lines are left out): when the code changes, the figure no longer describes the kernel
 # and `traffic` is reported as null.
 TRAFFIC = {
-    "band_kernel": {"sha": "bca65672847b88a4", "bytes_per_launch": 2.8331e+09},
-    "split_rows_kernel": {"sha": "0733d21749a8c317", "bytes_per_launch": 8.5959e+09},
-    "split_rows_kernel_paged": {"sha": "0733d21749a8c317", "bytes_per_launch": 8.5969e+09},
+    "band_kernel": {"sha": "e48c5486bc378dc5", "bytes_per_launch": 2.8370e+09},
+    "split_rows_kernel": {"sha": "b7961c0ace5f389f", "bytes_per_launch": 8.5959e+09},
+    "split_rows_kernel_paged": {"sha": "b7961c0ace5f389f", "bytes_per_launch": 8.5969e+09},
 }
 
 
