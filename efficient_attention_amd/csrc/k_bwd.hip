@@ -280,13 +280,22 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_q_kernel(BwdQParams p) {
     const unsigned char* kt = kb + (idx_t)tb * rowb;
     const unsigned char* vt = vb + (idx_t)tb * rowb;
     const uint32_t st = lds0 + (uint32_t)((e & 1) * STAGEB);
+    if (tb + kTK <= T) {  // a whole tile
 #pragma unroll
-    for (int i = 0; i < NINST; ++i) {
-      const int over = crow[i] - (T - 1 - tb);  // rows past the end re-read the last row
-      const uint32_t back = over > 0 ? (uint32_t)over * rowb : 0u;
-      const uint32_t kd = st + (uint32_t)(wv_s * NINST + i) * 1024u;
-      copy_to_lds(kt, coff[i] - back, kd);
-      copy_to_lds(vt, coff[i] - back, kd + TILEB);
+      for (int i = 0; i < NINST; ++i) {
+        const uint32_t kd = st + (uint32_t)(wv_s * NINST + i) * 1024u;
+        copy_to_lds(kt, coff[i], kd);
+        copy_to_lds(vt, coff[i], kd + TILEB);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NINST; ++i) {
+        const int over = crow[i] - (T - 1 - tb);  // rows past the end re-read the last row
+        const uint32_t back = over > 0 ? (uint32_t)over * rowb : 0u;
+        const uint32_t kd = st + (uint32_t)(wv_s * NINST + i) * 1024u;
+        copy_to_lds(kt, coff[i] - back, kd);
+        copy_to_lds(vt, coff[i] - back, kd + TILEB);
+      }
     }
   };
 
@@ -558,13 +567,22 @@ __global__ __launch_bounds__(64 * kKNW, 2) void bwd_kv_kernel(BwdKVParams p) {
     const unsigned char* qg = reinterpret_cast<const unsigned char*>((st ? qs[1] : qs[0]) + off0);
     const unsigned char* dg = reinterpret_cast<const unsigned char*>((st ? ds[1] : ds[0]) + off0);
     const uint32_t sb = lds0 + VBYTES + (uint32_t)(slot * STG);
+    if (t0 + kQW <= NR) {  // a whole tile (every tile but a stream's last)
 #pragma unroll
-    for (int k = 0; k < NQI; ++k) {
-      const int over = crow[k] - (NR - 1 - t0);  // rows past the end re-read the last row
-      const uint32_t back = over > 0 ? (uint32_t)over * rowq : 0u;
-      const uint32_t dst = sb + (uint32_t)(wk_s * NQI + k) * 1024u;
-      copy_to_lds(qg, coff[k] - back, dst);
-      copy_to_lds(dg, coff[k] - back, dst + QTB);
+      for (int k = 0; k < NQI; ++k) {
+        const uint32_t dst = sb + (uint32_t)(wk_s * NQI + k) * 1024u;
+        copy_to_lds(qg, coff[k], dst);
+        copy_to_lds(dg, coff[k], dst + QTB);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < NQI; ++k) {
+        const int over = crow[k] - (NR - 1 - t0);  // rows past the end re-read the last row
+        const uint32_t back = over > 0 ? (uint32_t)over * rowq : 0u;
+        const uint32_t dst = sb + (uint32_t)(wk_s * NQI + k) * 1024u;
+        copy_to_lds(qg, coff[k] - back, dst);
+        copy_to_lds(dg, coff[k] - back, dst + QTB);
+      }
     }
     if (tid < kQW) {
       const int r = t0 + tid < NR ? t0 + tid : NR - 1;
