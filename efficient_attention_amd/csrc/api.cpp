@@ -339,8 +339,8 @@ NoAllocLayout noalloc_layout(const orthros_shape* s, int nsplit) {
 }
 
 // Backward workspace: status word | q' per stream (bf16) | D per stream | -lse per stream (bf16) |
-// fp32 dq per stream and the scale-offset partials (fp32) | per-stream partials of 32-row
-// tiles (bf16: the query-side kernel writes them).
+// fp32 calls: fp32 dq per stream and the 16-row scale-offset partials | bf16 calls: per-stream
+// scale-offset partials of 32-row tiles (the query-side kernel writes them).
 struct BwdLayout {
   size_t qp[2], D[2], L2[2], dq[2], part, partq[2], total;
   int chunk_rows, nchunk, nrt[2];

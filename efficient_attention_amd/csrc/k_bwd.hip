@@ -10,8 +10,9 @@
 // Kernels:
 //   qprep_kernel   q' = bf16((alpha (.) q_raw + beta) s log2 e) for both streams: the score
 //                  operand, rounded once as in the forward
-//   bwd_q_kernel   per 32 query rows of one stream: dq (fp32, before the scale-offset), and
-//                  -D_t and -lse_t (log2 units), the key side's accumulator seeds
+//   bwd_q_kernel   per 32 query rows of one stream: dq_raw = alpha (.) dq (the raw query's
+//                  gradient) and the rows' scale-offset partial sums, and -D_t and -lse_t (log2
+//                  units), the key side's accumulator seeds
 //                    S^T = K Q'^T, dP^T = V dO^T   (A operand: key / value rows from LDS)
 //                    dQ^T += K^T dZ^T              (A operand: transposed key reads)
 //   bwd_kv_kernel  per 32 keys: dk and dv over both streams' rows of every query head of the

@@ -18,7 +18,7 @@ struct BwdQParams {
   const float* lse;        // [B, Hq, nrows] natural-log log-sum-exp of the forward rows
   float* D;                // out: [B, Hq, nrows] rowsum(dout * o); the bf16 kernel stores -D
   float* lse2n;            // out (bf16 kernel): [B, Hq, nrows] -lse in log2 units
-  float* dq;               // out: [B, nrows, Hq, d] fp32 gradient of the post-affine query
+  float* dq;               // out (fp32 kernel): [B, nrows, Hq, d] gradient of the post-affine query
   // bf16 kernel with part set: instead of dq, the raw query's gradient dq_raw = alpha (.) dq
   // (bf16, [B, nrows, Hq, d]) and, per 32-row tile and head, the tile's sums of dq (.) q_raw and
   // dq into part[(b nrt + tile) 2 + {0, 1}][Hq d] (nrt = row tiles per sequence)
