@@ -100,6 +100,9 @@ CASES = [
     (1, 4, 2, 128, 96, 500, "bf16"),      # window longer than the sequence
     (1, 2, 1, 128, 1, 8, "bf16"),         # one token
     (2, 4, 2, 64, 70, 33, "f32"),
+    (3, 7, 7, 64, 512, 100, "bf16"),      # 21 (sequence, head) pairs: the causal and key-side
+                                          # work orders end on a partial group of pairs
+    (1, 16, 2, 128, 320, 128, "bf16"),    # eight query heads per kv head (8-wavefront groups)
 ]
 
 
