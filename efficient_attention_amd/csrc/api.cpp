@@ -490,7 +490,13 @@ int backward_impl(const orthros_shape* s, int64_t T, const void* q_base, const v
   const int nrows[2] = {(int)T, (int)R};
   const int32_t* poss[2] = {nullptr, out_pos};
   void* dqo[2] = {dq_base, dq_out};
-  if (bf) {
+  if (bf && nrows[0] == nrows[1]) {  // one launch prepares both streams' score operands
+    rc = launch_rc(run_stage(ORTHROS_STAGE_BWD_Q, st, [&] {
+      return launch_qprep(qs[0], qs[1], al[0], be[0], al[1], be[1], qps[0], qps[1],
+                          (idx_t)B * nrows[0] * Hq * d, Hq * d, scale * kLog2e, st, 2);
+    }));
+    if (rc) return rc;
+  } else if (bf) {
     for (int i = 0; i < 2; ++i) {
       rc = launch_rc(run_stage(ORTHROS_STAGE_BWD_Q, st, [&] {
         return launch_qprep(qs[i], qs[i], al[i], be[i], al[i], be[i], qps[i], qps[i],
@@ -531,17 +537,21 @@ int backward_impl(const orthros_shape* s, int64_t T, const void* q_base, const v
   if (rc) return rc;
   float* da[2] = {dg->dalpha_base, dg->dalpha_out};
   float* db[2] = {dg->dbeta_base, dg->dbeta_out};
+  AffineGradParams ag[2] = {};
   for (int i = 0; i < 2; ++i) {
-    AffineGradParams ag{};
-    ag.dq = dqs[i]; ag.q = qs[i]; ag.alpha = al[i]; ag.dq_raw = dqo[i];
-    ag.part = reinterpret_cast<float*>(w + (bf ? L.partq[i] : L.part));
-    ag.dalpha = da[i]; ag.dbeta = db[i];
-    ag.rows = B * nrows[i]; ag.n = Hq * d; ag.chunk_rows = L.chunk_rows;
-    ag.nchunk = bf ? B * L.nrt[i] : L.nchunk;
-    ag.bf16 = bf ? 1 : 0;
-    rc = launch_rc(run_stage(ORTHROS_STAGE_BWD_AFFINE, st, [&] {
-      return bf ? launch_affine_grad_final(ag, st) : launch_affine_grad(ag, st);
+    ag[i].dq = dqs[i]; ag[i].q = qs[i]; ag[i].alpha = al[i]; ag[i].dq_raw = dqo[i];
+    ag[i].part = reinterpret_cast<float*>(w + (bf ? L.partq[i] : L.part));
+    ag[i].dalpha = da[i]; ag[i].dbeta = db[i];
+    ag[i].rows = B * nrows[i]; ag[i].n = Hq * d; ag[i].chunk_rows = L.chunk_rows;
+    ag[i].nchunk = bf ? B * L.nrt[i] : L.nchunk;
+    ag[i].bf16 = bf ? 1 : 0;
+  }
+  if (bf)  // both streams' partials were written by the query-side kernels: one launch sums them
+    return launch_rc(run_stage(ORTHROS_STAGE_BWD_AFFINE, st, [&] {
+      return launch_affine_grad_final(ag, 2, st);
     }));
+  for (int i = 0; i < 2; ++i) {  // the fp32 path shares one partial buffer between the streams
+    rc = launch_rc(run_stage(ORTHROS_STAGE_BWD_AFFINE, st, [&] { return launch_affine_grad(ag[i], st); }));
     if (rc) return rc;
   }
   return ORTHROS_OK;

@@ -187,7 +187,12 @@ __global__ __launch_bounds__(256) void affine_grad_partial_kernel(AffineGradPara
 
 // Sum of the chunk partials, per column: 16 slices of 16 threads each add every 16th chunk
 // (loads unrolled so several are in flight), then the slices combine in a fixed order.
-__global__ __launch_bounds__(256) void affine_grad_final_kernel(AffineGradParams p) {
+// One launch serves one or two streams (blockIdx.y picks the parameter set).
+struct AffineGradPair {
+  AffineGradParams s[2];
+};
+
+__device__ __forceinline__ void affine_grad_final_body(const AffineGradParams& p) {
   __shared__ float red[2][16][16];
   const int cl = threadIdx.x & 15, sl = threadIdx.x >> 4;
   const int c = blockIdx.x * 16 + cl;
@@ -214,6 +219,11 @@ __global__ __launch_bounds__(256) void affine_grad_final_kernel(AffineGradParams
   }
 }
 
+__global__ __launch_bounds__(256) void affine_grad_final_kernel(AffineGradPair pp) {
+  if (blockIdx.y == 0) affine_grad_final_body(pp.s[0]);
+  else affine_grad_final_body(pp.s[1]);
+}
+
 hipError_t launch_bwd_q_f32(const BwdQParams& p, int d, hipStream_t s) {
   dim3 grid(p.nrows, p.Hq, p.B);
   if (d == 128)
@@ -232,8 +242,10 @@ hipError_t launch_bwd_kv_f32(const BwdKVParams& p, int d, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_affine_grad_final(const AffineGradParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(affine_grad_final_kernel, dim3((unsigned)((p.n + 15) / 16)), dim3(256), 0, s, p);
+hipError_t launch_affine_grad_final(const AffineGradParams* p, int count, hipStream_t s) {
+  if (count < 1 || count > 2 || (count == 2 && p[1].n != p[0].n)) return hipErrorInvalidValue;
+  AffineGradPair pp{{p[0], p[count > 1 ? 1 : 0]}};
+  hipLaunchKernelGGL(affine_grad_final_kernel, dim3((unsigned)((p[0].n + 15) / 16), (unsigned)count), dim3(256), 0, s, pp);
   return hipGetLastError();
 }
 
@@ -242,7 +254,8 @@ hipError_t launch_affine_grad(const AffineGradParams& p, hipStream_t s) {
   hipLaunchKernelGGL(affine_grad_partial_kernel, dim3((unsigned)p.nchunk, cb4), dim3(256), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(affine_grad_final_kernel, dim3((unsigned)((p.n + 15) / 16)), dim3(256), 0, s, p);
+  AffineGradPair pp{{p, p}};
+  hipLaunchKernelGGL(affine_grad_final_kernel, dim3((unsigned)((p.n + 15) / 16), 1u), dim3(256), 0, s, pp);
   return hipGetLastError();
 }
 

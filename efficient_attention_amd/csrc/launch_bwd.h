@@ -71,8 +71,9 @@ hipError_t launch_bwd_kv_f32(const BwdKVParams& p, int d, hipStream_t s);
 hipError_t launch_bwd_q_bf16(const BwdQParams& p, int d, hipStream_t s);
 hipError_t launch_bwd_kv_bf16(const BwdKVParams& p, int d, hipStream_t s);
 hipError_t launch_affine_grad(const AffineGradParams& p, hipStream_t s);
-// Only the fixed-order sum of p.nchunk partials (the bf16 query-side kernel writes them).
-hipError_t launch_affine_grad_final(const AffineGradParams& p, hipStream_t s);
+// Only the fixed-order sums of the p[i].nchunk partials of `count` (1 or 2) streams in one launch
+// (the bf16 query-side kernel writes the partials).
+hipError_t launch_affine_grad_final(const AffineGradParams* p, int count, hipStream_t s);
 hipError_t launch_qprep(const void* q0, const void* q1, const float* a0, const float* b0,
                         const float* a1, const float* b1, void* o0, void* o1, idx_t n, int hd,
                         float c, hipStream_t s, int nstreams);
