@@ -51,7 +51,7 @@ CSRC = os.path.join(ROOT, "efficient_attention_amd", "csrc")
 # blank lines are left out): when the code changes, the figure no longer describes the kernel
 # and `traffic` is reported as null.
 TRAFFIC = {
-    "band_kernel": {"sha": "e48c5486bc378dc5", "bytes_per_launch": 2.8376e+09},
+    "band_kernel": {"sha": "db380cfdff7eeecd", "bytes_per_launch": 2.8645e+09},
     "split_rows_kernel": {"sha": "b7961c0ace5f389f", "bytes_per_launch": 8.5959e+09},
     "split_rows_kernel_paged": {"sha": "b7961c0ace5f389f", "bytes_per_launch": 8.5969e+09},
 }

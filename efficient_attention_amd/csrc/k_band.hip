@@ -7,19 +7,21 @@
 // with the score scale and log2 e, and rounded once to bf16.
 //
 // Work-group: 8 wavefronts (two per SIMD), HPW query heads sharing one kv head x (8 / HPW)
-// position blocks of 32 rows. One kv head's 64-key K and V tiles are copied straight from
-// global memory into a 4-slot LDS ring (row-major, 16-byte slots XOR-swizzled per row so the
-// operand reads hit all 64 banks) and read by all eight wavefronts. The copies are waited for
-// only at the barrier that publishes them, never by the reads of the other slots. With the transposed score
-// layout S^T (keys x queries) each lane owns one query and its softmax stays in registers:
-//   S^T[64 x 32]  = K . Q^T        16 x mfma_f32_32x32x16_bf16 (d = 128)
-//   online softmax in the exp2 domain, p = exp2(s - m); the reference m moves only when a half-tile's
-//   probabilities could exceed 2^8 (their sum does), so the common path computes no maximum
-//   O^T[d x 32]  += V^T . P^T      16 x mfma_f32_32x32x16_bf16; P^T straight from the S^T
+// position blocks of 32 rows. One kv head's keys and values are copied in 64-key units straight
+// from global memory into LDS (two K and two V slots of 128 keys; row-major, 16-byte slots
+// XOR-swizzled per row so the operand reads hit all 64 banks) and read by all eight wavefronts.
+// The copies are waited for only at the barrier that publishes them, one per 128 keys. With the
+// transposed score layout S^T (keys x queries) each lane owns one query and its softmax stays in
+// registers; per 32-key chunk:
+//   S^T[32 x 32]  = K . Q^T        8 x mfma_f32_32x32x16_bf16 (d = 128)
+//   online softmax in the exp2 domain, p = exp2(s - m); the reference m moves only when a
+//   chunk's probabilities could exceed 2^8 (their sum does), so the common path computes no
+//   maximum
+//   O^T[d x 32]  += V^T . P^T      8 x mfma_f32_32x32x16_bf16; P^T straight from the S^T
 //                                  registers; V^T through the LDS transpose read
-// The tile loop is software-pipelined over key halves so the vector work issues in the shadow
-// of the matrix cores (see the pipeline comment below). Tiles are visited from the diagonal
-// downwards.
+// The key loop is software-pipelined over chunks so the vector work of one chunk issues in the
+// shadow of the matrix work of its neighbours (see the pipeline comment below). Keys are visited
+// from the diagonal downwards.
 #include "common.h"
 #include "launch.h"
 #include "lds_mfma.h"
@@ -27,12 +29,11 @@
 namespace orthros {
 
 namespace {
-constexpr int kTK = 64;      // keys per tile
+constexpr int kTK = 64;      // keys per copy unit
 constexpr int kQW = 32;      // query rows per wavefront
 constexpr int kNW = 8;       // wavefronts per work-group (two per SIMD)
 constexpr int kThreads = 64 * kNW;
-constexpr int kStages = 4;   // LDS ring depth
-constexpr float kLazyBound = 256.f;  // largest tolerated sum of a half's probabilities
+constexpr float kLazyBound = 256.f;  // largest tolerated sum of a chunk's probabilities
 // Reference of a query that has met no key yet: any finite score then gives an infinite
 // tentative probability, which sends the query through the rescale path, and the rescale
 // factor exp2(kUnstarted - max) is 0 (nothing has been accumulated).
@@ -44,13 +45,12 @@ template <int D, int HPW>
 __global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
   constexpr int NCH = D / 8;             // 16-byte slots per row
   constexpr int ROWB = D * 2;            // bytes per K/V row
-  constexpr int TILEB = kTK * ROWB;      // bytes per K (or V) tile
-  constexpr int STAGEB = 2 * TILEB;      // K + V
+  constexpr int UNITB = kTK * ROWB;      // bytes per 64-key unit of K (or V)
   constexpr int PB = kNW / HPW;          // position blocks per work-group
   constexpr int BMP = kQW * PB;          // positions per work-group
   constexpr int NKS = D / 16;            // QK k-steps
   constexpr int NDT = D / 32;            // O^T tiles
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kStages * STAGEB];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[8 * UNITB];  // K slots 0, 1; V slots 2, 3
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int nhc = p.G / HPW;
@@ -152,28 +152,33 @@ __global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
     for (int s = 0; s < NKS; ++s) asm volatile("" : "+v"(qf[s]));
   }
 
-  // Key range of the work-group (tiles tile_hi, tile_hi - 64, ..., tile_lo) and of this wave.
+  // Key range of the work-group, in 64-key units visited from the top down: unit m holds keys
+  // unit_hi - 64 m .. + 63, m = 0 .. nunits - 1. Each unit is two 32-key chunks, upper first, so
+  // chunk u holds keys chunk_hi - 32 u .. + 31 and the keys descend throughout.
   const int w = p.window;
   const int nk = p.nkeys;
   const int glo = qmin_b - w + 1 > 0 ? qmin_b - w + 1 : 0;
   const int ghi = qmax_b < nk - 1 ? qmax_b : nk - 1;
-  const int tile_lo = glo / kTK * kTK;
-  const int tile_hi = ghi / kTK * kTK;
-  const int ntiles = (tile_hi - tile_lo) / kTK + 1;
-  // Scalar copies for the loop and the tile copies (the per-wavefront conditions below keep
-  // their vector form: as scalar branches they cost the register allocator more than they save).
-  const int tile_hi_s = __builtin_amdgcn_readfirstlane(tile_hi);
-  const int ntiles_s = __builtin_amdgcn_readfirstlane(ntiles);
-  const int wlo = qmin_w - w + 1;  // lowest key any row of this wavefront needs (may be < 0)
-  auto tile_key = [&](int e) { return tile_hi - kTK * e; };
-  // This wavefront's tiles: ea (holds its highest row) .. eb (holds its lowest key), contiguous.
-  const int ea = tile_hi > qmax_w ? (tile_hi - qmax_w + kTK - 1) / kTK : 0;
-  const int eb_w = (tile_hi + kTK - 1 - wlo) / kTK;
-  const int eb = eb_w < ntiles - 1 ? eb_w : ntiles - 1;
-  // Unmasked only if every key of the tile lies in every row's window.
-  auto full = [&](int e) {
-    const int tb = tile_key(e);
-    return (tb + kTK - 1 <= qmin_w) && (tb >= qmax_w - w + 1) && (tb + kTK - 1 <= nk - 1);
+  const int unit_lo = glo / kTK * kTK;
+  const int unit_hi = ghi / kTK * kTK;
+  const int nunits = (unit_hi - unit_lo) / kTK + 1;
+  // Scalar copies for the loop and the copies (the per-wavefront conditions below keep their
+  // vector form: as scalar branches they cost the register allocator more than they save).
+  const int unit_hi_s = __builtin_amdgcn_readfirstlane(unit_hi);
+  const int nunits_s = __builtin_amdgcn_readfirstlane(nunits);
+  const int nspans = (nunits_s + 1) / 2;  // spans of two units (128 keys)
+  const int chunk_hi = unit_hi + 32;
+  auto chunk_key = [&](int u) { return chunk_hi - 32 * u; };
+  // This wavefront's chunks: ua (holds its highest row) .. ub (holds its lowest key).
+  const int wlo = qmin_w - w + 1 > 0 ? qmin_w - w + 1 : 0;  // lowest key any row needs
+  const int ua = chunk_hi > qmax_w ? (chunk_hi - qmax_w + 31) / 32 : 0;
+  const int ub_w = (chunk_hi + 31 - wlo) / 32;
+  const int ub = !wactive ? -1 : (ub_w < 2 * nunits - 1 ? ub_w : 2 * nunits - 1);
+  auto in_range = [&](int u) { return (u >= ua) & (u <= ub); };
+  // Unmasked only if every key of the chunk lies in every row's window.
+  auto full = [&](int u) {
+    const int kb = chunk_key(u);
+    return (kb + 31 <= qmin_w) & (kb >= qmax_w - w + 1) & (kb + 31 <= nk - 1);
   };
 
   const uint16_t* kbase = reinterpret_cast<const uint16_t*>(p.k) + (idx_t)b * p.k_sb + (idx_t)g * p.k_sh;
@@ -187,12 +192,12 @@ __global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
   // per LDS cycle: 64 bytes from each of 4 consecutive rows, which f places in four different
   // 16-bank groups (with f = 4 ((r >> 1) % 4), rows r and r + 1 shared one: 2-way conflicts, 155
   // against 239 bytes per clock and CU measured). Wave wv fills rows (wv NINST + i) LROWS ..
-  // of every tile.
+  // of every unit.
   constexpr int LROWS = 1024 / ROWB;
   constexpr int NINST = kTK / LROWS / kNW;
-  static_assert(NINST >= 1 && NINST * LROWS * kNW == kTK, "staging covers a tile exactly");
-  // Each lane's byte offsets within a tile are fixed; a tile's base address is a scalar, so a
-  // load is one instruction with no address arithmetic. In the tile holding the last key, rows
+  static_assert(NINST >= 1 && NINST * LROWS * kNW == kTK, "staging covers a unit exactly");
+  // Each lane's byte offsets within a unit are fixed; a unit's base address is a scalar, so a
+  // load is one instruction with no address arithmetic. In the unit holding the last key, rows
   // past the sequence end re-read the last row (every read stays inside K and V).
   const uint32_t rowb = (uint32_t)p.k_st * 2u;  // bytes between consecutive keys
   uint32_t skoff[NINST], svoff[NINST];
@@ -207,54 +212,49 @@ __global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
   }
   const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) unsigned char*)smem);
   const int wv_s = __builtin_amdgcn_readfirstlane(wv);
-  // Paged pool: a 64-key tile lies inside one page (pages hold >= 64 rows, tiles start at
-  // multiples of 64), so one table entry (a scalar read) gives the tile's base. Tiles are
-  // requested in order 0, 1, 2, ...; the entry of the next one is read a request ahead.
-  auto page_of = [&](int e) -> int32_t {
-    const int tb = tile_hi_s - kTK * (e < ntiles_s ? e : ntiles_s - 1);
+  // Paged pool: a 64-key unit lies inside one page (pages hold >= 64 rows, units start at
+  // multiples of 64), so one table entry (a scalar read) gives the unit's base. The entries a
+  // span's copies use are read one span ahead.
+  auto page_of = [&](int m) -> int32_t {
+    const int tb = unit_hi_s - kTK * (m < nunits_s ? m : nunits_s - 1);
     // read through the scalar cache (the table is constant while the kernel runs): a vector
     // load here would make the wave wait for it, and for every copy in flight, on the spot
     const __attribute__((address_space(4))) int32_t* tbl =
         (const __attribute__((address_space(4))) int32_t*)p.pg.table;
     return tbl[(idx_t)b * p.pg.tbl_sb + (tb >> p.pg.ps_log2)];
   };
-  int32_t next_page = p.pg.table ? page_of(0) : 0;
-  auto load_tile = [&](int e) {
-    const int tb = tile_hi_s - kTK * e;
-    idx_t toff = (idx_t)tb * rowb;  // bytes from the (sequence, kv head) base to the tile
+  // Unit m of K (or V) -> LDS byte offset `dst`; `page` is its table entry (paged pool).
+  auto copy_unit = [&](int m, int32_t page, const uint16_t* base, const uint32_t* off, uint32_t dst) {
+    const int tb = unit_hi_s - kTK * m;
+    idx_t toff = (idx_t)tb * rowb;  // bytes from the (sequence, kv head) base to the unit
     if (p.pg.table) {
-      int32_t page = next_page;
-      next_page = page_of(e + 1);
       if (page < 0 || (int64_t)page >= p.pg.num_pages) {
         __hip_atomic_fetch_or(p.pg.status, kStatusBadPage, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         page = 0;
       }
-      // bytes: the page's start (k_sp elements of 2 bytes per page) plus the tile's rows
+      // the page's start (k_sp elements of 2 bytes per page) plus the unit's rows
       toff = (idx_t)page * p.pg.k_sp * 2 + (idx_t)(tb & ((1 << p.pg.ps_log2) - 1)) * rowb;
     }
-    const unsigned char* kt = reinterpret_cast<const unsigned char*>(kbase) + toff;
-    const unsigned char* vt = reinterpret_cast<const unsigned char*>(vbase) + toff;
-    unsigned char* st = smem + (e % kStages) * STAGEB;
+    const unsigned char* src = reinterpret_cast<const unsigned char*>(base) + toff;
+    const uint32_t d0 = lds0 + dst + (uint32_t)(wv_s * NINST) * 1024u;
     if (tb + kTK <= nk) {
 #pragma unroll
-      for (int i = 0; i < NINST; ++i) {
-        const uint32_t kd = lds0 + (uint32_t)(st - smem) + (wv_s * NINST + i) * 1024;
-        copy_to_lds(kt, skoff[i], kd);
-        copy_to_lds(vt, svoff[i], kd + TILEB);
-      }
+      for (int i = 0; i < NINST; ++i) copy_to_lds(src, off[i], d0 + (uint32_t)i * 1024u);
     } else {
 #pragma unroll
       for (int i = 0; i < NINST; ++i) {
         const int over = srow[i] - (nk - 1 - tb);
         const uint32_t back = over > 0 ? (uint32_t)over * rowb : 0u;
-        const uint32_t kd = lds0 + (uint32_t)(st - smem) + (wv_s * NINST + i) * 1024;
-        copy_to_lds(kt, skoff[i] - back, kd);
-        copy_to_lds(vt, svoff[i] - back, kd + TILEB);
+        copy_to_lds(src, off[i] - back, d0 + (uint32_t)i * 1024u);
       }
     }
   };
+  // LDS: K spans in slots 0, 1 (span e = units 2e, 2e + 1 at +0 and +UNITB), V spans in slots
+  // 2, 3 (V span e = units 2e - 1, 2e at +0 and +UNITB).
+  auto k_dst = [&](int m) { return (uint32_t)(((m >> 1) & 1) * 2 * UNITB + (m & 1) * UNITB); };
+  auto v_dst = [&](int m) { return (uint32_t)(4 * UNITB + (((m + 1) >> 1) & 1) * 2 * UNITB + (m & 1 ? 0 : UNITB)); };
 
-  // Per-lane LDS read offsets (bytes within a stage).
+  // Per-lane LDS read offsets (bytes within a unit).
   // QK A operand: key row 32 m + j, channel slot 2 s + hh.
   int qk_off[NKS];
 #pragma unroll
@@ -269,7 +269,7 @@ __global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
       const int chunk = 4 * dt + 2 * (G & 1) + ((L & 3) >> 1);
-      pv_off[dt] = TILEB + row * ROWB + 16 * (chunk ^ fv) + 8 * (L & 1);
+      pv_off[dt] = row * ROWB + 16 * (chunk ^ fv) + 8 * (L & 1);
     }
   }
 
@@ -287,40 +287,41 @@ __global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
   for (int r = 0; r < 16; ++r) zero16[r] = 0.f;
 
   // ---- building blocks ----------------------------------------------------------------------
-  // Scores of key half m of tile e (NKS MFMAs): S = K rows 32 m .. 32 m + 31 . Q^T.
-  auto qk = [&](f32x16& S, int e, int m) {
-    const unsigned char* st = smem + (e % kStages) * STAGEB + 32 * m * ROWB;
+  // A chunk's rows in LDS: ka / va are this lane's read offsets into the span's K / V slot
+  // (formed once per span), at the chunk's constant offset `co` in the slot, which folds into
+  // the read instructions.
+  // Scores of a chunk (NKS MFMAs): S = K rows of the chunk . Q^T.
+  auto qk = [&](f32x16& S, const int* ka, int co) {
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(st + qk_off[s]);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(smem + ka[s] + co);
       S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], s == 0 ? zero16 : S, 0, 0, 0);
     }
   };
-  // O^T += V^T . P^T over key half m of tile e (2 16-key steps x NDT MFMAs).
-  auto pv = [&](const bf16x8* Ph, int e, int m) {
-    unsigned char* st = smem + (e % kStages) * STAGEB;
+  // O^T += V^T . P^T over a chunk (2 16-key steps x NDT MFMAs).
+  auto pv = [&](const bf16x8* Ph, const int* va, int co) {
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        unsigned char* base = st + pv_off[dt] + (16 * (2 * m + k2)) * ROWB;
+        unsigned char* base = smem + va[dt] + co + 16 * k2 * ROWB;
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base));
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + 8 * ROWB));
         O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cat_tr(lo, hi), Ph[k2], O[dt], 0, 0, 0);
       }
     }
   };
-  // Keys outside the query's window (or past the sequence) of half m of tile e -> -inf.
-  auto mask = [&](f32x16& S, int e, int m) {
-    const int kb = tile_key(e) + 32 * m + 4 * hh;
+  // Keys of chunk u outside the query's window (or past the sequence) -> -inf.
+  auto mask = [&](f32x16& S, int u) {
+    const int kb = chunk_key(u) + 4 * hh;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int k = kb + 8 * (r >> 2) + (r & 3);
-      const bool ok = k <= tq && k > tq - w && k < nk;
+      const bool ok = (k <= tq) & (k > tq - w) & (k < nk);
       S[r] = ok ? S[r] : kNegInf;
     }
   };
-  // Probabilities of one half against the current reference (bf16, as the PV operand) and
+  // Probabilities of one chunk against the current reference (bf16, as the PV operand) and
   // this lane's sum of them.
   auto expo = [&](const f32x16& S, bf16x8* Ph) {
     float s0 = 0.f, s1 = 0.f;
@@ -335,11 +336,11 @@ __global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
     }
     return s0 + s1;
   };
-  // After the tentative probabilities of a half: the reference moves only if a probability of
+  // After the tentative probabilities of a chunk: the reference moves only if a probability of
   // the query could exceed 2^8 (their sum over both lane halves does; a query meeting its first
-  // key has an infinite sum). Then O and l are rescaled and this half's probabilities
-  // recomputed against the new reference (the scores are kept unshifted, so the other half's
-  // need no correction). The new reference is the exact maximum, so the probabilities end up
+  // key has an infinite sum). Then O and l are rescaled and this chunk's probabilities
+  // recomputed against the new reference (the scores are kept unshifted, so no other chunk's
+  // need a correction). The new reference is the exact maximum, so the probabilities end up
   // <= 1. The common path tests only this lane's own part of the sum against half the bound
   // (one compare and a branch); the sum over both lane halves is formed only past that test.
   auto settle = [&](const f32x16& S, bf16x8* Ph, float ps) {
@@ -363,78 +364,109 @@ __global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
     }
     l += ps;
   };
+  // Region u, one basic block on the common path, so the matrix cores and the vector ALUs work
+  // side by side: MFMA scores of chunk u + 1 (into Sn) and PV of chunk u - 1 (from Pp) | the
+  // tentative probabilities of chunk u (from Sc into Pc). Returns this lane's part of their
+  // sum, 0 if the wavefront has no keys in chunk u (the settle that follows is then a no-op;
+  // kept outside the region's branches, where it stays a branch of its own).
+  auto region = [&](int u, const int* ka, const int* va, int co, f32x16& Sn, const bf16x8* Pp,
+                    f32x16& Sc, bf16x8* Pc) -> float {
+    const bool dn = in_range(u + 1), dp = in_range(u - 1), dc = in_range(u);
+    float ps = 0.f;
+    if (dn & dp & dc & full(u)) {
+      qk(Sn, ka, co);
+      pv(Pp, va, co);
+      ps = expo(Sc, Pc);
+      interleave<16, 4, 2, 3>();
+    } else {
+      if (dn) qk(Sn, ka, co);
+      if (dp) pv(Pp, va, co);
+      if (dc) {
+        mask(Sc, u);
+        ps = expo(Sc, Pc);
+      }
+    }
+    return ps;
+  };
 
   // ---- pipeline -----------------------------------------------------------------------------
-  // Per tile e, in two regions that are each one basic block, so the matrix cores and the
-  // vector ALUs work side by side:
-  //   A: MFMA scores of keys 32..63 of e and PV of keys 32..63 of e-1 | softmax of keys 0..31 of e
-  //   B: MFMA scores of keys 0..31 of e+1 and PV of keys 0..31 of e  | softmax of keys 32..63 of e
-  // PV of tile e-1 in A is why the LDS ring holds four tiles.
-  // Tiles 0 and 1 before the loop; tile e + 2 is requested in iteration e into the slot tile
-  // e - 2 left (free since the previous barrier) and has landed by the barrier that ends
-  // iteration e (the barrier waits for outstanding loads). A copy instruction holds up its
-  // wavefront for ~100 clocks while the address unit works through the queue, so the two
-  // wavefronts of a SIMD take turns: the second (wavefronts 4..7) copies at the top of the tile,
-  // while the first computes region A, and the first copies after its region A (1-2% on the
-  // 128K prefill against both at the top).
-  load_tile(0);
-  if (ntiles_s > 1) load_tile(1);
+  // Regions u = -1, 0, 1, ... in order; region u reads K of chunk u + 1 and V of chunk u - 1.
+  // A barrier stands before every region u = 4e - 1, after which the span of regions 4e - 1 ..
+  // 4e + 2 reads K units 2e, 2e + 1 (chunks 4e .. 4e + 3) and V units 2e - 1, 2e (chunks
+  // 4e - 2 .. 4e + 1), and the region at offset q in the span reads each at the constant offset
+  // (q / 2) UNITB + (q even ? 32 rows : 0) in its slot. During the span each wavefront copies
+  // its rows of K units 2e + 2, 2e + 3 and V units 2e + 1, 2e + 2 into the slots the previous
+  // span read, so two K and two V slots (128 KB at d = 128) suffice, and the copies have landed
+  // by the next barrier (each wavefront waits for its own before it). A copy instruction holds
+  // up its wavefront while the address unit works through the queue, so the two wavefronts of
+  // a SIMD take turns: the second (wavefronts 4..7) copies at the top of the span, the first
+  // after its first region.
+  int32_t pg1 = 0, pg2 = 0, pg3 = 0;  // table entries of units 2e + 1 .. 2e + 3
+  if (p.pg.table) {
+    copy_unit(0, page_of(0), kbase, skoff, k_dst(0));
+    copy_unit(0, page_of(0), vbase, svoff, v_dst(0));
+    if (nunits_s > 1) copy_unit(1, page_of(1), kbase, skoff, k_dst(1));
+    pg1 = page_of(1);
+    pg2 = page_of(2);
+    pg3 = page_of(3);
+  } else {
+    copy_unit(0, 0, kbase, skoff, k_dst(0));
+    copy_unit(0, 0, vbase, svoff, v_dst(0));
+    if (nunits_s > 1) copy_unit(1, 0, kbase, skoff, k_dst(1));
+  }
   wait_lds_copies();
   __syncthreads();
 
   f32x16 S0 = zero16, S1 = zero16;
   bf16x8 P0[2], P1[2];
-  for (int e = 0; e < ntiles_s; ++e) {
-    const bool copy_late = wv_s < kNW / 2;  // the first wavefront of its SIMD
-    if (!copy_late && e + 2 < ntiles_s) load_tile(e + 2);
-    if (wactive && e >= ea && e <= eb) {
-      const bool prev = e > ea, next = e < eb, fl = full(e);
-      // Region A runs at raised wavefront priority, region B at the normal one: the wavefront
-      // of a SIMD that is still in region A (the one that lags) gets the issue slots first, so
-      // the pair reaches the barrier closer together (2-3% on the 128K prefill).
-      __builtin_amdgcn_s_setprio(1);
-      if (!prev) qk(S0, e, 0);
-      float ps;
-      if (prev && fl) {
-        qk(S1, e, 1);
-        pv(P1, e - 1, 1);
-        ps = expo(S0, P0);
-        interleave<16, 4, 2, 3>();
-      } else if (prev) {
-        qk(S1, e, 1);
-        pv(P1, e - 1, 1);
-        mask(S0, e, 0);
-        ps = expo(S0, P0);
-      } else {
-        qk(S1, e, 1);
-        mask(S0, e, 0);
-        ps = expo(S0, P0);
-      }
-      __builtin_amdgcn_s_setprio(0);
-      settle(S0, P0, ps);
-      if (copy_late && e + 2 < ntiles_s) load_tile(e + 2);
-      if (next && fl) {
-        qk(S0, e + 1, 0);
-        pv(P0, e, 0);
-        ps = expo(S1, P1);
-        interleave<16, 4, 2, 3>();
-      } else if (next) {
-        qk(S0, e + 1, 0);
-        pv(P0, e, 0);
-        mask(S1, e, 1);
-        ps = expo(S1, P1);
-      } else {
-        pv(P0, e, 0);
-        mask(S1, e, 1);
-        ps = expo(S1, P1);
-      }
-      settle(S1, P1, ps);
-      if (!next) pv(P1, e, 1);
-    } else if (copy_late && e + 2 < ntiles_s) {
-      load_tile(e + 2);
+  const bool copy_late = wv_s < kNW / 2;  // the first wavefront of its SIMD
+  auto copies = [&](int e) {
+    const int m = 2 * e;
+    if (m + 1 < nunits_s) copy_unit(m + 1, pg1, vbase, svoff, v_dst(m + 1));
+    if (m + 2 < nunits_s) {
+      copy_unit(m + 2, pg2, vbase, svoff, v_dst(m + 2));
+      copy_unit(m + 2, pg2, kbase, skoff, k_dst(m + 2));
     }
-    wait_lds_copies();  // tile e + 2 has landed before the barrier publishes it
-    __syncthreads();
+    if (m + 3 < nunits_s) copy_unit(m + 3, pg3, kbase, skoff, k_dst(m + 3));
+    if (p.pg.table) {  // the next span's entries, read now (after the last use) and used then
+      pg1 = pg3;
+      pg2 = page_of(m + 4);
+      pg3 = page_of(m + 5);
+    }
+  };
+  for (int e = 0; e <= nspans; ++e) {
+    if (!copy_late) copies(e);
+    // Read offsets into K span e (slot e % 2) and V span e (slot 2 + e % 2).
+    int ka[NKS], va[NDT];
+    const int ks = (e & 1) * 2 * UNITB, vs = (4 + 2 * (e & 1)) * UNITB;
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+      ka[s] = qk_off[s] + ks;
+      asm volatile("" : "+v"(ka[s]));  // formed here, not inside each region
+    }
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      va[dt] = pv_off[dt] + vs;
+      asm volatile("" : "+v"(va[dt]));
+    }
+    const int u0 = 4 * e - 1;
+    // The first half of a span runs at raised wavefront priority: the wavefront of a SIMD
+    // that lags (the one that copied first) gets the issue slots first.
+    __builtin_amdgcn_s_setprio(1);
+    float ps = region(u0, ka, va, 32 * ROWB, S0, P0, S1, P1);
+    settle(S1, P1, ps);
+    if (copy_late) copies(e);
+    ps = region(u0 + 1, ka, va, 0, S1, P1, S0, P0);
+    __builtin_amdgcn_s_setprio(0);
+    settle(S0, P0, ps);
+    ps = region(u0 + 2, ka, va, UNITB + 32 * ROWB, S0, P0, S1, P1);
+    settle(S1, P1, ps);
+    ps = region(u0 + 3, ka, va, UNITB, S1, P1, S0, P0);
+    settle(S0, P0, ps);
+    if (e < nspans) {
+      wait_lds_copies();  // this wave's copies of the next span have landed
+      __syncthreads();
+    }
   }
 
   const float lt = lane_pair_sum(l);  // both lane halves of the query column
