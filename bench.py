@@ -13,7 +13,8 @@ The same JSON line carries:
   * decode: the 16 x 131072-token decode workload, 128 consecutive decode steps, as
     microseconds per step and the split-key kernel's algorithmic HBM bytes / launch time
     against 8 TB/s;
-  * prefill_chunked: the same prompt fed as 16 chunks of 8192 tokens (orthros_prefill_chunk);
+  * prefill_chunked: the same prompt fed as 16 chunks of 8192 tokens (orthros_prefill_chunk),
+    the output row computed with the last chunk only;
   * sft: the supervised fine-tuning regime at the 1.3B-like shape (batch 4, T 2048, 16 heads,
     window 512) with output rows at the last 512 positions, and its banded kernels' share of
     the bf16 peak;
@@ -51,7 +52,7 @@ CSRC = os.path.join(ROOT, "efficient_attention_amd", "csrc")
 # blank lines are left out): when the code changes, the figure no longer describes the kernel
 # and `traffic` is reported as null.
 TRAFFIC = {
-    "band_kernel": {"sha": "db380cfdff7eeecd", "bytes_per_launch": 2.8645e+09},
+    "band_kernel": {"sha": "5ae97701e3583e93", "bytes_per_launch": 2.8577e+09},
     "split_rows_kernel": {"sha": "b7961c0ace5f389f", "bytes_per_launch": 8.5959e+09},
     "split_rows_kernel_paged": {"sha": "b7961c0ace5f389f", "bytes_per_launch": 8.5969e+09},
 }
@@ -315,7 +316,8 @@ def bench_training(wl, steps, warmup, dev):
 def bench_prefill_chunked(wl, chunk, steps, warmup, dev, inp, page_size=0):
     """The same prompt prefilled in chunks of `chunk` tokens (cache grows chunk by chunk); with
     page_size > 0 into a shuffled pool of pages (cache_len is reset to 0 at the start of each
-    step, one small fill kernel)."""
+    step, one small fill kernel). Only the last chunk computes the output-stream row (the
+    prompt's last token); the chunks before it pass none."""
     B, P, Hq, d = inp["q_base"].shape
     Hkv = inp["k"].shape[2]
     cap = P if not page_size else -(-P // page_size) * page_size
@@ -339,15 +341,18 @@ def bench_prefill_chunked(wl, chunk, steps, warmup, dev, inp, page_size=0):
     obs = [torch.empty(B, q.shape[1], Hq, d, dtype=torch.bfloat16, device=dev) for _, q, _, _ in views]
     oo = torch.empty(B, 1, Hq, d, dtype=torch.bfloat16, device=dev)
 
+    last = starts[-1]
+
     def step():
         if page_size:
             cl.zero_()
             for (s0, q, k, v), ob in zip(views, obs):
-                ox.prefill_chunk_paged(shape, s0, q, inp["q_out"], k, v, aff, cache, cl, ob, oo,
-                                       ws)
+                qo, o = (inp["q_out"], oo) if s0 == last else (None, None)
+                ox.prefill_chunk_paged(shape, s0, q, qo, k, v, aff, cache, cl, ob, o, ws)
             return
         for (s0, q, k, v), ob in zip(views, obs):
-            ox.prefill_chunk(shape, s0, q, inp["q_out"], k, v, aff, ck, cv, cl, ob, oo, ws)
+            qo, o = (inp["q_out"], oo) if s0 == last else (None, None)
+            ox.prefill_chunk(shape, s0, q, qo, k, v, aff, ck, cv, cl, ob, o, ws)
 
     for _ in range(warmup):
         step()
@@ -632,14 +637,16 @@ def main():
     if not args.skip_regimes:
         ch = bench_prefill_chunked(wl, 8192, max(2, args.steps // 3), 1, dev, pf["inp"])
         rec["prefill_chunked"] = {
-            "workload": f"{wl.name} in chunks of 8192", "chunks": ch["chunks"],
+            "workload": f"{wl.name} in chunks of 8192, output row with the last chunk",
+            "chunks": ch["chunks"],
             "ms_per_step": round(ch["ms"], 4), "tokens_per_s": round(tokens / (ch["ms"] / 1e3), 1),
             "band_frac": round(base_flops / (ch["band_ms"] / 1e3) / PEAK_BF16_FLOPS, 4),
         }
         chp = bench_prefill_chunked(wl, 8192, max(2, args.steps // 3), 1, dev, pf["inp"],
                                     page_size=64)
         rec["prefill_chunked_paged"] = {
-            "workload": f"{wl.name} in chunks of 8192 into a shuffled pool of 64-token pages",
+            "workload": f"{wl.name} in chunks of 8192 into a shuffled pool of 64-token pages, "
+                        "output row with the last chunk",
             "chunks": chp["chunks"], "ms_per_step": round(chp["ms"], 4),
             "tokens_per_s": round(tokens / (chp["ms"] / 1e3), 1),
             "band_frac": round(base_flops / (chp["band_ms"] / 1e3) / PEAK_BF16_FLOPS, 4),

@@ -677,7 +677,11 @@ int prefill_chunk_impl(const orthros_shape* s, int64_t past_len, int64_t C, cons
   int rc;
   if (past_len < 0 || C < 1 || C > INT_MAX / 2 || past_len > INT_MAX / 2) return ORTHROS_E_INVALID;
   if ((rc = check_affine(aff))) return rc;
-  if ((rc = check_ptrs({q_base, q_out, k, v, cache_k, cache_v, cache_len, o_base, o_out}))) return rc;
+  if ((rc = check_ptrs({q_base, k, v, cache_k, cache_v, cache_len, o_base}))) return rc;
+  // the output row is optional (a chunk before the prompt's last one needs none): both or neither
+  if ((q_out == nullptr) != (o_out == nullptr)) return ORTHROS_E_INVALID;
+  const bool out_row = q_out != nullptr;
+  if (out_row && (rc = check_ptrs({q_out, o_out}))) return rc;
   if ((rc = check_ws(s, ws, ws_bytes))) return rc;
   if (past_len + C > s->capacity) return ORTHROS_E_INVALID;
   const bool paged = pg.table != nullptr;
@@ -718,7 +722,7 @@ int prefill_chunk_impl(const orthros_shape* s, int64_t past_len, int64_t C, cons
     r.B = B; r.Hq = Hq; r.Hkv = Hkv; r.G = G; r.d = d; r.nrows = (int)C; r.t0 = (int)past_len;
     r.window = s->window; r.scale = scale;
     rc = launch_rc(run_stage(ORTHROS_STAGE_ROWS_F32, st, [&] { return launch_rows_f32(r, st); }));
-    if (rc) return rc;
+    if (rc || !out_row) return rc;
     RowsF32Params o = r;
     o.q = static_cast<const float*>(q_out);
     o.q_sb = (idx_t)Hq * d; o.q_st = 0;
@@ -741,7 +745,7 @@ int prefill_chunk_impl(const orthros_shape* s, int64_t past_len, int64_t C, cons
   bp.window = s->window < (int)n ? s->window : (int)n;
   bp.scale_log2 = scale * kLog2e;
   rc = launch_rc(run_stage(ORTHROS_STAGE_BAND, st, [&] { return launch_band(bp, d, st); }));
-  if (rc) return rc;
+  if (rc || !out_row) return rc;
 
   // Output row at the chunk's last token over the whole cache.
   SplitParams sp{};

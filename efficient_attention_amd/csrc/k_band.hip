@@ -223,18 +223,24 @@ __global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
         (const __attribute__((address_space(4))) int32_t*)p.pg.table;
     return tbl[(idx_t)b * p.pg.tbl_sb + (tb >> p.pg.ps_log2)];
   };
-  // Unit m of K (or V) -> LDS byte offset `dst`; `page` is its table entry (paged pool).
-  auto copy_unit = [&](int m, int32_t page, const uint16_t* base, const uint32_t* off, uint32_t dst) {
+  // Bytes from the (sequence, kv head) base to unit m, through its table entry `page` in a
+  // paged pool (the page's start, k_sp elements of 2 bytes per page, plus the unit's rows). K
+  // and V share it, and a unit's V is copied a span after its K, so each unit's offset is
+  // formed once.
+  const idx_t page_bytes = (idx_t)p.pg.k_sp * 2;
+  const int page_mask = (1 << p.pg.ps_log2) - 1;
+  auto unit_off = [&](int m, int32_t page) -> idx_t {
     const int tb = unit_hi_s - kTK * m;
-    idx_t toff = (idx_t)tb * rowb;  // bytes from the (sequence, kv head) base to the unit
-    if (p.pg.table) {
-      if (page < 0 || (int64_t)page >= p.pg.num_pages) {
-        __hip_atomic_fetch_or(p.pg.status, kStatusBadPage, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        page = 0;
-      }
-      // the page's start (k_sp elements of 2 bytes per page) plus the unit's rows
-      toff = (idx_t)page * p.pg.k_sp * 2 + (idx_t)(tb & ((1 << p.pg.ps_log2) - 1)) * rowb;
+    if (!p.pg.table) return (idx_t)tb * rowb;
+    if (page < 0 || (int64_t)page >= p.pg.num_pages) {
+      __hip_atomic_fetch_or(p.pg.status, kStatusBadPage, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      page = 0;
     }
+    return (idx_t)page * page_bytes + (idx_t)(tb & page_mask) * rowb;
+  };
+  // Unit m of K (or V), `toff` bytes from `base`, -> LDS byte offset `dst`.
+  auto copy_unit = [&](int m, idx_t toff, const uint16_t* base, const uint32_t* off, uint32_t dst) {
+    const int tb = unit_hi_s - kTK * m;
     const unsigned char* src = reinterpret_cast<const unsigned char*>(base) + toff;
     const uint32_t d0 = lds0 + dst + (uint32_t)(wv_s * NINST) * 1024u;
     if (tb + kTK <= nk) {
@@ -401,18 +407,22 @@ __global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
   // up its wavefront while the address unit works through the queue, so the two wavefronts of
   // a SIMD take turns: the second (wavefronts 4..7) copies at the top of the span, the first
   // after its first region.
-  int32_t pg1 = 0, pg2 = 0, pg3 = 0;  // table entries of units 2e + 1 .. 2e + 3
-  if (p.pg.table) {
-    copy_unit(0, page_of(0), kbase, skoff, k_dst(0));
-    copy_unit(0, page_of(0), vbase, svoff, v_dst(0));
-    if (nunits_s > 1) copy_unit(1, page_of(1), kbase, skoff, k_dst(1));
-    pg1 = page_of(1);
-    pg2 = page_of(2);
-    pg3 = page_of(3);
-  } else {
-    copy_unit(0, 0, kbase, skoff, k_dst(0));
-    copy_unit(0, 0, vbase, svoff, v_dst(0));
-    if (nunits_s > 1) copy_unit(1, 0, kbase, skoff, k_dst(1));
+  // Offset of unit 2e + 1 (its K went with span e - 1's copies, its V goes with span e's) and
+  // the table entries of units 2e + 2, 2e + 3.
+  idx_t off1 = 0;
+  int32_t pg2 = 0, pg3 = 0;
+  {
+    const idx_t off0 = unit_off(0, p.pg.table ? page_of(0) : 0);
+    copy_unit(0, off0, kbase, skoff, k_dst(0));
+    copy_unit(0, off0, vbase, svoff, v_dst(0));
+    if (nunits_s > 1) {
+      off1 = unit_off(1, p.pg.table ? page_of(1) : 0);
+      copy_unit(1, off1, kbase, skoff, k_dst(1));
+    }
+    if (p.pg.table) {
+      pg2 = page_of(2);
+      pg3 = page_of(3);
+    }
   }
   wait_lds_copies();
   __syncthreads();
@@ -422,14 +432,15 @@ __global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
   const bool copy_late = wv_s < kNW / 2;  // the first wavefront of its SIMD
   auto copies = [&](int e) {
     const int m = 2 * e;
-    if (m + 1 < nunits_s) copy_unit(m + 1, pg1, vbase, svoff, v_dst(m + 1));
+    const idx_t off2 = unit_off(m + 2, pg2), off3 = unit_off(m + 3, pg3);
+    if (m + 1 < nunits_s) copy_unit(m + 1, off1, vbase, svoff, v_dst(m + 1));
     if (m + 2 < nunits_s) {
-      copy_unit(m + 2, pg2, vbase, svoff, v_dst(m + 2));
-      copy_unit(m + 2, pg2, kbase, skoff, k_dst(m + 2));
+      copy_unit(m + 2, off2, vbase, svoff, v_dst(m + 2));
+      copy_unit(m + 2, off2, kbase, skoff, k_dst(m + 2));
     }
-    if (m + 3 < nunits_s) copy_unit(m + 3, pg3, kbase, skoff, k_dst(m + 3));
-    if (p.pg.table) {  // the next span's entries, read now (after the last use) and used then
-      pg1 = pg3;
+    if (m + 3 < nunits_s) copy_unit(m + 3, off3, kbase, skoff, k_dst(m + 3));
+    off1 = off3;
+    if (p.pg.table) {  // the next span's entries, read now (after their last use), used then
       pg2 = page_of(m + 4);
       pg3 = page_of(m + 5);
     }

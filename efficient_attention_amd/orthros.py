@@ -224,6 +224,20 @@ def _check(t, shape, dtype, device, what):
         raise ValueError(f"{what} must be contiguous")
 
 
+def _ptr(t):
+    """Device address of an optional tensor (0, i.e. NULL, for None)."""
+    return 0 if t is None else t.data_ptr()
+
+
+def _check_out_row(q_out, o_out, shape, dtype, device):
+    """An optional output-stream row: q_out and o_out both given (and checked) or both None."""
+    if (q_out is None) != (o_out is None):
+        raise ValueError("q_out and o_out must both be given or both be None")
+    if q_out is not None:
+        _check(q_out, shape, dtype, device, "q_out")
+        _check(o_out, shape, dtype, device, "o_out")
+
+
 def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -276,24 +290,24 @@ def prefill(shape: Shape, q_base, q_out, k, v, affine: Affine, cache_k, cache_v,
 
 def prefill_chunk(shape: Shape, past_len: int, q_base, q_out, k, v, affine: Affine, cache_k,
                   cache_v, cache_len, o_base, o_out, workspace, stream=None):
-    """orthros_prefill_chunk: C more prompt tokens after past_len already cached ones."""
+    """orthros_prefill_chunk: C more prompt tokens after past_len already cached ones. q_out
+    and o_out may both be None: no output-stream row (a chunk before the prompt's last)."""
     B, Hq, Hkv, d = shape.batch, shape.num_q_heads, shape.num_kv_heads, shape.head_dim
     C = q_base.shape[1]
     dev, dt = q_base.device, shape.dtype
     _check(q_base, (B, C, Hq, d), dt, dev, "q_base")
-    _check(q_out, (B, 1, Hq, d), dt, dev, "q_out")
+    _check_out_row(q_out, o_out, (B, 1, Hq, d), dt, dev)
     _check(k, (B, C, Hkv, d), dt, dev, "k")
     _check(v, (B, C, Hkv, d), dt, dev, "v")
     _check(cache_k, (B, Hkv, shape.capacity, d), dt, dev, "cache_k")
     _check(cache_v, (B, Hkv, shape.capacity, d), dt, dev, "cache_v")
     _check(cache_len, (B,), torch.int32, dev, "cache_len")
     _check(o_base, (B, C, Hq, d), dt, dev, "o_base")
-    _check(o_out, (B, 1, Hq, d), dt, dev, "o_out")
     aff = affine.c(Hq * d, dev)
     rc = lib().orthros_prefill_chunk(
-        ctypes.byref(shape.c()), int(past_len), C, q_base.data_ptr(), q_out.data_ptr(),
+        ctypes.byref(shape.c()), int(past_len), C, q_base.data_ptr(), _ptr(q_out),
         k.data_ptr(), v.data_ptr(), ctypes.byref(aff), cache_k.data_ptr(), cache_v.data_ptr(),
-        cache_len.data_ptr(), o_base.data_ptr(), o_out.data_ptr(), workspace.data_ptr(),
+        cache_len.data_ptr(), o_base.data_ptr(), _ptr(o_out), workspace.data_ptr(),
         workspace.numel(), _stream(stream))
     _rc(rc, "orthros_prefill_chunk")
 
@@ -372,23 +386,23 @@ def decode_step_paged(shape: Shape, q_base, q_out, k_new, v_new, affine: Affine,
 
 def prefill_chunk_paged(shape: Shape, past_len: int, q_base, q_out, k, v, affine: Affine,
                         cache: PagedKV, cache_len, o_base, o_out, workspace, stream=None):
-    """orthros_prefill_chunk_paged: C more prompt tokens into a paged cache."""
+    """orthros_prefill_chunk_paged: C more prompt tokens into a paged cache (q_out and o_out
+    may both be None, as for prefill_chunk)."""
     B, Hq, Hkv, d = shape.batch, shape.num_q_heads, shape.num_kv_heads, shape.head_dim
     C = q_base.shape[1]
     dev, dt = q_base.device, shape.dtype
     _check(q_base, (B, C, Hq, d), dt, dev, "q_base")
-    _check(q_out, (B, 1, Hq, d), dt, dev, "q_out")
+    _check_out_row(q_out, o_out, (B, 1, Hq, d), dt, dev)
     _check(k, (B, C, Hkv, d), dt, dev, "k")
     _check(v, (B, C, Hkv, d), dt, dev, "v")
     _check(cache_len, (B,), torch.int32, dev, "cache_len")
     _check(o_base, (B, C, Hq, d), dt, dev, "o_base")
-    _check(o_out, (B, 1, Hq, d), dt, dev, "o_out")
     aff = affine.c(Hq * d, dev)
     pc = cache.c(shape, dev)
     rc = lib().orthros_prefill_chunk_paged(
-        ctypes.byref(shape.c()), int(past_len), C, q_base.data_ptr(), q_out.data_ptr(),
+        ctypes.byref(shape.c()), int(past_len), C, q_base.data_ptr(), _ptr(q_out),
         k.data_ptr(), v.data_ptr(), ctypes.byref(aff), ctypes.byref(pc), cache_len.data_ptr(),
-        o_base.data_ptr(), o_out.data_ptr(), workspace.data_ptr(), workspace.numel(),
+        o_base.data_ptr(), _ptr(o_out), workspace.data_ptr(), workspace.numel(),
         _stream(stream))
     _rc(rc, "orthros_prefill_chunk_paged")
 

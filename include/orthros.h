@@ -223,6 +223,10 @@ int orthros_forward_sft(const orthros_shape* shape, int64_t T,
  *   q_base  [B, C, H_q, d]; q_out [B, 1, H_q, d]; k, v [B, C, H_kv, d]
  *   o_base  [B, C, H_q, d]  Eq. 4 at positions past_len .. past_len+C-1
  *   o_out   [B, 1, H_q, d]  Eq. 5 at position past_len + C - 1
+ * q_out and o_out may both be NULL: then no output-stream row is computed. The prefilling
+ * regime duplicates only the prompt's last token (T_out = 1), so the chunks before the last
+ * one need no output row, and skipping it saves a pass over the whole cache per chunk.
+ * Exactly one of them NULL is ORTHROS_E_INVALID.
  * Requires past_len >= 0, C >= 1, past_len + C <= capacity. */
 int orthros_prefill_chunk(const orthros_shape* shape, int64_t past_len, int64_t C,
                           const void* q_base, const void* q_out, const void* k, const void* v,
@@ -342,7 +346,7 @@ int orthros_decode_step_paged(const orthros_shape* shape,
  * the chunk's keys/values go to positions past_len .. past_len+C-1 through the table
  * (cache_len[b] must equal past_len on entry and becomes past_len + C), its base rows' windows
  * and the output row read the cached tokens through the table. Same outputs as
- * orthros_prefill_chunk. bf16 calls need pages of at least 64 rows (ORTHROS_E_UNSUPPORTED
+ * orthros_prefill_chunk (q_out and o_out may both be NULL, as there). bf16 calls need pages of at least 64 rows (ORTHROS_E_UNSUPPORTED
  * otherwise); a bad table entry sets ORTHROS_STATUS_BAD_PAGE. */
 int orthros_prefill_chunk_paged(const orthros_shape* shape, int64_t past_len, int64_t C,
                                 const void* q_base, const void* q_out,

@@ -10,6 +10,7 @@ import subprocess
 import sys
 
 import pytest
+import torch
 
 from efficient_attention_amd import orthros as ox
 
@@ -206,6 +207,19 @@ def _chunk(shape, past=100, C=64, ws_bytes=None, **ptrs):
 def test_prefill_chunk_rejects_null_and_misaligned(name):
     assert _chunk(_shape(), **{name: None}) == ox.E_INVALID
     assert _chunk(_shape(), **{name: FAKE + 4}) == ox.E_INVALID
+
+
+def test_prefill_chunk_output_row_is_both_or_neither():
+    # q_out and o_out may both be NULL (no output row); one of them alone is invalid, and with
+    # both NULL the other arguments are still checked
+    assert _chunk(_shape(), q_out=None) == ox.E_INVALID
+    assert _chunk(_shape(), o_out=None) == ox.E_INVALID
+    assert _chunk(_shape(), q_out=None, o_out=None, past=-1) == ox.E_INVALID
+    assert _chunk(_shape(), q_out=None, o_out=None, k=None) == ox.E_INVALID
+    assert _chunk(_shape(), q_out=None, o_out=None, o_base=FAKE + 4) == ox.E_INVALID
+    assert _chunk(_shape(), q_out=None, o_out=None, ws_bytes=64) == ox.E_WORKSPACE
+    with pytest.raises(ValueError):
+        ox._check_out_row(None, torch.zeros(1), (1,), torch.float32, torch.device("cpu"))
 
 
 def test_prefill_chunk_rejects_bad_lengths_and_workspace():
