@@ -505,6 +505,7 @@ int backward_impl(const orthros_shape* s, int64_t T, const void* q_base, const v
       if (rc) return rc;
     }
   }
+  BwdQParams qp2[2] = {};
   for (int i = 0; i < 2; ++i) {
     BwdQParams q{};
     q.q = bf ? qps[i] : qs[i];
@@ -517,9 +518,13 @@ int backward_impl(const orthros_shape* s, int64_t T, const void* q_base, const v
     }
     q.pos = poss[i]; q.nrows = nrows[i];
     q.B = B; q.T = (int)T; q.Hq = Hq; q.Hkv = Hkv; q.G = G; q.window = wins[i]; q.scale = scale;
-    rc = launch_rc(run_stage(ORTHROS_STAGE_BWD_Q, st, [&] {
-      return bf ? launch_bwd_q_bf16(q, d, st) : launch_bwd_q_f32(q, d, st);
-    }));
+    qp2[i] = q;
+    if (bf) continue;  // both bf16 query sides go in one launch below
+    rc = launch_rc(run_stage(ORTHROS_STAGE_BWD_Q, st, [&] { return launch_bwd_q_f32(q, d, st); }));
+    if (rc) return rc;
+  }
+  if (bf) {  // the output stream's (longer, causal) rows first, the base rows after them
+    rc = launch_rc(run_stage(ORTHROS_STAGE_BWD_Q, st, [&] { return launch_bwd_q_bf16_pair(qp2[1], qp2[0], d, st); }));
     if (rc) return rc;
   }
   BwdKVParams kv{};

@@ -12,7 +12,8 @@
 //                  operand, rounded once as in the forward
 //   bwd_q_kernel   per 32 query rows of one stream: dq_raw = alpha (.) dq (the raw query's
 //                  gradient) and the rows' scale-offset partial sums, and -D_t and -lse_t (log2
-//                  units), the key side's accumulator seeds
+//                  units), the key side's accumulator seeds; bwd_q_pair_kernel runs both
+//                  streams' rows in one launch (the bf16 path)
 //                    S^T = K Q'^T, dP^T = V dO^T   (A operand: key / value rows from LDS)
 //                    dQ^T += K^T dZ^T              (A operand: transposed key reads)
 //   bwd_kv_kernel  per 32 keys: dk and dv over both streams' rows of every query head of the
@@ -156,7 +157,7 @@ __device__ __forceinline__ void lane_transpose_sum(float (&v)[N], int j) {
 // (two work-groups per CU): the work-group's rows then span 128 positions instead of 256, and
 // its wavefronts idle on fewer of its tiles (a base-stream wavefront uses w / 64 + 1 of them).
 template <int D, int HPW, int NW>
-__global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_q_kernel(BwdQParams p) {
+__device__ __forceinline__ void bwd_q_body(const BwdQParams& p, uint32_t blk) {
   constexpr int NCH = D / 8, ROWB = D * 2, TILEB = kTK * ROWB, STAGEB = 2 * TILEB;
   constexpr int PB = NW / HPW, BMP = kQW * PB, NKS = D / 16, NDT = D / 32;
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGEB];
@@ -166,7 +167,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_q_kernel(BwdQParams p) {
   const int nhc = p.G / HPW;
   const int npb = (NR + BMP - 1) / BMP;
   const uint32_t total = (uint32_t)p.B * p.Hkv * nhc * npb;
-  const uint32_t lid = xcd_swizzle(blockIdx.x, total);
+  const uint32_t lid = xcd_swizzle(blk, total);
   int from_longest, rest;  // a few (sequence, head group) pairs at a time, longest rows first
   grouped_order(lid, p.B * p.Hkv * nhc, npb, 32 * (8 / NW), from_longest, rest);
   const int pb = __builtin_amdgcn_readfirstlane(npb - 1 - from_longest);
@@ -436,6 +437,22 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_q_kernel(BwdQParams p) {
         *reinterpret_cast<f32x4*>(out + 32 * dt + 8 * rg + 4 * hh) = v4;
       }
   }
+}
+
+template <int D, int HPW, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_q_kernel(BwdQParams p) {
+  bwd_q_body<D, HPW, NW>(p, blockIdx.x);
+}
+// Both streams' query sides in one launch: work-groups 0 .. n0-1 serve p0, the rest p1 (each
+// stream's own work order within its range), so the second stream's work-groups start as the
+// first stream's leave CUs free.
+template <int D, int HPW, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_q_pair_kernel(BwdQParams p0, BwdQParams p1,
+                                                                    uint32_t n0) {
+  if (blockIdx.x < n0)
+    bwd_q_body<D, HPW, NW>(p0, blockIdx.x);
+  else
+    bwd_q_body<D, HPW, NW>(p1, blockIdx.x - n0);
 }
 
 // ---- key side --------------------------------------------------------------------------------
@@ -789,6 +806,32 @@ hipError_t launch_bwd_q_bf16(const BwdQParams& p, int d, hipStream_t s) {
     else ORTHROS_BWDQ(64, 1);
   }
 #undef ORTHROS_BWDQ
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_q_bf16_pair(const BwdQParams& p0, const BwdQParams& p1, int d, hipStream_t s) {
+  int hpw = 1;
+  if (p0.G % 8 == 0) hpw = 8;
+  else if (p0.G % 4 == 0) hpw = 4;
+  else if (p0.G % 2 == 0) hpw = 2;
+  const int nw = hpw >= 4 ? 8 : 4;  // wavefronts per work-group
+  const int bmp = kQW * (nw / hpw);
+  const uint32_t n0 = (uint32_t)(p0.B * p0.Hkv * (p0.G / hpw) * ((p0.nrows + bmp - 1) / bmp));
+  const uint32_t n1 = (uint32_t)(p1.B * p1.Hkv * (p1.G / hpw) * ((p1.nrows + bmp - 1) / bmp));
+  dim3 grid(n0 + n1), block(64 * nw);
+#define ORTHROS_BWDQ2(DD, HH) hipLaunchKernelGGL((bwd_q_pair_kernel<DD, HH, (HH >= 4 ? 8 : 4)>), grid, block, 0, s, p0, p1, n0)
+  if (d == 128) {
+    if (hpw == 8) ORTHROS_BWDQ2(128, 8);
+    else if (hpw == 4) ORTHROS_BWDQ2(128, 4);
+    else if (hpw == 2) ORTHROS_BWDQ2(128, 2);
+    else ORTHROS_BWDQ2(128, 1);
+  } else {
+    if (hpw == 8) ORTHROS_BWDQ2(64, 8);
+    else if (hpw == 4) ORTHROS_BWDQ2(64, 4);
+    else if (hpw == 2) ORTHROS_BWDQ2(64, 2);
+    else ORTHROS_BWDQ2(64, 1);
+  }
+#undef ORTHROS_BWDQ2
   return hipGetLastError();
 }
 

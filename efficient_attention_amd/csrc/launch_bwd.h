@@ -69,6 +69,8 @@ struct AffineGradParams {
 hipError_t launch_bwd_q_f32(const BwdQParams& p, int d, hipStream_t s);
 hipError_t launch_bwd_kv_f32(const BwdKVParams& p, int d, hipStream_t s);
 hipError_t launch_bwd_q_bf16(const BwdQParams& p, int d, hipStream_t s);
+// Both streams' query sides (same shape and head grouping) in one launch, p0's work first.
+hipError_t launch_bwd_q_bf16_pair(const BwdQParams& p0, const BwdQParams& p1, int d, hipStream_t s);
 hipError_t launch_bwd_kv_bf16(const BwdKVParams& p, int d, hipStream_t s);
 hipError_t launch_affine_grad(const AffineGradParams& p, hipStream_t s);
 // Only the fixed-order sums of the p[i].nchunk partials of `count` (1 or 2) streams in one launch
