@@ -93,6 +93,30 @@ def copy_calibration(dev, gib=1, reps=3):
     del src, dst
 
 
+def gemm_reference(dev, n=16384, reps=5):
+    """A plain bf16 matrix product (torch.matmul, the vendor GEMM library) of n x n x n on the
+    same GPU: the dense matrix-core rate this part sustains in practice. Reported beside the
+    banded kernel's fraction of the 2.5 PFLOP/s figure, as context; that fraction stays taken
+    against the published figure."""
+    a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    for _ in range(2):
+        c = a @ b
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        c = a @ b
+    e1.record()
+    torch.cuda.synchronize()
+    s = e0.elapsed_time(e1) / 1e3 / reps
+    del a, b, c
+    flops = 2.0 * n ** 3
+    log(f"gemm reference: {n}^3 bf16 in {s * 1e3:.3f} ms = {flops / s / 1e12:.1f} TFLOP/s")
+    return {"kernel": f"torch.matmul bf16 {n}x{n}x{n}", "tflops": round(flops / s / 1e12, 1),
+            "frac_of_peak": round(flops / s / PEAK_BF16_FLOPS, 4)}
+
+
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
@@ -687,6 +711,11 @@ def main():
                                   "roundings (post-affine query, probabilities, score gradient, "
                                   "the forward output inside D), each <= 2^-9 relative",
         }
+    # last of the GPU legs: the product draws the most power of anything here, and a leg timed
+    # right after it (the decode step) read ~5% slower
+    ref = gemm_reference(dev)
+    ref["band_vs_gemm"] = round(achieved / 1e12 / ref["tflops"], 4)
+    rec["roofline"]["gemm_reference"] = ref
     if not args.skip_cpu:
         rec["cpu_baseline"] = cpu_baseline(pf["inp"], wl)
     print(json.dumps(rec), flush=True)
