@@ -77,6 +77,47 @@ def test_prefill_matches_oracle(B, Hq, Hkv, d, P, w, dt):
     assert torch.isnan(g["cache_k"][:, :, P:].float()).all()
 
 
+def _far_key_inputs(wl, amp):
+    """Prefill inputs with one key far below the rows that see it: key 50 gets the direction u
+    scaled by amp, and the base queries of rows 400..649 (after their scale-offset) the same, so
+    their score against it is amp^2 s log2 e (log2 units), while their scores against the keys
+    near their diagonal stay of the order of amp."""
+    inp = syn.make_prefill(wl)
+    g = torch.Generator().manual_seed(wl.seed + 1)
+    u = torch.randn(wl.head_dim, generator=g, dtype=torch.float64)
+    u /= u.norm()
+    a_b, b_b = (x.double().view(wl.q_heads, wl.head_dim) for x in inp["affine"][:2])
+    inp["k"][0, 50, 0, :] = (amp * u).to(inp["k"].dtype)
+    for t in range(400, 650):
+        inp["q_base"][0, t] = ((amp * u[None, :] - b_b) / a_b).to(inp["q_base"].dtype)
+    return inp
+
+
+def test_prefill_far_dominant_key_matches_oracle():
+    """A key that dominates rows far above it (as a sink token does): rows 400..649 meet it more
+    than 300 keys below their diagonal, with a score 80-90 (log2 units) above every score they
+    met before it. The band kernel's reference then moves by that much in one rescale (the
+    accumulated output scaled by ~2^-85), and the rows' weight sits on that key."""
+    wl = _case(batch=1, q_heads=4, kv_heads=1, head_dim=128, length=700, window=600,
+               dtype="bf16", seed=4242)
+    inp = _far_key_inputs(wl, 27.3)
+    _say("prefill, far dominant key", wl)
+    s = oracle.default_scale(wl.head_dim) * np.log2(np.e)
+    q64 = oracle.scale_offset(H.to64(inp["q_base"][0]), *H.affine64(inp["affine"][:2]))
+    k64 = H.to64(inp["k"][0, :, 0])
+    for t in (400, 500, 649):  # the jump the rows meet, from the scores of the pages' Eq. 4
+        sc = q64[t] @ k64[: t + 1].T * s  # [Hq, t + 1], log2 units
+        jump = sc[:, 50] - sc[:, t - 300:].max(axis=1)
+        assert ((jump > 60) & (jump < 110)).all(), jump
+    g = H.gpu_prefill(inp, wl.window, torch.bfloat16)
+    ob, oo, _, _, _ = H.oracle_prefill(inp, wl.window)
+    H.assert_close(H.to64(g["o_base"]), ob, torch.bfloat16, "o_base")
+    H.assert_close(H.to64(g["o_out"]), oo, torch.bfloat16, "o_out")
+    v50 = H.to64(inp["v"][0, 50, 0])
+    np.testing.assert_allclose(H.to64(g["o_base"][0, 500]), np.broadcast_to(v50, (4, 128)),
+                               atol=2e-2)
+
+
 def test_prefill_cache_is_ready_on_the_callers_stream():
     """Work enqueued after the call on the caller's own stream (here a non-default one, not
     synchronised in between) already sees the whole cache and cache_len."""
