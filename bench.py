@@ -52,9 +52,9 @@ CSRC = os.path.join(ROOT, "efficient_attention_amd", "csrc")
 # blank lines are left out): when the code changes, the figure no longer describes the kernel
 # and `traffic` is reported as null.
 TRAFFIC = {
-    "band_kernel": {"sha": "5ae97701e3583e93", "bytes_per_launch": 2.8637e+09},
-    "split_rows_kernel": {"sha": "b7961c0ace5f389f", "bytes_per_launch": 8.5959e+09},
-    "split_rows_kernel_paged": {"sha": "b7961c0ace5f389f", "bytes_per_launch": 8.5969e+09},
+    "band_kernel": {"sha": "b2a1f56195090eee", "bytes_per_launch": 2.8647e+09},
+    "split_rows_kernel": {"sha": "764e1b6c96dcf5eb", "bytes_per_launch": 8.5959e+09},
+    "split_rows_kernel_paged": {"sha": "764e1b6c96dcf5eb", "bytes_per_launch": 8.5969e+09},
 }
 
 
@@ -684,7 +684,7 @@ def main():
             "roofline": {"bound": "mfma", "achieved": round(sf["flops"] / (sf["band_ms"] / 1e3) / 1e12, 2),
                          "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
                          "frac": round(sf["flops"] / (sf["band_ms"] / 1e3) / PEAK_BF16_FLOPS, 4),
-                         "kernel": "band_kernel (both launches)"},
+                         "kernel": "band_kernel (both row sets, one launch)"},
         }
     if not args.skip_regimes:
         tw = syn.WORKLOADS["pt_1p3b_2k"]

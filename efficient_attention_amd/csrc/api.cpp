@@ -630,11 +630,11 @@ int forward_sft_impl(const orthros_shape* s, int64_t T, const void* q_base, cons
   bp.window = s->window < (int)T ? s->window : (int)T;
   bp.scale_log2 = scale * kLog2e;
   bp.lse = lse_b; bp.lse_sb = (idx_t)Hq * T; bp.lse_sh = T;
-  rc = launch_rc(run_stage(ORTHROS_STAGE_BAND, st, [&] { return launch_band(bp, d, st); }));
-  if (rc) return rc;
 
   if (R > kSftSplitRows) {
-    // Many response rows: the banded kernel with the row positions, full causal windows.
+    // Many response rows: the banded kernel with the row positions, full causal windows, in
+    // one launch with the base rows, the response rows' (longer) work-groups first, so the
+    // base rows' work-groups fill the CUs the response rows leave free.
     BandParams op = bp;
     op.q = q_out; op.q_sb = R * Hq * d; op.q_st = (idx_t)Hq * d;
     op.alpha = aff->alpha_out; op.beta = aff->beta_out;
@@ -642,8 +642,10 @@ int forward_sft_impl(const orthros_shape* s, int64_t T, const void* q_base, cons
     op.nrows = (int)R; op.pos = out_pos;
     op.window = (int)T;
     op.lse = lse_o; op.lse_sb = (idx_t)Hq * R; op.lse_sh = R;
-    return launch_rc(run_stage(ORTHROS_STAGE_BAND, st, [&] { return launch_band(op, d, st); }));
+    return launch_rc(run_stage(ORTHROS_STAGE_BAND, st, [&] { return launch_band_pair(op, bp, d, st); }));
   }
+  rc = launch_rc(run_stage(ORTHROS_STAGE_BAND, st, [&] { return launch_band(bp, d, st); }));
+  if (rc) return rc;
 
   // Few response rows: split-key rows, each (row, head) pair over keys 0 .. pos[row].
   SplitParams sp{};

@@ -41,8 +41,15 @@ constexpr float kUnstarted = -1e30f;
 
 }  // namespace
 
-template <int D, int HPW>
-__global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
+// PAIR: two row sets over the same keys in one launch, work-groups 0 .. n0-1 serving p0, the
+// rest p1 (each set in its own work order), so the second set's work-groups fill the CUs the
+// first leaves free instead of waiting for its last work-group. Without PAIR only p0 is used
+// (the body stays in the kernel itself: as a separate device function it compiled ~2% slower).
+template <int D, int HPW, bool PAIR>
+__global__ __launch_bounds__(kThreads) void band_kernel(BandParams p0, BandParams p1, uint32_t n0) {
+  const bool second = PAIR && blockIdx.x >= n0;
+  const BandParams& p = second ? p1 : p0;
+  const uint32_t blk = second ? blockIdx.x - n0 : blockIdx.x;
   constexpr int NCH = D / 8;             // 16-byte slots per row
   constexpr int ROWB = D * 2;            // bytes per K/V row
   constexpr int UNITB = kTK * ROWB;      // bytes per 64-key unit of K (or V)
@@ -56,7 +63,7 @@ __global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
   const int nhc = p.G / HPW;
   const int npb = (p.nrows + BMP - 1) / BMP;
   const uint32_t total = (uint32_t)p.B * p.Hkv * nhc * npb;
-  const uint32_t lid = xcd_swizzle(blockIdx.x, total);
+  const uint32_t lid = xcd_swizzle(blk, total);
   const bool causal = p.window >= p.nkeys;
   int pb, rest;
   if (causal) {  // a few (sequence, head group) pairs at a time, longest rows first
@@ -500,16 +507,19 @@ __global__ __launch_bounds__(kThreads) void band_kernel(BandParams p) {
   }
 }
 
-hipError_t launch_band(const BandParams& p, int d, hipStream_t s) {
-  int hpw = 1;
-  if (p.G % 8 == 0) hpw = 8;
-  else if (p.G % 4 == 0) hpw = 4;
-  else if (p.G % 2 == 0) hpw = 2;
+namespace {
+int band_hpw(int G) { return G % 8 == 0 ? 8 : (G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1)); }
+uint32_t band_groups(const BandParams& p, int hpw) {
   const int bmp = kQW * (kNW / hpw);
   const int npb = (p.nrows + bmp - 1) / bmp;
-  const uint32_t total = (uint32_t)p.B * p.Hkv * (p.G / hpw) * npb;
-  dim3 grid(total), block(kThreads);
-#define ORTHROS_BAND(DD, HH) hipLaunchKernelGGL((band_kernel<DD, HH>), grid, block, 0, s, p)
+  return (uint32_t)p.B * p.Hkv * (p.G / hpw) * npb;
+}
+}  // namespace
+
+hipError_t launch_band(const BandParams& p, int d, hipStream_t s) {
+  const int hpw = band_hpw(p.G);
+  dim3 grid(band_groups(p, hpw)), block(kThreads);
+#define ORTHROS_BAND(DD, HH) hipLaunchKernelGGL((band_kernel<DD, HH, false>), grid, block, 0, s, p, p, 0u)
   if (d == 128) {
     if (hpw == 8) ORTHROS_BAND(128, 8);
     else if (hpw == 4) ORTHROS_BAND(128, 4);
@@ -522,6 +532,26 @@ hipError_t launch_band(const BandParams& p, int d, hipStream_t s) {
     else ORTHROS_BAND(64, 1);
   }
 #undef ORTHROS_BAND
+  return hipGetLastError();
+}
+
+hipError_t launch_band_pair(const BandParams& p0, const BandParams& p1, int d, hipStream_t s) {
+  const int hpw = band_hpw(p0.G);  // both sets share the head grouping
+  const uint32_t n0 = band_groups(p0, hpw);
+  dim3 grid(n0 + band_groups(p1, hpw)), block(kThreads);
+#define ORTHROS_BAND2(DD, HH) hipLaunchKernelGGL((band_kernel<DD, HH, true>), grid, block, 0, s, p0, p1, n0)
+  if (d == 128) {
+    if (hpw == 8) ORTHROS_BAND2(128, 8);
+    else if (hpw == 4) ORTHROS_BAND2(128, 4);
+    else if (hpw == 2) ORTHROS_BAND2(128, 2);
+    else ORTHROS_BAND2(128, 1);
+  } else {
+    if (hpw == 8) ORTHROS_BAND2(64, 8);
+    else if (hpw == 4) ORTHROS_BAND2(64, 4);
+    else if (hpw == 2) ORTHROS_BAND2(64, 2);
+    else ORTHROS_BAND2(64, 1);
+  }
+#undef ORTHROS_BAND2
   return hipGetLastError();
 }
 

@@ -183,6 +183,8 @@ hipError_t launch_paged_write(const PagedWriteParams& p, hipStream_t s);
 hipError_t launch_split_rows(const SplitParams& p, int d, hipStream_t s);
 hipError_t launch_merge(const MergeParams& p, hipStream_t s);
 hipError_t launch_band(const BandParams& p, int d, hipStream_t s);
+// p0's and p1's rows (same shape and head grouping, same keys) in one launch, p0's first.
+hipError_t launch_band_pair(const BandParams& p0, const BandParams& p1, int d, hipStream_t s);
 hipError_t launch_rows_f32(const RowsF32Params& p, hipStream_t s);
 
 }  // namespace orthros
