@@ -38,6 +38,9 @@ SFT_CASES = [
     (2, 4, 1, 128, 500, 50, list(range(420, 500)), "bf16", True),        # 80 rows: banded path
     (1, 8, 2, 128, 260, 40, [259, 7, 130, 64, 63, 200, 1, 0, 255, 128, 129, 30, 31, 32, 33,
                              100, 101, 102, 250, 251], "bf16", False),  # 20 unsorted: banded
+    (1, 4, 4, 64, 200, 33, list(range(150, 200)), "bf16", True),         # d 64, MHA, 50 rows
+    (2, 16, 2, 128, 180, 48, [179, 0, 90, 91, 17, 179, 60, 120, 5, 6, 7, 8, 150, 151, 33, 34,
+                              100, 101, 170, 2, 44, 45, 46, 47], "bf16", False),  # 8 heads/kv, 24
     (1, 4, 2, 64, 150, 9, [149, 0, 77], "f32", False),                  # fp32 rows
     (1, 4, 2, 128, 129, 128, list(range(100, 129)), "f32", False),      # fp32, 29 rows
 ]
